@@ -1,0 +1,37 @@
+"""CPU oracle of the block token-eviction hot path — TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, obviously-correct float64 implementations (numpy) of the six
+operations of the path, written from the pages' definitions:
+
+* ``focus_importance_delta`` — FOCUS importance I_j and delta Delta-I
+  (FOCUS paper, arXiv 2601.23278: Section 3.1 Eq. 2, Section 3.2 Eq. 3,
+  Section 4.2; App. E.2.1; FOCUS notes page, key design 1).
+* ``esdllm_score`` — ES-dLLM importance score (ES-dLLM notes page, key
+  design 1).
+* ``topk_select`` — per-sequence top-K of masked tokens (FOCUS paper
+  Section 4.2; ES-dLLM notes page, key design 1 "top-(1-r_l)|S|").
+* ``gather_rows`` — Gather of the kept block hidden rows into H_reduced
+  (FOCUS paper Section 4.2; App. E.2.3 prefix-sum compaction).
+* ``kv_scatter`` — in-place scatter of the kept rows' new K/V into the
+  exact KV cache (ES-dLLM notes page, key design 2; FOCUS paper App. E.2.4).
+* ``reduced_attention`` — attention of the kept queries over prefix plus
+  block KV (FOCUS paper Section 2, Section 4.2; App. E.2.4).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package. The product path
+(``block_token_eviction_amd``) never imports, links or calls it, and this
+package shares no code with the HIP kernels.
+
+Every function is pinned by tests in ``tests/test_oracle_*.py`` against
+closed forms, hand-worked examples, library routines and invariants.
+"""
+from .focus import (block_scores, maxpool_keys, softmax_keys, importance,
+                    focus_importance_delta)
+from .esdllm import esdllm_score
+from .selection import topk_select
+from .rows import gather_rows, kv_scatter
+from .attention import reduced_attention
+
+__all__ = ["block_scores", "maxpool_keys", "softmax_keys", "importance",
+           "focus_importance_delta", "esdllm_score", "topk_select", "gather_rows",
+           "kv_scatter", "reduced_attention"]

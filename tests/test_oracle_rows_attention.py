@@ -1,0 +1,113 @@
+"""Pins of the gather, scatter and attention oracles (CPU only): torch
+index_select / index_copy_ and scaled_dot_product_attention as library
+routines, closed forms and invariants."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+
+def _sel(batch, n, k_max, seed):
+    r = np.random.default_rng(seed)
+    count = r.integers(0, k_max + 1, size=batch).astype(np.int32)
+    idx = np.full((batch, k_max), -1, np.int32)
+    for b in range(batch):
+        idx[b, :count[b]] = np.sort(r.choice(n, count[b], replace=False))
+    cu = np.zeros(batch + 1, np.int32); cu[1:] = np.cumsum(count)
+    return idx, count, cu
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.uint16, np.float64])
+def test_gather_matches_index_select(dtype):
+    batch, n, h = 5, 32, 24
+    src = (np.random.default_rng(0).standard_normal((batch, n, h)) * 100).astype(dtype)
+    idx, count, cu = _sel(batch, n, 12, 1)
+    flat = np.concatenate([b * n + idx[b, :count[b]] for b in range(batch)]).astype(np.int64)
+    want = torch.index_select(torch.from_numpy(src.reshape(batch * n, h)), 0, torch.from_numpy(flat))
+    got = oracle.gather_rows(src, idx, count, cu)
+    assert got.dtype == src.dtype
+    np.testing.assert_array_equal(got, want.numpy())
+
+
+@pytest.mark.parametrize("use_map", [False, True])
+def test_scatter_matches_index_copy(use_map):
+    batch, n, hkv, D = 4, 32, 2, 8
+    r = np.random.default_rng(2)
+    L = r.integers(40, 80, size=batch)
+    seq_start = np.concatenate([[0], np.cumsum(L)[:-1]])
+    rows = int(L.sum())
+    cache_k = r.standard_normal((rows, hkv, D)).astype(np.float32)
+    cache_v = r.standard_normal((rows, hkv, D)).astype(np.float32)
+    idx, count, cu = _sel(batch, n, 10, 3)
+    new_k = r.standard_normal((int(cu[-1]), hkv, D)).astype(np.float32)
+    new_v = r.standard_normal((int(cu[-1]), hkv, D)).astype(np.float32)
+    pos_map = np.stack([r.permutation(n) + 5 for _ in range(batch)]) if use_map else None
+    row_base = seq_start + (L - n - 5 if use_map else L - n)
+    ok, ov = oracle.kv_scatter(new_k, new_v, idx, count, cu, row_base, cache_k, cache_v, pos_map)
+    dest = []
+    for b in range(batch):
+        for t in range(count[b]):
+            j = idx[b, t]
+            dest.append(row_base[b] + (pos_map[b, j] if use_map else j))
+    dest = torch.tensor(dest, dtype=torch.int64)
+    for new, cache, got in ((new_k, cache_k, ok), (new_v, cache_v, ov)):
+        want = torch.from_numpy(cache.copy()).index_copy_(0, dest, torch.from_numpy(new))
+        np.testing.assert_array_equal(got, want.numpy())
+        untouched = np.setdiff1d(np.arange(rows), dest.numpy())
+        np.testing.assert_array_equal(got[untouched], cache[untouched])   # bit-identical
+
+
+def _attn_case(seed, batch=3, hq=8, hkv=2, D=16):
+    r = np.random.default_rng(seed)
+    L = r.integers(1, 70, size=batch).astype(np.int32)
+    seq_start = np.concatenate([[0], np.cumsum(L)[:-1]]).astype(np.int64)
+    rows = int(L.sum())
+    count = r.integers(0, 6, size=batch).astype(np.int32)
+    cu = np.zeros(batch + 1, np.int32); cu[1:] = np.cumsum(count)
+    q = r.standard_normal((int(cu[-1]), hq, D))
+    ck = r.standard_normal((rows, hkv, D)); cv = r.standard_normal((rows, hkv, D))
+    return q, count, cu, ck, cv, seq_start, L
+
+
+def test_attention_matches_torch_sdpa():
+    hq, hkv, D = 8, 2, 16
+    q, count, cu, ck, cv, ss, L = _attn_case(5, hq=hq, hkv=hkv, D=D)
+    scale = 1.0 / np.sqrt(D)
+    got = oracle.reduced_attention(q, count, cu, ck, cv, ss, L, hq, hkv, scale)
+    for b in range(len(count)):
+        if count[b] == 0:
+            continue
+        qq = torch.from_numpy(q[cu[b]:cu[b + 1]]).transpose(0, 1)            # [hq, n, D]
+        kk = torch.from_numpy(ck[ss[b]:ss[b] + L[b]]).transpose(0, 1)
+        vv = torch.from_numpy(cv[ss[b]:ss[b] + L[b]]).transpose(0, 1)
+        kk = kk.repeat_interleave(hq // hkv, 0); vv = vv.repeat_interleave(hq // hkv, 0)
+        want = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, scale=scale)
+        np.testing.assert_allclose(got[cu[b]:cu[b + 1]], want.transpose(0, 1).numpy(),
+                                   rtol=1e-10, atol=1e-12)
+
+
+def test_attention_closed_forms():
+    hq, hkv, D = 4, 1, 8
+    r = np.random.default_rng(6)
+    q = r.standard_normal((3, hq, D))
+    count = np.array([1, 1, 1], np.int32); cu = np.array([0, 1, 2, 3], np.int32)
+    ck = r.standard_normal((1 + 5 + 4, hkv, D)); cv = r.standard_normal(ck.shape)
+    ck[1:6] = ck[1]                                    # seq 1: five identical keys
+    ck[6:10] = 0.0; ck[6 + 2] = 50.0 * q[2, 0] / np.linalg.norm(q[2, 0]) ** 2 * np.sqrt(D)
+    ss = np.array([0, 1, 6], np.int64); L = np.array([1, 5, 4], np.int32)
+    out = oracle.reduced_attention(q, count, cu, ck, cv, ss, L, hq, hkv, 1 / np.sqrt(D))
+    np.testing.assert_array_equal(out[0], np.broadcast_to(cv[0, 0], (hq, D)))   # kv_len 1 -> V0
+    np.testing.assert_allclose(out[1], np.broadcast_to(cv[1:6, 0].mean(0), (hq, D)), rtol=1e-12)
+    np.testing.assert_allclose(out[2, 0], cv[8, 0], atol=1e-15)               # logit 50 dominates
+
+
+def test_attention_key_permutation_invariance():
+    hq, hkv, D = 8, 2, 16
+    q, count, cu, ck, cv, ss, L = _attn_case(7, hq=hq, hkv=hkv, D=D)
+    base = oracle.reduced_attention(q, count, cu, ck, cv, ss, L, hq, hkv, 0.25)
+    perm = np.arange(ck.shape[0])
+    for b in range(len(L)):
+        perm[ss[b]:ss[b] + L[b]] = ss[b] + np.random.default_rng(b).permutation(L[b])
+    got = oracle.reduced_attention(q, count, cu, ck[perm], cv[perm], ss, L, hq, hkv, 0.25)
+    np.testing.assert_allclose(got, base, rtol=1e-11, atol=1e-13)
