@@ -1,0 +1,204 @@
+"""Throughput of the block token-eviction hot path on one MI355X.
+
+One step = one pass of the FOCUS chain over the batch-1024 workload
+(block 32, 32 query / 8 KV heads, head dim 128, bf16, MaxPool 7, budgets
+K ~ U{4..12}, prefixes ~ U{1024..4096}, hidden 4096), all on one stream:
+
+    importance delta (layers 0/1) -> top-K -> gather -> KV scatter -> reduced attention
+
+Prints one JSON line: block tokens/s (batch * block / step time), per-kernel
+average durations from HIP events recorded on the launch stream, the
+roofline of the dominant kernel (reduced attention, HBM-bound) from its
+algorithmic bytes, and the CPU oracle timed on a bounded sample of the same
+workload. The ES-dLLM mode (score -> top-K -> gather -> scatter, batch 8) is
+timed as well and reported under "es_mode".
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+METRIC = "block tokens/s through score→top-K→gather→reduced attn; % of HBM/MFMA roofline"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path shards by sequence with no exchange, "
+              "so run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_token_eviction_amd as bte
+    from block_token_eviction_amd.chain import EsStep, FocusStep
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    fc, ac = W.CHAIN_FOCUS_B1024, W.CHAIN_ATTN_B1024
+    log("generating inputs on the device")
+    x = W.chain_inputs(fc, ac, device=dev)
+    step = FocusStep(fc.batch, fc.block, fc.hidden, fc.hq, fc.head_dim, fc.k_hi, fc.dtype, dev)
+    run_args = {k: x[k] for k in ("q0", "k0", "q1", "k1", "decoded", "k", "hidden_rows",
+                                  "pool_kernel", "new_k", "new_v", "q_kept", "cache_k", "cache_v",
+                                  "seq_start", "kv_len", "row_base")}
+    stages = [
+        ("focus_importance_delta", lambda: step.score(x["q0"], x["k0"], x["q1"], x["k1"], x["decoded"], fc.pool_kernel)),
+        ("topk_select", lambda: step.select(x["k"])),
+        ("gather_rows", lambda: step.gather(x["hidden_rows"])),
+        ("kv_scatter", lambda: step.scatter(x["new_k"], x["new_v"], x["row_base"], x["cache_k"], x["cache_v"])),
+        ("reduced_attention", lambda: step.attend(x["q_kept"], x["cache_k"], x["cache_v"], x["seq_start"], x["kv_len"])),
+    ]
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step.run(**run_args)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` full steps, per-stage events on the launch stream
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in stages] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for i, (_, fn) in enumerate(stages):
+            ev[s][i][0].record()
+            fn()
+            ev[s][i][1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {name: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
+                for i, (name, _) in enumerate(stages)}
+
+    # algorithmic bytes per launch (counts read back after the timed region)
+    count = step.count.cpu().numpy().astype(np.int64)
+    sum_k = int(count.sum())
+    kv_len = x["kv_len"].cpu().numpy().astype(np.int64)
+    es = 2
+    B, hq, hkv, D, H = fc.block, fc.hq, fc.hkv, fc.head_dim, fc.hidden
+    bytes_ = {
+        "focus_importance_delta": 2 * fc.batch * B * (hq + hkv) * D * es + fc.batch * B * (1 + 4),
+        "topk_select": fc.batch * B * 4 + fc.batch * 4 + fc.batch * (fc.k_hi + 2) * 4,
+        "gather_rows": 2 * sum_k * H * es,
+        "kv_scatter": 2 * 2 * sum_k * hkv * D * es,
+        "reduced_attention": int(kv_len.sum()) * hkv * D * es * 2 + 2 * sum_k * hq * D * es,
+    }
+    flops_attn = 0
+    for b in range(fc.batch):
+        flops_attn += 4 * int(count[b]) * hq * int(kv_len[b]) * D
+    kernels = {n: {"ms": round(stage_ms[n], 4), "algo_bytes": int(bytes_[n]),
+                   "GB/s": round(bytes_[n] / (stage_ms[n] * 1e-3) / 1e9, 1),
+                   "hbm_frac": round(bytes_[n] / (stage_ms[n] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+               for n in stage_ms}
+    dom = "reduced_attention"
+    achieved = bytes_[dom] / (stage_ms[dom] * 1e-3) / 1e9
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "algo_bytes_per_launch": int(bytes_[dom]),
+                "tflops": round(flops_attn / (stage_ms[dom] * 1e-3) / 1e12, 2)}
+    value = fc.batch * fc.block / (ms_step * 1e-3)
+
+    # ES-dLLM mode (auxiliary): batch 8, 256 survivors, keep 128
+    ec = W.ES_B8
+    ei = W.esdllm_inputs(ec, device=dev)
+    es_step = EsStep(ec.batch, ec.generated, ec.hidden, ec.keep, ec.dtype, dev)
+    es_args = dict(h_new=ei["h_new"], h_prev=ei["h_prev"], surv_pos=ei["surv_pos"], conf=ei["conf"],
+                   alpha=ei["alpha"], k=ei["k"], new_k=ei["new_k"], new_v=ei["new_v"],
+                   row_base=ei["row_base"], cache_k=ei["cache_k"], cache_v=ei["cache_v"])
+    for _ in range(3):
+        es_step.run(**es_args)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        es_step.run(**es_args)
+    e1.record()
+    torch.cuda.synchronize()
+    es_ms = e0.elapsed_time(e1) / args.steps
+    es_mode = {"workload": "esdllm_b8 (batch 8, 512+256 positions, hidden 4096, keep 128 of 256)",
+               "ms_per_step": round(es_ms, 4),
+               "survivor positions/s": round(ec.batch * ec.generated / (es_ms * 1e-3), 1)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(x, fc, ac)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "block tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V/hidden, Bernoulli decoded mask, U{4..12} budgets)",
+        "config": {"workload": "chain_b1024", "batch": fc.batch, "block": fc.block, "hq": hq,
+                   "hkv": hkv, "head_dim": D, "hidden": H, "pool_kernel": fc.pool_kernel,
+                   "k_range": [fc.k_lo, fc.k_hi], "prefix_range": [ac.prefix_lo, ac.prefix_hi],
+                   "kept_rows": sum_k, "kv_rows": int(kv_len.sum()), "parallelism": "none (1 GPU)"},
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "es_mode": es_mode,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(x, fc, ac, budget_s: float = 12.0):
+    """The float64 oracle on the first sequences of the same workload, chunk by
+    chunk until about `budget_s` seconds of CPU work; block tokens/s of that sample."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import oracle.chain as oc
+
+    def f64(t):
+        return t.detach().to("cpu", torch.float64).numpy()
+
+    def bits(t):
+        return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    seq_start = x["seq_start"].cpu().numpy()
+    kv_len = x["kv_len"].cpu().numpy()
+    done, elapsed, chunk = 0, 0.0, 16
+    log("cpu baseline (oracle)")
+    while done < fc.batch and elapsed < budget_s:
+        lo, hi = done, min(fc.batch, done + chunk)
+        r0, r1 = int(seq_start[lo]), int(seq_start[hi - 1] + kv_len[hi - 1])
+        cap = (hi - lo) * fc.k_hi
+        inp = dict(q0=f64(x["q0"][lo:hi]), k0=f64(x["k0"][lo:hi]), q1=f64(x["q1"][lo:hi]),
+                   k1=f64(x["k1"][lo:hi]), decoded=x["decoded"][lo:hi].cpu().numpy(),
+                   k=x["k"][lo:hi].cpu().numpy(), hidden_rows=bits(x["hidden_rows"][lo:hi]),
+                   pool_kernel=fc.pool_kernel, new_k=bits(x["new_k"][:cap]),
+                   new_v=bits(x["new_v"][:cap]), q_kept=bits(x["q_kept"][:cap]),
+                   cache_k=bits(x["cache_k"][r0:r1]), cache_v=bits(x["cache_v"][r0:r1]),
+                   seq_start=seq_start[lo:hi] - r0, kv_len=kv_len[lo:hi],
+                   row_base=x["row_base"][lo:hi].cpu().numpy() - r0)
+        t0 = time.perf_counter()
+        oc.focus_step(**inp, hq=fc.hq, hkv=fc.hkv, k_max=fc.k_hi, scale=1.0 / math.sqrt(fc.head_dim))
+        elapsed += time.perf_counter() - t0
+        done = hi
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(done * fc.block / elapsed, 1), "unit": "block tokens/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"first {done} of {fc.batch} sequences of chain_b1024, whole step, "
+                      f"{elapsed:.1f} s (numpy float64; BLAS threads = {threads})"}
+
+
+if __name__ == "__main__":
+    main()

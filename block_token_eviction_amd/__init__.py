@@ -1,0 +1,199 @@
+"""Python binding of libbte, the MI355X (gfx950) block token-eviction library.
+
+Argument marshalling only: every function checks tensor shapes, dtypes and
+devices on the host, passes raw device pointers and the current HIP stream
+to the C ABI declared in ``include/bte.h``, and raises on a nonzero status.
+All arithmetic runs in the library's HIP kernels. There is no fallback: if
+``libbte.so`` is missing or fails to load, importing this package raises.
+
+Names follow the C ABI: ``focus_importance_delta``, ``esdllm_score``,
+``topk_select``, ``gather_rows``, ``kv_scatter``, ``reduced_attention``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["lib", "LIB_PATH", "BteError", "status_string", "focus_importance_delta",
+           "esdllm_score", "topk_select", "gather_rows", "kv_scatter", "reduced_attention",
+           "BTE_F32", "BTE_BF16"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbte.so")
+BTE_F32, BTE_BF16 = 0, 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python -m block_token_eviction_amd.build` (hipcc, gfx950)")
+lib = ctypes.CDLL(LIB_PATH)
+
+_p, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIG = {
+    "bte_status_string": ([_i], ctypes.c_char_p),
+    "bte_version": ([], _i),
+    "bte_focus_importance_delta": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p], _i),
+    "bte_esdllm_score": ([_p, _p, _p, _p, _f, _p, _i, _i, _i, _i, _i, _p], _i),
+    "bte_topk_select": ([_p, _p, _p, _p, _p, _i, _i, _i, _p], _i),
+    "bte_gather_rows": ([_p, _p, _p, _p, _p, _i, _i, _i, _sz, _p], _i),
+    "bte_kv_scatter": ([_p, _p, _p, _p, _p, _p, _i, _p, _p, _p, _i, _i, _sz, _p], _i),
+    "bte_reduced_attention": ([_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p], _i),
+}
+for _name, (_args, _res) in _SIG.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+
+class BteError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({status_string(status)})")
+        self.status = status
+
+
+def status_string(status: int) -> str:
+    return lib.bte_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise BteError(fn, status)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("libbte works on device tensors only")
+            if not t.is_contiguous():
+                raise ValueError("libbte needs contiguous tensors")
+
+
+def _dtype(t) -> int:
+    if t.dtype == torch.bfloat16:
+        return BTE_BF16
+    if t.dtype == torch.float32:
+        return BTE_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _want(t, dtype, name):
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def focus_importance_delta(q0, k0, q1, k1, decoded, pool_kernel: int, out=None):
+    """q* [batch, B, hq, D], k* [batch, B, hkv, D], decoded uint8 [batch, B] -> delta f32 [batch, B]."""
+    _dev(q0, k0, q1, k1, decoded, out)
+    batch, block, hq, d = q0.shape
+    hkv = k0.shape[2]
+    for t in (q1,):
+        assert t.shape == q0.shape and t.dtype == q0.dtype
+    for t in (k0, k1):
+        assert t.shape == (batch, block, hkv, d) and t.dtype == q0.dtype
+    _want(decoded, torch.uint8, "decoded")
+    assert decoded.shape == (batch, block)
+    if out is None:
+        out = torch.empty((batch, block), dtype=torch.float32, device=q0.device)
+    _want(out, torch.float32, "out")
+    _check("bte_focus_importance_delta", lib.bte_focus_importance_delta(
+        _ptr(q0), _ptr(k0), _ptr(q1), _ptr(k1), _ptr(decoded), _ptr(out), batch, block, hq, hkv,
+        d, pool_kernel, _dtype(q0), _stream()))
+    return out
+
+
+def esdllm_score(h_new, h_prev, surv_pos, conf, alpha: float, out=None):
+    """h_new [batch, n_surv, h], h_prev [batch, L, h], surv_pos int32, conf f32 [batch, L]."""
+    _dev(h_new, h_prev, surv_pos, conf, out)
+    batch, n_surv, hidden = h_new.shape
+    seq_len = h_prev.shape[1]
+    assert h_prev.shape == (batch, seq_len, hidden) and h_prev.dtype == h_new.dtype
+    _want(surv_pos, torch.int32, "surv_pos")
+    _want(conf, torch.float32, "conf")
+    assert surv_pos.shape == (batch, n_surv) and conf.shape == (batch, seq_len)
+    if out is None:
+        out = torch.empty((batch, n_surv), dtype=torch.float32, device=h_new.device)
+    _check("bte_esdllm_score", lib.bte_esdllm_score(
+        _ptr(h_new), _ptr(h_prev), _ptr(surv_pos), _ptr(conf), float(alpha), _ptr(out), batch,
+        n_surv, seq_len, hidden, _dtype(h_new), _stream()))
+    return out
+
+
+def topk_select(scores, k, k_max: int, idx=None, count=None, cu=None):
+    """scores f32 [batch, n], k int32 [batch] -> (idx [batch, k_max], count [batch], cu [batch+1])."""
+    _dev(scores, k, idx, count, cu)
+    _want(scores, torch.float32, "scores")
+    _want(k, torch.int32, "k")
+    batch, n = scores.shape
+    dev = scores.device
+    if idx is None:
+        idx = torch.empty((batch, max(k_max, 0)), dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty((batch,), dtype=torch.int32, device=dev)
+    if cu is None:
+        cu = torch.empty((batch + 1,), dtype=torch.int32, device=dev)
+    _check("bte_topk_select", lib.bte_topk_select(
+        _ptr(scores), _ptr(k), _ptr(idx) if k_max > 0 else None, _ptr(count), _ptr(cu), batch, n,
+        k_max, _stream()))
+    return idx, count, cu
+
+
+def gather_rows(src, idx, count, cu, out=None):
+    """src [batch, n, ...] -> out [capacity, ...]; rows cu[b]+t for t < count[b] are written.
+
+    Without `out`, the capacity is batch * k_max rows (the device-side total is
+    not read back)."""
+    _dev(src, idx, count, cu, out)
+    batch, n = src.shape[:2]
+    k_max = idx.shape[1]
+    row_bytes = src[0, 0].numel() * src.element_size()
+    if out is None:
+        out = torch.empty((batch * k_max,) + tuple(src.shape[2:]), dtype=src.dtype, device=src.device)
+    assert out.dtype == src.dtype and out[0].numel() * out.element_size() == row_bytes
+    _check("bte_gather_rows", lib.bte_gather_rows(
+        _ptr(src), _ptr(idx), _ptr(count), _ptr(cu), _ptr(out), batch, n, k_max, row_bytes,
+        _stream()))
+    return out
+
+
+def kv_scatter(new_k, new_v, idx, count, cu, row_base, cache_k, cache_v, pos_map=None):
+    """Write new_k/new_v rows cu[b]+t into cache rows row_base[b] + pos (in place)."""
+    _dev(new_k, new_v, idx, count, cu, row_base, cache_k, cache_v, pos_map)
+    _want(row_base, torch.int64, "row_base")
+    batch, k_max = idx.shape
+    row_bytes = cache_k[0].numel() * cache_k.element_size()
+    assert new_k[0].numel() * new_k.element_size() == row_bytes
+    n = 0 if pos_map is None else pos_map.shape[1]
+    _check("bte_kv_scatter", lib.bte_kv_scatter(
+        _ptr(new_k), _ptr(new_v), _ptr(idx), _ptr(count), _ptr(cu), _ptr(pos_map), n,
+        _ptr(row_base), _ptr(cache_k), _ptr(cache_v), batch, k_max, row_bytes, _stream()))
+    return cache_k, cache_v
+
+
+def reduced_attention(q, count, cu, cache_k, cache_v, seq_start, kv_len, k_max: int,
+                      scale: float | None = None, out=None):
+    """q [capacity, hq, D], cache [rows, hkv, D] -> out [capacity, hq, D] (rows cu[b]+t written)."""
+    _dev(q, count, cu, cache_k, cache_v, seq_start, kv_len, out)
+    _want(seq_start, torch.int64, "seq_start")
+    _want(kv_len, torch.int32, "kv_len")
+    hq, d = q.shape[1], q.shape[2]
+    hkv = cache_k.shape[1]
+    batch = count.shape[0]
+    assert cache_v.shape == cache_k.shape and cache_k.dtype == q.dtype
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _check("bte_reduced_attention", lib.bte_reduced_attention(
+        _ptr(q), _ptr(count), _ptr(cu), _ptr(cache_k), _ptr(cache_v), _ptr(seq_start),
+        _ptr(kv_len), _ptr(out), batch, k_max, hq, hkv, d, float(scale), _dtype(q), _stream()))
+    return out

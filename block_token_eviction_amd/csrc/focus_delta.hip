@@ -1,0 +1,311 @@
+// FOCUS importance delta on gfx950.
+//
+// Computes, per sequence b and block key j (FOCUS: DLLMs Know How to Tame
+// Their Compute Bound, Section 3.1 Eq. 2 and Section 3.2 Eq. 3; App. E.2.1):
+//   I_l[j]  = sum_{h, i} softmax_j( maxpool_j( q_l[i,h] . k_l[j,g(h)] / sqrt(D) ) )
+//   dI[j]   = I_1[j] - I_0[j], -inf where decoded.
+//
+// Work layout: one workgroup per sequence, one wave per KV-head group g
+// (looping when there are more groups than waves). A wave keeps the group's
+// key tiles of both layers in registers and streams the G query-head tiles of
+// each layer through a 2-deep register ring, so that the next 8 KB tile is in
+// flight while one is being reduced.
+//
+// Score tile: S^T = K . Q^T on the matrix cores, keys as MFMA rows and query
+// rows as MFMA columns. Key row m of the MFMA is fed from block key
+// pi(m) = 16*((m/4)%2) + m%4 + 4*(m/8), which makes lane l own query row l%32
+// and the 16 contiguous keys 16*(l/32) .. +15 in registers 0..15. Pooling,
+// row max, exp and row sum are then in-lane; the only cross-lane traffic per
+// tile is the R boundary keys and two scalars with lane l^32. Column sums are
+// accumulated per lane over all tiles and reduced across lanes and waves once,
+// in a fixed order (no atomics), so results are bitwise reproducible and two
+// identical layers give dI = +0.0 exactly.
+#include <math.h>
+
+#include "bte_device.h"
+
+namespace bte {
+namespace {
+
+constexpr int kRing = 2;
+
+// This lane's half of one D-element row: elements [h*D/2, (h+1)*D/2).
+template <int D, bool BF16>
+struct HalfRow {
+  static constexpr int kBytes = BF16 ? D : 2 * D;
+  static constexpr int kN = kBytes / 16;
+  u32x4 v[kN];
+};
+
+template <int D, bool BF16>
+__device__ __forceinline__ void load_half(HalfRow<D, BF16>& r, const char* row, int h, bool valid) {
+  const char* p = row + h * HalfRow<D, BF16>::kBytes;
+#pragma unroll
+  for (int c = 0; c < HalfRow<D, BF16>::kN; ++c) {
+    r.v[c] = valid ? ld16_stream(p + 16 * c) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// S^T tile (32 keys x 32 query rows): contraction over the lane-halves' D/2
+// elements each; both operands use the same element order, so the sum is
+// over all D.
+template <int D, bool BF16>
+__device__ __forceinline__ f32x16 score_tile(const HalfRow<D, BF16>& k, const HalfRow<D, BF16>& q) {
+  f32x16 acc = {};
+  if constexpr (BF16) {
+#pragma unroll
+    for (int c = 0; c < HalfRow<D, BF16>::kN; ++c) acc = mfma_bf16(k.v[c], q.v[c], acc);
+  } else {
+#pragma unroll
+    for (int c = 0; c < HalfRow<D, BF16>::kN; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc = mfma_f32(__uint_as_float(k.v[c][e]), __uint_as_float(q.v[c][e]), acc);
+  }
+  return acc;
+}
+
+// Max over windows of 2R+1 entries of ext (16 + 2R entries): out[r] covers
+// ext[r .. r + 2R]. Doubling: after the pass of width w, a[x] = max(ext[x..x+2w-1]).
+template <int R>
+__device__ __forceinline__ void sliding_max(float (&ext)[16 + 2 * R], float (&out)[16]) {
+  constexpr int W = 2 * R + 1;
+  constexpr int N = 16 + 2 * R;
+  if constexpr (R == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) out[r] = ext[r];
+  } else {
+    float a[N];
+#pragma unroll
+    for (int x = 0; x < N; ++x) a[x] = ext[x];
+    int w = 1;
+#pragma unroll
+    for (int pass = 0; pass < 5; ++pass) {
+      if (2 * w <= W) {
+#pragma unroll
+        for (int x = 0; x + w < N; ++x) a[x] = fmaxf(a[x], a[x + w]);
+        w *= 2;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) out[r] = fmaxf(a[r], a[r + W - w]);
+  }
+}
+
+// Pool along keys (radius R, compile time; R < 0 selects the runtime radius
+// rt_r), softmax over the row, and add the row's weights into acc.
+// s[r] is the score of this lane's query row with key 16*h + r (masked keys
+// are -inf). row_ok = 0 for padding query rows.
+template <int R>
+__device__ __forceinline__ void pool_softmax_accumulate(const f32x16& s, int h, int rt_r, float c,
+                                                        bool row_ok, float (&acc)[16]) {
+  float m = s[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) m = fmaxf(m, s[r]);
+  m = fmaxf(m, swap_halves(m));
+
+  float p[16];
+  if constexpr (R >= 0) {
+    float ext[16 + 2 * R];
+    if constexpr (R > 0) {
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        // lower half sends its top R keys, upper half its bottom R keys
+        const float recv = swap_halves(h ? s[t] : s[16 - R + t]);
+        ext[t] = h ? recv : -INFINITY;                 // keys 16h - R + t
+        ext[R + 16 + t] = h ? -INFINITY : recv;        // keys 16h + 16 + t
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ext[R + r] = s[r];
+    sliding_max<R>(ext, p);
+  } else {
+    // Any radius: bring the whole 32-key row into the lane.
+    float full[32];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float o = swap_halves(s[r]);
+      full[r] = h ? o : s[r];
+      full[16 + r] = h ? s[r] : o;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 16 * h + r;
+      float v = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const int d = j - key;
+        v = (d <= rt_r && -d <= rt_r) ? fmaxf(v, full[j]) : v;
+      }
+      p[r] = v;
+    }
+  }
+
+  const float mc = m * c;
+  float e[16];
+  float sum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    e[r] = fast_exp2(fmaf(p[r], c, -mc));
+    sum += e[r];
+  }
+  sum += swap_halves(sum);
+  const float inv = row_ok ? 1.0f / sum : 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = fmaf(e[r], inv, acc[r]);
+}
+
+template <int D, bool BF16, int R>
+__global__ __launch_bounds__(512) void focus_delta_kernel(
+    const char* __restrict__ q0, const char* __restrict__ k0, const char* __restrict__ q1,
+    const char* __restrict__ k1, const uint8_t* __restrict__ decoded, float* __restrict__ out,
+    int B, int hq, int hkv, int rt_r, float c) {
+  constexpr int ES = BF16 ? 2 : 4;
+  using Row = HalfRow<D, BF16>;
+  __shared__ float red[16][2][32];
+
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int n = lane & 31;
+  const int h = lane >> 5;
+  const int G = hq / hkv;
+  const size_t qrow = (size_t)hq * D * ES;
+  const size_t krow = (size_t)hkv * D * ES;
+  const int kj = 16 * ((n >> 2) & 1) + (n & 3) + 4 * (n >> 3);
+  const bool kvalid = kj < B;
+  const bool qvalid = n < B;
+  const char* qbase0 = q0 + ((size_t)b * B + n) * qrow;
+  const char* qbase1 = q1 + ((size_t)b * B + n) * qrow;
+
+  float acc0[16], acc1[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
+
+  for (int g = w; g < hkv; g += nw) {
+    Row K0, K1;
+    load_half<D, BF16>(K0, k0 + ((size_t)b * B + kj) * krow + (size_t)g * D * ES, h, kvalid);
+    load_half<D, BF16>(K1, k1 + ((size_t)b * B + kj) * krow + (size_t)g * D * ES, h, kvalid);
+    // Query tiles in the order (head e, layer l) = (0,0), (0,1), (1,0), ...
+    const int ntile = 2 * G;
+    auto qtile = [&](Row& dst, int t) {
+      if (t < ntile) {
+        const size_t off = (size_t)(g * G + (t >> 1)) * D * ES;
+        load_half<D, BF16>(dst, ((t & 1) ? qbase1 : qbase0) + off, h, qvalid);
+      }
+    };
+    Row ring[kRing];
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) qtile(ring[s], s);
+
+    auto step = [&](Row& slot, int t) {
+      if (t < ntile) {
+        if (t & 1) {
+          f32x16 s = score_tile<D, BF16>(K1, slot);
+          if (B < 32) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = (16 * h + r < B) ? s[r] : -INFINITY;
+          }
+          qtile(slot, t + kRing);
+          pool_softmax_accumulate<R>(s, h, rt_r, c, qvalid, acc1);
+        } else {
+          f32x16 s = score_tile<D, BF16>(K0, slot);
+          if (B < 32) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = (16 * h + r < B) ? s[r] : -INFINITY;
+          }
+          qtile(slot, t + kRing);
+          pool_softmax_accumulate<R>(s, h, rt_r, c, qvalid, acc0);
+        }
+      }
+    };
+    for (int t = 0; t < ntile; t += kRing) {
+#pragma unroll
+      for (int u = 0; u < kRing; ++u) step(ring[u], t + u);
+    }
+  }
+
+  // Sum over the 32 query rows held by each lane half (fixed butterfly order).
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+#pragma unroll
+    for (int x = 1; x < 32; x <<= 1) {
+      acc0[r] += __shfl_xor(acc0[r], x, kWave);
+      acc1[r] += __shfl_xor(acc1[r], x, kWave);
+    }
+  }
+  if (n == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      red[w][0][16 * h + r] = acc0[r];
+      red[w][1][16 * h + r] = acc1[r];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < B) {
+    const int j = threadIdx.x;
+    float i0 = 0.f, i1 = 0.f;
+    for (int v = 0; v < nw; ++v) {
+      i0 += red[v][0][j];
+      i1 += red[v][1][j];
+    }
+    out[(size_t)b * B + j] = decoded[(size_t)b * B + j] ? -INFINITY : i1 - i0;
+  }
+}
+
+template <int D, bool BF16, int R>
+hipError_t launch_r(const void* q0, const void* k0, const void* q1, const void* k1,
+                    const uint8_t* decoded, float* out, int batch, int B, int hq, int hkv, int rt_r,
+                    float c, hipStream_t stream) {
+  const int waves = hkv < 8 ? hkv : 8;
+  hipLaunchKernelGGL((focus_delta_kernel<D, BF16, R>), dim3(batch), dim3(64 * waves), 0, stream,
+                     (const char*)q0, (const char*)k0, (const char*)q1, (const char*)k1, decoded,
+                     out, B, hq, hkv, rt_r, c);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16>
+hipError_t launch_d(const void* q0, const void* k0, const void* q1, const void* k1,
+                    const uint8_t* decoded, float* out, int batch, int B, int hq, int hkv, int r,
+                    float c, hipStream_t stream) {
+  switch (r) {
+    case 0: return launch_r<D, BF16, 0>(q0, k0, q1, k1, decoded, out, batch, B, hq, hkv, r, c, stream);
+    case 1: return launch_r<D, BF16, 1>(q0, k0, q1, k1, decoded, out, batch, B, hq, hkv, r, c, stream);
+    case 2: return launch_r<D, BF16, 2>(q0, k0, q1, k1, decoded, out, batch, B, hq, hkv, r, c, stream);
+    case 3: return launch_r<D, BF16, 3>(q0, k0, q1, k1, decoded, out, batch, B, hq, hkv, r, c, stream);
+    default: return launch_r<D, BF16, -1>(q0, k0, q1, k1, decoded, out, batch, B, hq, hkv, r, c, stream);
+  }
+}
+
+}  // namespace
+}  // namespace bte
+
+extern "C" int bte_focus_importance_delta(const void* q0, const void* k0, const void* q1,
+                                          const void* k1, const uint8_t* decoded, float* delta_out,
+                                          int batch, int block, int hq, int hkv, int head_dim,
+                                          int pool_kernel, bte_dtype dtype, hipStream_t stream) {
+  using namespace bte;
+  if (!q0 || !k0 || !q1 || !k1 || !decoded || !delta_out) return BTE_ERR_NULL;
+  if (batch <= 0 || hq <= 0 || hkv <= 0 || block < 1 || hq % hkv != 0) return BTE_ERR_DIM;
+  if (block > 32) return BTE_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return BTE_ERR_UNSUPPORTED;
+  if (pool_kernel < 1 || pool_kernel % 2 == 0) return BTE_ERR_UNSUPPORTED;
+  if (dtype != BTE_F32 && dtype != BTE_BF16) return BTE_ERR_UNSUPPORTED;
+  if (!aligned16(q0) || !aligned16(k0) || !aligned16(q1) || !aligned16(k1)) return BTE_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(delta_out) & 3u) != 0) return BTE_ERR_ALIGN;
+  // Radii beyond the block are all equivalent to "whole row".
+  const int r = (pool_kernel - 1) / 2 > 32 ? 32 : (pool_kernel - 1) / 2;
+  const float c = (float)(1.4426950408889634 / sqrt((double)head_dim));
+  hipError_t e;
+  if (dtype == BTE_BF16) {
+    e = head_dim == 128
+            ? launch_d<128, true>(q0, k0, q1, k1, decoded, delta_out, batch, block, hq, hkv, r, c, stream)
+            : launch_d<64, true>(q0, k0, q1, k1, decoded, delta_out, batch, block, hq, hkv, r, c, stream);
+  } else {
+    e = head_dim == 128
+            ? launch_d<128, false>(q0, k0, q1, k1, decoded, delta_out, batch, block, hq, hkv, r, c, stream)
+            : launch_d<64, false>(q0, k0, q1, k1, decoded, delta_out, batch, block, hq, hkv, r, c, stream);
+  }
+  return e == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
+}

@@ -1,0 +1,346 @@
+// Reduced-query GQA attention over prefix + block KV, gfx950.
+//
+// For kept row r of sequence b and query head h (KV head g = h / G):
+//   o = softmax_j(scale * q[r,h] . K[seq_start[b] + j, g]) . V[...],  j < kv_len[b]
+// (FOCUS paper Section 2 / Table 2, KV-cache attention over the exact cache;
+// Section 4.2, later layers on the kept rows only with the evicted tokens as
+// fixed reference KV; App. E.2.4, attention for ragged non-contiguous queries.
+// ES-dLLM notes page, key design 2: survivors read the whole cached KV.)
+//
+// Work item: one workgroup per (sequence b, KV head g, group of 32*T query
+// rows); the group's rows are the kept tokens' G query heads that share KV
+// head g (row = token * G + head-in-group), so every K/V byte of the sequence
+// is read once per KV head. The 4 waves split the key tiles (32 keys each)
+// round-robin, each keeping a private flash-style state (running max, sum and
+// output) and the 4 states are merged in LDS in a fixed order at the end: no
+// HBM workspace and no second launch.
+//
+// Per key tile: S^T = K . Q^T on the matrix cores (keys as MFMA rows fed in a
+// permuted order so that lane l owns query column l%32 and the 16 contiguous
+// keys 16*(l/32)..+15), online softmax in fp32 in-lane, then O^T += V^T . P^T
+// on the matrix cores. V must be read key-by-key per output column, so the
+// tile is staged in a per-wave LDS buffer whose 16-byte chunks are XOR-
+// swizzled by key (conflict-free 16-byte writes and 2-byte column reads).
+// K and V tiles for the wave's next tile are requested as soon as the current
+// ones have been consumed, so one 16 KB tile per wave is always in flight.
+#include <math.h>
+
+#include "bte_device.h"
+
+namespace bte {
+namespace {
+
+constexpr int kWaves = 4;
+
+template <int D, bool BF16>
+struct Cfg {
+  static constexpr int ES = BF16 ? 2 : 4;
+  static constexpr int kRowBytes = D * ES;            // one head's K or V row
+  static constexpr int kChunks = kRowBytes / 16;      // 16-byte chunks per row
+  static constexpr int kHalf = kChunks / 2;           // chunks per lane half
+  static constexpr int kVTile = 32 * kRowBytes;       // LDS bytes of one V tile
+  static constexpr int kOStride = D + 1;              // floats per row of the merge buffer
+  static constexpr int kMerge = kWaves * 32 * kOStride * 4 + 2 * kWaves * 32 * 4;
+  static constexpr int kLds = (kWaves * kVTile > kMerge) ? kWaves * kVTile : kMerge;
+};
+
+__device__ __forceinline__ int swz(int k) { return (k & 7) ^ (((k >> 4) & 1) << 2); }
+
+template <int D, bool BF16, int T>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T == 1 ? 2 : 1))) void attn_kernel(
+    const char* __restrict__ q, const int32_t* __restrict__ count, const int32_t* __restrict__ cu,
+    const char* __restrict__ cache_k, const char* __restrict__ cache_v,
+    const int64_t* __restrict__ seq_start, const int32_t* __restrict__ kv_len,
+    char* __restrict__ out, int hq, int hkv, int n_rg, float c) {
+  using C = Cfg<D, BF16>;
+  constexpr int ES = C::ES;
+  constexpr int DT = D / 32;                           // 32-wide output column tiles
+  __shared__ __attribute__((aligned(16))) char smem[C::kLds];
+
+  const int rg = blockIdx.x % n_rg;
+  const int bg = blockIdx.x / n_rg;
+  const int g = bg % hkv;
+  const int b = bg / hkv;
+  const int G = hq / hkv;
+  const int rows = count[b] * G;
+  const int row0 = rg * 32 * T;
+  if (row0 >= rows) return;
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int n = lane & 31;
+  const int h = lane >> 5;
+  const int L = kv_len[b];
+  const int64_t s0 = seq_start[b];
+  const int cub = cu[b];
+  const size_t kv_row = (size_t)hkv * C::kRowBytes;    // bytes per cache position
+  const char* kbase = cache_k + (size_t)s0 * kv_row + (size_t)g * C::kRowBytes;
+  const char* vbase = cache_v + (size_t)s0 * kv_row + (size_t)g * C::kRowBytes;
+
+  // Query operands (B of S^T): lane (n, h) holds half h of query row n.
+  u32x4 qop[T][C::kHalf];
+#pragma unroll
+  for (int tq = 0; tq < T; ++tq) {
+    const int rho = row0 + 32 * tq + n;
+    const bool ok = rho < rows;
+    const int tok = ok ? rho / G : 0;
+    const int head = g * G + (ok ? rho - tok * G : 0);
+    const char* p = q + (((size_t)(cub + tok)) * hq + head) * C::kRowBytes + h * (C::kRowBytes / 2);
+#pragma unroll
+    for (int cc = 0; cc < C::kHalf; ++cc) qop[tq][cc] = ok ? ld16(p + 16 * cc) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  float m[T], lsum[T];
+  f32x16 o[T][DT];
+#pragma unroll
+  for (int tq = 0; tq < T; ++tq) {
+    m[tq] = -INFINITY;
+    lsum[tq] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[tq][dt] = f32x16{};
+  }
+
+  const int ntiles = (L + 31) / 32;
+  const int kj = 16 * ((n >> 2) & 1) + (n & 3) + 4 * (n >> 3);   // key fed as MFMA row n
+  char* vt = smem + w * C::kVTile;                                 // this wave's V tile
+
+  u32x4 kreg[C::kHalf], vreg[C::kHalf];
+  auto load_tile = [&](int kt) {
+    const int keyk = kt * 32 + kj;
+    const int keyv = kt * 32 + n;
+    const bool okk = keyk < L, okv = keyv < L;
+    const char* pk = kbase + (size_t)keyk * kv_row + h * (C::kRowBytes / 2);
+    const char* pv = vbase + (size_t)keyv * kv_row + h * (C::kRowBytes / 2);
+#pragma unroll
+    for (int cc = 0; cc < C::kHalf; ++cc) {
+      kreg[cc] = okk ? ld16_stream(pk + 16 * cc) : u32x4{0u, 0u, 0u, 0u};
+      vreg[cc] = okv ? ld16_stream(pv + 16 * cc) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
+  if (w < ntiles) load_tile(w);
+  for (int kt = w; kt < ntiles; kt += kWaves) {
+    // S^T tiles: lane (n, h), register r = score of query row n with key kt*32 + 16h + r.
+    f32x16 s[T];
+#pragma unroll
+    for (int tq = 0; tq < T; ++tq) {
+      f32x16 acc = {};
+      if constexpr (BF16) {
+#pragma unroll
+        for (int cc = 0; cc < C::kHalf; ++cc) acc = mfma_bf16(kreg[cc], qop[tq][cc], acc);
+      } else {
+#pragma unroll
+        for (int cc = 0; cc < C::kHalf; ++cc)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc = mfma_f32(__uint_as_float(kreg[cc][e]), __uint_as_float(qop[tq][cc][e]), acc);
+      }
+      s[tq] = acc;
+    }
+    // Stage V: lane (key n, half h) writes its chunks at swizzled positions.
+#pragma unroll
+    for (int cc = 0; cc < C::kHalf; ++cc) {
+      const int chunk = h * C::kHalf + cc;
+      st16(vt + n * C::kRowBytes + ((chunk ^ swz(n)) << 4), vreg[cc]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (kt + kWaves < ntiles) load_tile(kt + kWaves);
+
+    const int kvalid = L - (kt * 32 + 16 * h);          // keys of this lane half that exist
+#pragma unroll
+    for (int tq = 0; tq < T; ++tq) {
+      if (kvalid < 16) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[tq][r] = r < kvalid ? s[tq][r] : -INFINITY;
+      }
+      float mt = s[tq][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[tq][r]);
+      mt = fmaxf(mt, swap_halves(mt));
+      const float mnew = fmaxf(m[tq], mt);
+      const float alpha = fast_exp2((m[tq] - mnew) * c);
+      const float mc = mnew * c;
+      float p[16];
+      float ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = fast_exp2(fmaf(s[tq][r], c, -mc));
+        ps += p[r];
+      }
+      lsum[tq] = fmaf(lsum[tq], alpha, ps);
+      m[tq] = mnew;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[tq][dt][r] *= alpha;
+
+      if constexpr (BF16) {
+        // B operand of O^T += V^T P^T: k-slot (h, t) of chunk cc is key 16h + 8cc + t.
+        u32x4 pb[2];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            pb[cc][u] = f32_to_bf16_bits(p[8 * cc + 2 * u]) |
+                        (f32_to_bf16_bits(p[8 * cc + 2 * u + 1]) << 16);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int d = 32 * dt + n;                     // A row: output column d
+          const int qd = (d * 2) >> 4, wd = (d * 2) & 15;
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            u32x4 a;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int k0 = 16 * h + 8 * cc + 2 * u;
+              const int k1 = k0 + 1;
+              const uint32_t lo = *reinterpret_cast<const uint16_t*>(
+                  vt + k0 * C::kRowBytes + ((qd ^ swz(k0)) << 4) + wd);
+              const uint32_t hi = *reinterpret_cast<const uint16_t*>(
+                  vt + k1 * C::kRowBytes + ((qd ^ swz(k1)) << 4) + wd);
+              a[u] = lo | (hi << 16);
+            }
+            o[tq][dt] = mfma_bf16(a, pb[cc], o[tq][dt]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int d = 32 * dt + n;
+          const int qd = (d * 4) >> 4, wd = (d * 4) & 15;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int k = 16 * h + i;
+            const float a = *reinterpret_cast<const float*>(vt + k * C::kRowBytes + ((qd ^ swz(k)) << 4) + wd);
+            o[tq][dt] = mfma_f32(a, p[i], o[tq][dt]);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // Merge the 4 wave states: out = sum_w e^(m_w - M) O_w / sum_w e^(m_w - M) l_w.
+  float* obuf = reinterpret_cast<float*>(smem);
+  float* mbuf = obuf + kWaves * 32 * C::kOStride;
+  float* lbuf = mbuf + kWaves * 32;
+#pragma unroll
+  for (int tq = 0; tq < T; ++tq) {
+    __syncthreads();
+    const float lt = lsum[tq] + swap_halves(lsum[tq]);
+    if (h == 0) {
+      mbuf[w * 32 + n] = m[tq];
+      lbuf[w * 32 + n] = lt;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = 32 * dt + 8 * (r >> 2) + 4 * h + (r & 3);
+        obuf[(w * 32 + n) * C::kOStride + d] = o[tq][dt][r];
+      }
+    __syncthreads();
+    const int rr = threadIdx.x >> 3;                     // query row of the tile
+    const int part = threadIdx.x & 7;                    // D/8 consecutive columns
+    const int rho = row0 + 32 * tq + rr;
+    if (rho < rows) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) M = fmaxf(M, mbuf[v * 32 + rr]);
+      float wgt[kWaves];
+      float Ls = 0.f;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) {
+        wgt[v] = fast_exp2((mbuf[v * 32 + rr] - M) * c);
+        Ls = fmaf(lbuf[v * 32 + rr], wgt[v], Ls);
+      }
+      const float inv = 1.0f / Ls;
+      const int tok = rho / G;
+      const int head = g * G + (rho - tok * G);
+      char* dst = out + (((size_t)(cub + tok)) * hq + head) * C::kRowBytes;
+      constexpr int DP = D / 8;
+      float res[DP];
+#pragma unroll
+      for (int i = 0; i < DP; ++i) {
+        const int d = part * DP + i;
+        float acc = 0.f;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) acc = fmaf(obuf[(v * 32 + rr) * C::kOStride + d], wgt[v], acc);
+        res[i] = acc * inv;
+      }
+      if constexpr (BF16) {
+#pragma unroll
+        for (int i = 0; i < DP; i += 8) {
+          u32x4 v;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            v[u] = f32_to_bf16_bits(res[i + 2 * u]) | (f32_to_bf16_bits(res[i + 2 * u + 1]) << 16);
+          st16(dst + (part * DP + i) * 2, v);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < DP; i += 4) {
+          u32x4 v = {__float_as_uint(res[i]), __float_as_uint(res[i + 1]),
+                     __float_as_uint(res[i + 2]), __float_as_uint(res[i + 3])};
+          st16(dst + (part * DP + i) * 4, v);
+        }
+      }
+    }
+  }
+}
+
+template <int D, bool BF16, int T>
+hipError_t launch(const void* q, const int32_t* count, const int32_t* cu, const void* ck,
+                  const void* cv, const int64_t* ss, const int32_t* kl, void* out, int batch,
+                  int k_max, int hq, int hkv, float c, hipStream_t stream) {
+  const int G = hq / hkv;
+  const long rows = (long)k_max * G;
+  const int n_rg = (int)((rows + 32 * T - 1) / (32 * T));
+  const long grid = (long)batch * hkv * n_rg;
+  if (grid > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_kernel<D, BF16, T>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream,
+                     (const char*)q, count, cu, (const char*)ck, (const char*)cv, ss, kl,
+                     (char*)out, hq, hkv, n_rg, c);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16>
+hipError_t launch_t(const void* q, const int32_t* count, const int32_t* cu, const void* ck,
+                    const void* cv, const int64_t* ss, const int32_t* kl, void* out, int batch,
+                    int k_max, int hq, int hkv, float c, hipStream_t stream) {
+  const long rows = (long)k_max * (hq / hkv);
+  if (rows > 32)
+    return launch<D, BF16, 2>(q, count, cu, ck, cv, ss, kl, out, batch, k_max, hq, hkv, c, stream);
+  return launch<D, BF16, 1>(q, count, cu, ck, cv, ss, kl, out, batch, k_max, hq, hkv, c, stream);
+}
+
+}  // namespace
+}  // namespace bte
+
+extern "C" int bte_reduced_attention(const void* q, const int32_t* count, const int32_t* cu,
+                                     const void* cache_k, const void* cache_v,
+                                     const int64_t* seq_start, const int32_t* kv_len, void* out,
+                                     int batch, int k_max, int hq, int hkv, int head_dim,
+                                     float scale, bte_dtype dtype, hipStream_t stream) {
+  using namespace bte;
+  if (!q || !count || !cu || !cache_k || !cache_v || !seq_start || !kv_len || !out)
+    return BTE_ERR_NULL;
+  if (batch <= 0 || k_max < 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0) return BTE_ERR_DIM;
+  if (head_dim != 64 && head_dim != 128) return BTE_ERR_UNSUPPORTED;
+  if (dtype != BTE_F32 && dtype != BTE_BF16) return BTE_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(cache_k) || !aligned16(cache_v) || !aligned16(out))
+    return BTE_ERR_ALIGN;
+  if (k_max == 0) return BTE_OK;
+  const float c = scale * kLog2e;
+  hipError_t e;
+  if (dtype == BTE_BF16)
+    e = head_dim == 128
+            ? launch_t<128, true>(q, count, cu, cache_k, cache_v, seq_start, kv_len, out, batch, k_max, hq, hkv, c, stream)
+            : launch_t<64, true>(q, count, cu, cache_k, cache_v, seq_start, kv_len, out, batch, k_max, hq, hkv, c, stream);
+  else
+    e = head_dim == 128
+            ? launch_t<128, false>(q, count, cu, cache_k, cache_v, seq_start, kv_len, out, batch, k_max, hq, hkv, c, stream)
+            : launch_t<64, false>(q, count, cu, cache_k, cache_v, seq_start, kv_len, out, batch, k_max, hq, hkv, c, stream);
+  if (e == hipErrorInvalidValue) return BTE_ERR_DIM;
+  return e == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
+}

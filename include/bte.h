@@ -1,0 +1,188 @@
+/*
+ * bte.h — C ABI of the block token-eviction hot path (MI355X / gfx950).
+ *
+ * One denoising step of block-diffusion decoding with token eviction:
+ * score every block token (FOCUS importance delta, or ES-dLLM's early-skip
+ * score), keep the top-K per sequence, gather the kept hidden rows, scatter
+ * the kept rows' new K/V into the exact KV cache, and run the kept queries'
+ * attention over prefix + block.
+ *
+ * Conventions for every call:
+ *   - Every array pointer is DEVICE memory owned by the caller; the library
+ *     allocates nothing, keeps no state between calls and never frees.
+ *   - Arrays are dense, row-major, in the layouts stated per argument, and
+ *     16-byte aligned unless stated otherwise.
+ *   - A call only validates its host-side arguments and enqueues kernels on
+ *     `stream`; it never synchronises. On a nonzero return nothing was
+ *     enqueued (BTE_ERR_LAUNCH: the launch itself failed).
+ *   - Device-side contents (indices in range, distinct scatter positions,
+ *     seq_start/kv_len consistent with the cache) are the caller's contract;
+ *     they are not checked.
+ *   - Calls on one stream run in order; outputs are deterministic (no
+ *     floating-point atomics; fixed reduction orders).
+ */
+#ifndef BTE_H_
+#define BTE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BTE_OK = 0,
+  BTE_ERR_NULL = -1,         /* a required pointer is NULL                        */
+  BTE_ERR_DIM = -2,          /* a size is out of range or inconsistent            */
+  BTE_ERR_UNSUPPORTED = -3,  /* valid request this build does not implement       */
+  BTE_ERR_ALIGN = -4,        /* a pointer or row size breaks the alignment rule   */
+  BTE_ERR_LAUNCH = -5        /* the HIP runtime rejected a kernel launch          */
+} bte_status;
+
+typedef enum { BTE_F32 = 0, BTE_BF16 = 1 } bte_dtype;
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* bte_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int bte_version(void);
+
+/*
+ * FOCUS importance delta (FOCUS: DLLMs Know How to Tame Their Compute Bound,
+ * Section 3.1 Eq. 2, Section 3.2 Eq. 3, App. E.2.1; FOCUS notes page, key
+ * design 1). For layer l in {0,1}, sequence b, query head h (KV head
+ * g = h / (hq/hkv)), block query row i and block key j:
+ *   S_l[h,i,j] = q_l[b,i,h,:] . k_l[b,j,g,:] / sqrt(head_dim)
+ *   P = MaxPool1D over j (window pool_kernel, stride 1, cut at block edges)
+ *   A = softmax over the `block` keys of each row of P
+ *   I_l[j] = sum over h < hq and i < block of A[h,i,j]
+ *   delta_out[b,j] = I_1[j] - I_0[j], or -INFINITY where decoded[b,j] != 0.
+ *
+ *   q0, q1   [batch, block, hq, head_dim]   dtype
+ *   k0, k1   [batch, block, hkv, head_dim]  dtype
+ *   decoded  [batch, block] uint8 (1 byte alignment)
+ *   delta_out[batch, block] float32 (4 byte alignment)
+ * Limits: 1 <= block <= 32; head_dim in {64, 128}; hq % hkv == 0;
+ * pool_kernel odd and >= 1 (>= 2*block-1 pools the whole row).
+ * Errors: NULL pointer -> BTE_ERR_NULL; batch/hq/hkv <= 0, block out of
+ * range or hq % hkv != 0 -> BTE_ERR_DIM; head_dim, even pool_kernel or
+ * dtype unsupported -> BTE_ERR_UNSUPPORTED.
+ */
+int bte_focus_importance_delta(const void* q0, const void* k0, const void* q1, const void* k1,
+                               const uint8_t* decoded, float* delta_out, int batch, int block,
+                               int hq, int hkv, int head_dim, int pool_kernel, bte_dtype dtype,
+                               hipStream_t stream);
+
+/*
+ * ES-dLLM early-skip importance score (ES-dLLM notes page, key design 1):
+ *   score[b,s] = alpha * conf[b,p] + (1 - alpha) * |x - y|_1 / (sqrt(hidden) * |y|_2)
+ * with p = surv_pos[b,s], x = h_new[b,s,:] (this iteration's hidden state of
+ * survivor s) and y = h_prev[b,p,:] (the cached previous iteration's state).
+ * An unchanged row (|x - y|_1 = 0) scores alpha * conf exactly; |y|_2 = 0 with
+ * a change gives +INFINITY in the variation term.
+ *
+ *   h_new    [batch, n_surv, hidden]   dtype
+ *   h_prev   [batch, seq_len, hidden]  dtype
+ *   surv_pos [batch, n_surv] int32 in [0, seq_len) (4 byte alignment)
+ *   conf     [batch, seq_len] float32 (4 byte alignment)
+ *   score_out[batch, n_surv] float32 (4 byte alignment)
+ * Limits: hidden * sizeof(dtype) a multiple of 16.
+ * Errors: NULL -> BTE_ERR_NULL; sizes <= 0 -> BTE_ERR_DIM; dtype or hidden
+ * unsupported -> BTE_ERR_UNSUPPORTED.
+ */
+int bte_esdllm_score(const void* h_new, const void* h_prev, const int32_t* surv_pos,
+                     const float* conf, float alpha, float* score_out, int batch, int n_surv,
+                     int seq_len, int hidden, bte_dtype dtype, hipStream_t stream);
+
+/*
+ * Per-sequence top-K (FOCUS paper Section 4.2: top-K masked tokens by delta;
+ * ES-dLLM notes page, key design 1: keep the top-(1-r)|S| survivors) and the
+ * prefix sum that places each sequence's kept rows (FOCUS paper App. E.2.3).
+ * A score is eligible unless it is NaN or -INFINITY. Positions are ranked by
+ * score descending, then index ascending (-0.0 equals +0.0).
+ *   count_out[b] = min(max(k[b], 0), #eligible in row b, k_max)
+ *   idx_out[b, 0..count-1] = the selected positions in ascending order;
+ *   idx_out[b, count..k_max-1] = -1
+ *   cu_out[0] = 0, cu_out[b+1] = cu_out[b] + count_out[b]
+ *
+ *   scores [batch, n] float32; k [batch] int32; idx_out [batch, k_max] int32;
+ *   count_out [batch] int32; cu_out [batch + 1] int32 (4 byte alignment each)
+ * Limits: 1 <= n <= 1024; k_max >= 0 (idx_out may be NULL when k_max == 0).
+ * Errors: NULL -> BTE_ERR_NULL; batch <= 0, n out of range, k_max < 0 ->
+ * BTE_ERR_DIM.
+ */
+int bte_topk_select(const float* scores, const int32_t* k, int32_t* idx_out, int32_t* count_out,
+                    int32_t* cu_out, int batch, int n, int k_max, hipStream_t stream);
+
+/*
+ * Gather-compaction of kept rows (FOCUS paper Section 4.2: H_reduced = H at
+ * the kept index set; App. E.2.3: destinations from a prefix sum):
+ *   dst[cu[b] + t, :] = src[b, idx[b,t], :]   for t < count[b]
+ * Rows are opaque byte strings of row_bytes bytes.
+ *
+ *   src [batch, n, row_bytes]; dst [>= cu[batch], row_bytes];
+ *   idx [batch, k_max], count [batch], cu [batch + 1] int32 (as written by
+ *   bte_topk_select)
+ * Limits: row_bytes a multiple of 16; count[b] <= k_max; 0 <= idx < n.
+ * Errors: NULL -> BTE_ERR_NULL; sizes <= 0 -> BTE_ERR_DIM; row_bytes or
+ * src/dst not 16-byte aligned -> BTE_ERR_ALIGN.
+ */
+int bte_gather_rows(const void* src, const int32_t* idx, const int32_t* count, const int32_t* cu,
+                    void* dst, int batch, int n, int k_max, size_t row_bytes, hipStream_t stream);
+
+/*
+ * In-place scatter of the kept rows' new K/V into the exact KV cache
+ * (ES-dLLM notes page, key design 2: partial cache update by in-place
+ * scatter, every other slot reused; FOCUS paper App. E.2.4: sparse KV cache
+ * filling at processing indices). For t < count[b]:
+ *   pos = pos_map ? pos_map[b, idx[b,t]] : idx[b,t]
+ *   cache_k[row_base[b] + pos, :] = new_k[cu[b] + t, :]   (same for V)
+ * Every other cache row is left untouched. Rows are opaque byte strings of
+ * row_bytes bytes (hkv * head_dim * element size for a K/V cache).
+ *
+ *   new_k, new_v [>= cu[batch], row_bytes]; cache_k, cache_v [rows, row_bytes]
+ *   idx [batch, k_max], count [batch], cu [batch + 1] int32
+ *   pos_map [batch, n] int32 or NULL (identity); row_base [batch] int64
+ * new_v and cache_v may both be NULL to scatter a single tensor.
+ * Limits: row_bytes a multiple of 16; target rows distinct within a call.
+ * Errors: NULL (or only one of new_v/cache_v NULL) -> BTE_ERR_NULL;
+ * sizes <= 0, or pos_map given with n <= 0 -> BTE_ERR_DIM; alignment ->
+ * BTE_ERR_ALIGN.
+ */
+int bte_kv_scatter(const void* new_k, const void* new_v, const int32_t* idx, const int32_t* count,
+                   const int32_t* cu, const int32_t* pos_map, int n, const int64_t* row_base,
+                   void* cache_k, void* cache_v, int batch, int k_max, size_t row_bytes,
+                   hipStream_t stream);
+
+/*
+ * Reduced-query GQA attention of the kept rows over prefix + block
+ * (FOCUS paper Section 2 / Table 2 KV-cache attention over the exact cache,
+ * Section 4.2: later layers run only on the kept rows, evicted tokens stay as
+ * fixed reference KV, App. E.2.4 ragged attention; ES-dLLM notes page, key
+ * design 2: survivors attend over the whole cached sequence). For kept row
+ * r = cu[b] + t (t < count[b]) and query head h with KV head g = h / (hq/hkv):
+ *   s_j = scale * q[r,h,:] . cache_k[seq_start[b] + j, g, :],  j < kv_len[b]
+ *   out[r,h,:] = sum_j softmax(s)_j * cache_v[seq_start[b] + j, g, :]
+ * No mask: each kept query sees the whole prefix and the whole block.
+ * Softmax and accumulation in float32; with BTE_BF16, the probabilities are
+ * rounded to bf16 for the P.V product and out is rounded once to bf16.
+ *
+ *   q, out [>= cu[batch], hq, head_dim] dtype
+ *   cache_k, cache_v [rows, hkv, head_dim] dtype
+ *   count [batch], cu [batch + 1] int32; seq_start [batch] int64;
+ *   kv_len [batch] int32 (>= 1 for every sequence with count > 0)
+ * Limits: head_dim in {64, 128}; hq % hkv == 0.
+ * Errors: NULL -> BTE_ERR_NULL; sizes <= 0, k_max < 0 or hq % hkv != 0 ->
+ * BTE_ERR_DIM; head_dim or dtype unsupported -> BTE_ERR_UNSUPPORTED.
+ */
+int bte_reduced_attention(const void* q, const int32_t* count, const int32_t* cu,
+                          const void* cache_k, const void* cache_v, const int64_t* seq_start,
+                          const int32_t* kv_len, void* out, int batch, int k_max, int hq, int hkv,
+                          int head_dim, float scale, bte_dtype dtype, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BTE_H_ */

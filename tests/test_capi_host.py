@@ -1,0 +1,113 @@
+"""Host-only checks of the C ABI (no GPU, no kernel launch): the library loads,
+exports every function that include/bte.h declares, and rejects invalid
+host-side arguments with the documented status codes before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bte.h")
+
+bte = pytest.importorskip("block_token_eviction_amd")
+lib = bte.lib
+OK, NULL, DIM, UNSUP, ALIGN = 0, -1, -2, -3, -4
+FAKE = ctypes.c_void_p(1 << 20)          # 16-byte aligned, never dereferenced on these paths
+MIS = ctypes.c_void_p((1 << 20) + 2)     # misaligned
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bte_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared()
+    assert len(names) == 8
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    for s in (OK, NULL, DIM, UNSUP, ALIGN, -5, 7):
+        assert bte.status_string(s)
+    assert lib.bte_version() >= 100
+
+
+def _focus(**kw):
+    a = dict(q0=FAKE, k0=FAKE, q1=FAKE, k1=FAKE, dec=FAKE, out=FAKE, batch=2, block=32, hq=8,
+             hkv=2, d=128, pool=7, dtype=1)
+    a.update(kw)
+    return lib.bte_focus_importance_delta(a["q0"], a["k0"], a["q1"], a["k1"], a["dec"], a["out"],
+                                          a["batch"], a["block"], a["hq"], a["hkv"], a["d"],
+                                          a["pool"], a["dtype"], None)
+
+
+def test_focus_errors():
+    assert _focus(q0=None) == NULL
+    assert _focus(dec=None) == NULL
+    assert _focus(batch=0) == DIM
+    assert _focus(hq=6, hkv=4) == DIM
+    assert _focus(block=0) == DIM
+    assert _focus(block=33) == UNSUP
+    assert _focus(d=96) == UNSUP
+    assert _focus(pool=4) == UNSUP
+    assert _focus(pool=0) == UNSUP
+    assert _focus(dtype=5) == UNSUP
+    assert _focus(k1=MIS) == ALIGN
+
+
+def test_esdllm_errors():
+    f = lib.bte_esdllm_score
+    assert f(None, FAKE, FAKE, FAKE, 0.5, FAKE, 1, 1, 1, 4096, 1, None) == NULL
+    assert f(FAKE, FAKE, FAKE, FAKE, 0.5, FAKE, 0, 1, 1, 4096, 1, None) == DIM
+    assert f(FAKE, FAKE, FAKE, FAKE, 0.5, FAKE, 1, 1, 1, 4100, 1, None) == UNSUP
+    assert f(FAKE, FAKE, FAKE, FAKE, 0.5, FAKE, 1, 1, 1, 4096, 9, None) == UNSUP
+    assert f(MIS, FAKE, FAKE, FAKE, 0.5, FAKE, 1, 1, 1, 4096, 1, None) == ALIGN
+
+
+def test_topk_errors():
+    f = lib.bte_topk_select
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 1, 32, 8, None) == NULL
+    assert f(FAKE, FAKE, None, FAKE, FAKE, 1, 32, 8, None) == NULL      # idx needed when k_max > 0
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 32, 8, None) == DIM
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, 8, None) == DIM
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1025, 8, None) == DIM
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 32, -1, None) == DIM
+
+
+def test_rows_errors():
+    g = lib.bte_gather_rows
+    assert g(None, FAKE, FAKE, FAKE, FAKE, 1, 32, 8, 8192, None) == NULL
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 32, 8, 8192, None) == DIM
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 32, 8, 8190, None) == ALIGN
+    assert g(FAKE, FAKE, FAKE, FAKE, MIS, 1, 32, 8, 8192, None) == ALIGN
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 32, 0, 8192, None) == OK   # nothing to do
+    s = lib.bte_kv_scatter
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, None, 1, 8, 2048, None) == NULL
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None, FAKE, FAKE, 1, 8, 2048, None) == NULL
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, 1, 8, 2048, None) == DIM
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, FAKE, 1, 8, 2040, None) == ALIGN
+    assert s(FAKE, None, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, None, 1, 0, 2048, None) == OK
+
+
+def test_attention_errors():
+    f = lib.bte_reduced_attention
+    args = [FAKE] * 8 + [4, 8, 32, 8, 128, 0.088, 1, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a0=None) == NULL
+    assert call(a7=None) == NULL
+    assert call(a8=0) == DIM
+    assert call(a9=-1) == DIM
+    assert call(a10=30) == DIM
+    assert call(a12=96) == UNSUP
+    assert call(a14=3) == UNSUP
+    assert call(a3=MIS) == ALIGN
+    assert call(a9=0) == OK

@@ -1,0 +1,124 @@
+"""GPU parity: reduced-query attention and the ES-dLLM score vs the float64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from helpers import assert_close, dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _bte():
+    import block_token_eviction_amd as bte
+    return bte
+
+
+def _attn(cfg, ai=None, rows=None):
+    bte = _bte()
+    ai = ai if ai is not None else W.attention_inputs(cfg)
+    g = dev(ai)
+    say(f"attention {cfg.name} batch={cfg.batch} hq={cfg.hq} hkv={cfg.hkv} D={cfg.head_dim} k_max={ai['k_max']}")
+    out = bte.reduced_attention(g["q"], g["count"], g["cu"], g["cache_k"], g["cache_v"],
+                                g["seq_start"], g["kv_len"], ai["k_max"])
+    torch.cuda.synchronize()
+    f64 = W.to_f64
+    ref = oracle.reduced_attention(f64(ai["q"]), ai["count"].numpy(), ai["cu"].numpy(),
+                                   f64(ai["cache_k"]), f64(ai["cache_v"]), ai["seq_start"].numpy(),
+                                   ai["kv_len"].numpy(), cfg.hq, cfg.hkv,
+                                   1.0 / math.sqrt(cfg.head_dim), rows=rows)
+    n = int(ai["cu"][-1])
+    got = out[:n].cpu().to(torch.float64).numpy()
+    sel = np.arange(n) if rows is None else np.asarray(rows)
+    assert_close(got[sel], ref[:n][sel], cfg.name)
+
+
+def test_tiny_fp32():
+    _attn(W.TINY_ATTN)
+
+
+def test_attn_b256_full_size():
+    """Batch 256, 8 kept rows, prefixes 256..2048 + 32: every output row."""
+    _attn(W.ATTN_B256)
+
+
+CASES = [
+    W.AttnCfg("len1", seed=31, batch=3, kept=1, hq=8, hkv=2, head_dim=128, prefix_lo=0, prefix_hi=0, block=1),
+    W.AttnCfg("partial_tiles", seed=32, batch=6, kept=5, hq=8, hkv=2, head_dim=128, prefix_lo=1, prefix_hi=70),
+    W.AttnCfg("two_row_tiles", seed=33, batch=7, kept=None, k_lo=0, k_hi=12, hq=32, hkv=8,
+              head_dim=128, prefix_lo=90, prefix_hi=500),
+    W.AttnCfg("no_gqa", seed=34, batch=4, kept=6, hq=8, hkv=8, head_dim=128, prefix_lo=100, prefix_hi=300),
+    W.AttnCfg("d64", seed=35, batch=4, kept=7, hq=16, hkv=4, head_dim=64, prefix_lo=33, prefix_hi=400),
+    W.AttnCfg("f32_d128", seed=36, batch=3, kept=4, hq=8, hkv=2, head_dim=128, dtype=W.F32,
+              prefix_lo=60, prefix_hi=200),
+    W.AttnCfg("rows_beyond_64", seed=37, batch=3, kept=20, hq=16, hkv=4, head_dim=128,
+              prefix_lo=40, prefix_hi=130),
+    W.AttnCfg("long", seed=38, batch=2, kept=3, hq=8, hkv=2, head_dim=128, prefix_lo=8000, prefix_hi=9000),
+]
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=[c.name for c in CASES])
+def test_attention_edge_cases(cfg):
+    _attn(cfg)
+
+
+def test_attention_kv_len_one_is_v0_exactly():
+    bte = _bte()
+    ai = W.attention_inputs(W.AttnCfg("one", seed=39, batch=4, kept=1, hq=8, hkv=2, head_dim=128,
+                                      prefix_lo=0, prefix_hi=0, block=1))
+    # every sequence holds one key: out must equal that V row bit for bit (bf16)
+    g = dev(ai)
+    say("attention kv_len=1")
+    out = bte.reduced_attention(g["q"], g["count"], g["cu"], g["cache_k"], g["cache_v"],
+                                g["seq_start"], g["kv_len"], 1).cpu()
+    for b in range(4):
+        v = ai["cache_v"][int(ai["seq_start"][b])]                       # [hkv, D]
+        want = v.repeat_interleave(4, dim=0)
+        assert torch.equal(out[b], want)
+
+
+def _es(cfg, ei=None):
+    bte = _bte()
+    ei = ei if ei is not None else W.esdllm_inputs(cfg)
+    g = dev(ei)
+    say(f"esdllm {cfg.name}")
+    out = bte.esdllm_score(g["h_new"], g["h_prev"], g["surv_pos"], g["conf"], ei["alpha"])
+    torch.cuda.synchronize()
+    ref = oracle.esdllm_score(W.to_f64(ei["h_new"]), W.to_f64(ei["h_prev"]), ei["surv_pos"].numpy(),
+                              ei["conf"].numpy(), ei["alpha"])
+    return out.cpu().numpy(), ref, ei
+
+
+def test_esdllm_b8_full_size_and_exact_copy_rows():
+    got, ref, ei = _es(W.ES_B8)
+    assert_close(got, ref, "esdllm_b8")
+    same = ~ei["perturbed"].numpy()
+    c = np.take_along_axis(ei["conf"].numpy(), ei["surv_pos"].numpy(), 1)
+    assert np.array_equal(got[same], (np.float32(0.5) * c[same]).astype(np.float32))
+
+
+def test_esdllm_closed_form_and_scale_invariance():
+    bte = _bte()
+    h = 4096
+    h_prev = torch.ones((1, 3, h), dtype=torch.bfloat16)
+    h_new = torch.ones((1, 1, h), dtype=torch.bfloat16); h_new[0, 0, 123] = 1.5
+    pos = torch.tensor([[2]], dtype=torch.int32)
+    conf = torch.zeros((1, 3))
+    say("esdllm closed form")
+    s = bte.esdllm_score(h_new.cuda(), h_prev.cuda(), pos.cuda(), conf.cuda(), 0.0).cpu()
+    assert s.item() == 2.0 ** -13
+    cfg = W.EsCfg("scale", seed=41, batch=2, prompt=8, generated=64, hidden=512, keep=32)
+    ei = W.esdllm_inputs(cfg)
+    g = dev(ei)
+    a = bte.esdllm_score(g["h_new"], g["h_prev"], g["surv_pos"], g["conf"], 0.3)
+    b = bte.esdllm_score(g["h_new"] * 2, g["h_prev"] * 2, g["surv_pos"], g["conf"], 0.3)
+    assert torch.equal(a, b)
+
+
+def test_esdllm_fp32_and_odd_sizes():
+    cfg = W.EsCfg("f32", seed=42, batch=3, prompt=5, generated=37, hidden=200, dtype=W.F32, keep=10)
+    got, ref, _ = _es(cfg)
+    assert_close(got, ref, "esdllm f32")

@@ -1,0 +1,103 @@
+"""GPU parity: FOCUS importance delta (HIP) vs the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from helpers import assert_close, dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _bte():
+    import block_token_eviction_amd as bte
+    return bte
+
+
+def _run(cfg, inputs=None):
+    bte = _bte()
+    fi = inputs if inputs is not None else W.focus_inputs(cfg)
+    g = dev(fi)
+    say(f"focus {cfg}")
+    out = bte.focus_importance_delta(g["q0"], g["k0"], g["q1"], g["k1"], g["decoded"], cfg.pool_kernel)
+    torch.cuda.synchronize()
+    f64 = W.to_f64
+    ref = oracle.focus_importance_delta(f64(fi["q0"]), f64(fi["k0"]), f64(fi["q1"]), f64(fi["k1"]),
+                                        fi["decoded"].numpy(), cfg.hq, cfg.hkv, cfg.pool_kernel)
+    return out.cpu().numpy(), ref, g
+
+
+def test_tiny_fp32():
+    got, ref, _ = _run(W.TINY_FOCUS)
+    assert_close(got, ref, "tiny")
+
+
+def test_focus_b256_full_size():
+    """Batch 256, 32q/8kv heads, head dim 128, bf16, MaxPool 7: every output."""
+    got, ref, _ = _run(W.FOCUS_B256)
+    assert_close(got, ref, "focus_b256")
+
+
+CASES = [
+    # block, hq, hkv, head_dim, pool, dtype
+    (32, 32, 8, 128, 3, W.BF16),
+    (32, 32, 8, 128, 1, W.BF16),
+    (32, 32, 8, 64, 5, W.BF16),
+    (32, 16, 16, 128, 7, W.BF16),     # more KV heads than waves: waves loop over groups
+    (20, 8, 2, 64, 5, W.BF16),        # ragged block
+    (7, 4, 1, 128, 9, W.BF16),        # runtime pooling radius, single KV head
+    (32, 8, 4, 64, 63, W.BF16),       # window covers the whole row
+    (32, 8, 4, 64, 41, W.BF16),       # window wider than a half row
+    (1, 2, 1, 64, 7, W.F32),          # one-token block
+    (32, 64, 8, 128, 7, W.BF16),      # 8 query heads per KV head
+    (32, 12, 4, 128, 7, W.BF16),      # odd group size 3
+    (32, 8, 8, 128, 7, W.F32),        # fp32 at head dim 128
+    (16, 8, 2, 128, 3, W.F32),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(c[:5]) for c in CASES])
+def test_shapes_and_pool_sizes(case):
+    B, hq, hkv, D, pool, dt = case
+    cfg = W.FocusCfg("edge", seed=11, batch=5, block=B, hq=hq, hkv=hkv, head_dim=D, dtype=dt,
+                     pool_kernel=pool, hidden=64)
+    got, ref, _ = _run(cfg)
+    assert_close(got, ref, str(case))
+
+
+def test_identical_layers_give_exact_zero_and_runs_are_bitwise_equal():
+    bte = _bte()
+    cfg = W.FocusCfg("det", seed=12, batch=16)
+    g = dev(W.focus_inputs(cfg))
+    say("focus determinism")
+    a = bte.focus_importance_delta(g["q0"], g["k0"], g["q0"], g["k0"], g["decoded"], 7)
+    b1 = bte.focus_importance_delta(g["q0"], g["k0"], g["q1"], g["k1"], g["decoded"], 7)
+    b2 = bte.focus_importance_delta(g["q0"], g["k0"], g["q1"], g["k1"], g["decoded"], 7)
+    torch.cuda.synchronize()
+    a = a.cpu().numpy()
+    dec = g["decoded"].cpu().numpy() != 0
+    assert np.all(np.isneginf(a[dec]))
+    assert np.all(a[~dec] == 0.0) and not np.any(np.signbit(a[~dec]))
+    assert torch.equal(b1, b2)
+
+
+def test_all_decoded_and_spike_closed_form():
+    bte = _bte()
+    B, hq, D = 32, 4, 64
+    q0 = torch.zeros((2, B, hq, D))
+    k0 = torch.randn((2, B, hq, D), generator=torch.Generator().manual_seed(1))
+    q1 = torch.zeros((2, B, hq, D)); q1[..., 0] = 1.0
+    k1 = torch.zeros((2, B, hq, D)); k1[0, 10, :, 0] = 5.5; k1[1, 0, :, 0] = 5.5   # bf16-exact spike
+    dec = torch.zeros((2, B), dtype=torch.uint8)
+    say("focus spike")
+    got = bte.focus_importance_delta(q0.cuda(), k0.cuda(), q1.cuda(), k1.cuda(), dec.cuda(), 7).cpu().numpy()
+    es, p_list = np.exp(5.5 / 8.0), (10, 0)
+    for b, p in enumerate(p_list):
+        nw = min(B - 1, p + 3) - max(0, p - 3) + 1
+        Z = nw * es + B - nw
+        want = np.where(np.abs(np.arange(B) - p) <= 3, hq * (B * es / Z - 1), hq * (B / Z - 1))
+        assert_close(got[b], want, f"spike {p}")
+    dec[:] = 1
+    got = bte.focus_importance_delta(q0.cuda(), k0.cuda(), q1.cuda(), k1.cuda(), dec.cuda(), 7).cpu().numpy()
+    assert np.all(np.isneginf(got))

@@ -250,3 +250,16 @@ def esdllm_inputs(cfg: EsCfg, device="cpu") -> dict:
                 perturbed=t(mask), k=t(kkeep), new_k=new_k, new_v=new_v,
                 cache_k=cache_k, cache_v=cache_v,
                 row_base=t(np.arange(n, dtype=np.int64) * L), alpha=cfg.alpha)
+
+
+def chain_inputs(fcfg: FocusCfg, acfg: AttnCfg, device="cpu") -> dict:
+    """Inputs of one full FOCUS step: scoring inputs of `fcfg` plus the KV cache,
+    capacity-sized new K/V and kept-query buffers (batch * k_hi rows) of `acfg`."""
+    assert fcfg.batch == acfg.batch and fcfg.block == acfg.block
+    fi = focus_inputs(fcfg, device)
+    ai = attention_inputs(acfg, device, capacity_rows=fcfg.batch * fcfg.k_hi)
+    return dict(q0=fi["q0"], k0=fi["k0"], q1=fi["q1"], k1=fi["k1"], decoded=fi["decoded"],
+                k=fi["k"], hidden_rows=fi["hidden"], pool_kernel=fcfg.pool_kernel,
+                new_k=ai["new_k"], new_v=ai["new_v"], q_kept=ai["q"], cache_k=ai["cache_k"],
+                cache_v=ai["cache_v"], seq_start=ai["seq_start"], kv_len=ai["kv_len"],
+                row_base=ai["row_base"], prefix=ai["prefix"], rows=ai["rows"])
