@@ -33,7 +33,9 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
-// Streaming (read-once) load: hints the caches not to retain the line.
+// Streaming (read-once) load: hints the caches not to retain the line. Only
+// for fully coalesced accesses; lines that other instructions of the wave still
+// have to read must use ld16, or they are evicted before reuse.
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }

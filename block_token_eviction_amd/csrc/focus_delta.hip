@@ -42,7 +42,7 @@ __device__ __forceinline__ void load_half(HalfRow<D, BF16>& r, const char* row, 
   const char* p = row + h * HalfRow<D, BF16>::kBytes;
 #pragma unroll
   for (int c = 0; c < HalfRow<D, BF16>::kN; ++c) {
-    r.v[c] = valid ? ld16_stream(p + 16 * c) : u32x4{0u, 0u, 0u, 0u};
+    r.v[c] = valid ? ld16(p + 16 * c) : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
@@ -95,10 +95,10 @@ __device__ __forceinline__ void sliding_max(float (&ext)[16 + 2 * R], float (&ou
 // Pool along keys (radius R, compile time; R < 0 selects the runtime radius
 // rt_r), softmax over the row, and add the row's weights into acc.
 // s[r] is the score of this lane's query row with key 16*h + r (masked keys
-// are -inf). row_ok = 0 for padding query rows.
+// are -inf). row_ok = 0 for padding query rows; keys >= B are padding.
 template <int R>
-__device__ __forceinline__ void pool_softmax_accumulate(const f32x16& s, int h, int rt_r, float c,
-                                                        bool row_ok, float (&acc)[16]) {
+__device__ __forceinline__ void pool_softmax_accumulate(const f32x16& s, int h, int rt_r, int B,
+                                                        float c, bool row_ok, float (&acc)[16]) {
   float m = s[0];
 #pragma unroll
   for (int r = 1; r < 16; ++r) m = fmaxf(m, s[r]);
@@ -139,6 +139,13 @@ __device__ __forceinline__ void pool_softmax_accumulate(const f32x16& s, int h, 
       }
       p[r] = v;
     }
+  }
+
+  // Keys past the block end are padding: a window next to the edge pools a
+  // real score into them, so they are removed again after the pooling.
+  if (B < 32) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = (16 * h + r < B) ? p[r] : -INFINITY;
   }
 
   const float mc = m * c;
@@ -208,7 +215,7 @@ __global__ __launch_bounds__(512) void focus_delta_kernel(
             for (int r = 0; r < 16; ++r) s[r] = (16 * h + r < B) ? s[r] : -INFINITY;
           }
           qtile(slot, t + kRing);
-          pool_softmax_accumulate<R>(s, h, rt_r, c, qvalid, acc1);
+          pool_softmax_accumulate<R>(s, h, rt_r, B, c, qvalid, acc1);
         } else {
           f32x16 s = score_tile<D, BF16>(K0, slot);
           if (B < 32) {
@@ -216,7 +223,7 @@ __global__ __launch_bounds__(512) void focus_delta_kernel(
             for (int r = 0; r < 16; ++r) s[r] = (16 * h + r < B) ? s[r] : -INFINITY;
           }
           qtile(slot, t + kRing);
-          pool_softmax_accumulate<R>(s, h, rt_r, c, qvalid, acc0);
+          pool_softmax_accumulate<R>(s, h, rt_r, B, c, qvalid, acc0);
         }
       }
     };

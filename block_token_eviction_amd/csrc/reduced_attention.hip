@@ -113,8 +113,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T =
     const char* pv = vbase + (size_t)keyv * kv_row + h * (C::kRowBytes / 2);
 #pragma unroll
     for (int cc = 0; cc < C::kHalf; ++cc) {
-      kreg[cc] = okk ? ld16_stream(pk + 16 * cc) : u32x4{0u, 0u, 0u, 0u};
-      vreg[cc] = okv ? ld16_stream(pv + 16 * cc) : u32x4{0u, 0u, 0u, 0u};
+      kreg[cc] = okk ? ld16(pk + 16 * cc) : u32x4{0u, 0u, 0u, 0u};
+      vreg[cc] = okv ? ld16(pv + 16 * cc) : u32x4{0u, 0u, 0u, 0u};
     }
   };
 

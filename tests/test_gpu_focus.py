@@ -46,6 +46,9 @@ CASES = [
     (32, 32, 8, 64, 5, W.BF16),
     (32, 16, 16, 128, 7, W.BF16),     # more KV heads than waves: waves loop over groups
     (20, 8, 2, 64, 5, W.BF16),        # ragged block
+    (16, 32, 8, 128, 7, W.BF16),      # half block: padding keys next to the edge
+    (31, 32, 8, 128, 3, W.BF16),
+    (17, 16, 4, 64, 41, W.BF16),      # runtime radius on a ragged block
     (7, 4, 1, 128, 9, W.BF16),        # runtime pooling radius, single KV head
     (32, 8, 4, 64, 63, W.BF16),       # window covers the whole row
     (32, 8, 4, 64, 41, W.BF16),       # window wider than a half row
