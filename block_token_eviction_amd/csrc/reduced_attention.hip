@@ -21,8 +21,9 @@
 // on the matrix cores. V must be read key-by-key per output column, so the
 // tile is staged in a per-wave LDS buffer whose 16-byte chunks are XOR-
 // swizzled by key (conflict-free 16-byte writes and 2-byte column reads).
-// K and V tiles for the wave's next tile are requested as soon as the current
-// ones have been consumed, so one 16 KB tile per wave is always in flight.
+// K and V tiles are copied from HBM straight into LDS (no registers) into two
+// stages per wave, so the next tile's 16 KB are in flight while the current one
+// is being used.
 #include <math.h>
 
 #include "bte_device.h"
@@ -37,14 +38,65 @@ struct Cfg {
   static constexpr int ES = BF16 ? 2 : 4;
   static constexpr int kRowBytes = D * ES;            // one head's K or V row
   static constexpr int kChunks = kRowBytes / 16;      // 16-byte chunks per row
-  static constexpr int kHalf = kChunks / 2;           // chunks per lane half
-  static constexpr int kVTile = 32 * kRowBytes;       // LDS bytes of one V tile
+  static constexpr int kHalf = kChunks / 2;           // chunks per lane half = loads per tile
+  static constexpr int kTile = 32 * kRowBytes;        // LDS bytes of one K or V tile
   static constexpr int kOStride = D + 1;              // floats per row of the merge buffer
   static constexpr int kMerge = kWaves * 32 * kOStride * 4 + 2 * kWaves * 32 * 4;
-  static constexpr int kLds = (kWaves * kVTile > kMerge) ? kWaves * kVTile : kMerge;
+  // LDS stages per wave (K + V tile each): two when 4 waves fit in 128 KB.
+  static constexpr int kStages = kWaves * 2 * 2 * kTile <= 128 * 1024 ? 2 : 1;
+  static constexpr int kStageBytes = 2 * kTile;
+  static constexpr int kStage = kWaves * kStages * kStageBytes;
+  static constexpr int kLds = kStage > kMerge ? kStage : kMerge;
 };
 
-__device__ __forceinline__ int swz(int k) { return (k & 7) ^ (((k >> 4) & 1) << 2); }
+// LDS placement of 16-byte chunk `c` of tile row `row`. K tiles: rows that the
+// K-operand reads fetch together differ in their low 3 bits, so XOR-ing the
+// chunk with them spreads a read over all banks. V tiles: the transpose reads
+// fetch rows r..r+3 and r+16..r+19 together, so bit 4 of the row moves the
+// chunk by 64 bytes.
+__device__ __forceinline__ int kpos(int row, int c) { return c ^ (row & 7); }
+__device__ __forceinline__ int vpos(int row, int c) { return c ^ (((row >> 4) & 1) << 2); }
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt left at their maxima, i.e. not waited on.
+constexpr int kVmcntNoLgkm = (0x7 << 4) | (0xF << 8);
+constexpr int vmcnt_bits(int n) { return (n & 15) | ((n >> 4) << 14); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposing LDS read (gfx950): in each 16-lane group, lane i receives element
+// i%4 of the 8 bytes addressed by group lanes i/4, i/4+4, i/4+8, i/4+12.
+// Issued as inline asm so that the compiler does not order it behind the
+// in-flight HBM->LDS copies of the other stage (it cannot prove they write
+// elsewhere). The compiler does not track these reads: results may only be
+// used after lds_wait_tr() has taken them as operands.
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(a) : "memory");
+  return v;
+}
+// Waits for all outstanding LDS reads; the results are in/out operands, so no
+// use of them can be scheduled before the wait.
+template <int N>
+__device__ __forceinline__ void lds_wait_tr(u32x2 (&v)[N]) {
+  static_assert(N == 8 || N == 16, "one asm operand per read");
+  if constexpr (N == 8) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                   "+v"(v[6]), "+v"(v[7])
+                 :
+                 : "memory");
+  } else {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                   "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]),
+                   "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])
+                 :
+                 : "memory");
+  }
+}
 
 template <int D, bool BF16, int T>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T == 1 ? 2 : 1))) void attn_kernel(
@@ -53,8 +105,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T =
     const int64_t* __restrict__ seq_start, const int32_t* __restrict__ kv_len,
     char* __restrict__ out, int hq, int hkv, int n_rg, float c) {
   using C = Cfg<D, BF16>;
-  constexpr int ES = C::ES;
   constexpr int DT = D / 32;                           // 32-wide output column tiles
+  constexpr int RPI = 64 / C::kChunks;                 // tile rows per coalesced load
   __shared__ __attribute__((aligned(16))) char smem[C::kLds];
 
   const int rg = blockIdx.x % n_rg;
@@ -102,49 +154,68 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T =
 
   const int ntiles = (L + 31) / 32;
   const int kj = 16 * ((n >> 2) & 1) + (n & 3) + 4 * (n >> 3);   // key fed as MFMA row n
-  char* vt = smem + w * C::kVTile;                                 // this wave's V tile
+  char* wave_lds = smem + w * C::kStages * C::kStageBytes;         // this wave's stages
 
-  u32x4 kreg[C::kHalf], vreg[C::kHalf];
-  auto load_tile = [&](int kt) {
-    const int keyk = kt * 32 + kj;
-    const int keyv = kt * 32 + n;
-    const bool okk = keyk < L, okv = keyv < L;
-    const char* pk = kbase + (size_t)keyk * kv_row + h * (C::kRowBytes / 2);
-    const char* pv = vbase + (size_t)keyv * kv_row + h * (C::kRowBytes / 2);
+  // Tile loads go straight from HBM into LDS (16 bytes per lane, no registers):
+  // load i of a tile fills the 1 KB at i*1024, lane l writing byte 16*l of it, i.e.
+  // tile row RPI*i + l/kChunks, LDS chunk l%kChunks. Each lane therefore fetches
+  // the global chunk that the swizzle maps to that LDS chunk. Rows past the
+  // sequence end repeat its last row; their scores are masked below, so they get
+  // probability 0 and a finite V row.
+  const int lrow = lane / C::kChunks;
+  const int lslot = lane % C::kChunks;
+  auto issue_tile = [&](int kt, int stage) {
+    char* kdst = wave_lds + stage * C::kStageBytes;
+    char* vdst = kdst + C::kTile;
 #pragma unroll
-    for (int cc = 0; cc < C::kHalf; ++cc) {
-      kreg[cc] = okk ? ld16(pk + 16 * cc) : u32x4{0u, 0u, 0u, 0u};
-      vreg[cc] = okv ? ld16(pv + 16 * cc) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < C::kHalf; ++i) {
+      const int row = RPI * i + lrow;
+      int key = kt * 32 + row;
+      key = key < L ? key : L - 1;
+      const size_t off = (size_t)key * kv_row;
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(kbase + off + 16 * kpos(row, lslot)),
+          (void __attribute__((address_space(3)))*)(kdst + 1024 * i), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(vbase + off + 16 * vpos(row, lslot)),
+          (void __attribute__((address_space(3)))*)(vdst + 1024 * i), 16, 0, 0);
     }
   };
 
-  if (w < ntiles) load_tile(w);
-  for (int kt = w; kt < ntiles; kt += kWaves) {
+  if (w < ntiles) issue_tile(w, 0);
+  if (C::kStages == 2 && w + kWaves < ntiles) issue_tile(w + kWaves, 1);
+  int it = 0;
+  for (int kt = w; kt < ntiles; kt += kWaves, ++it) {
+    const int stage = C::kStages == 2 ? (it & 1) : 0;
+    // Wait for this tile's loads; the next tile's (2 * kHalf loads) may stay in flight.
+    if (C::kStages == 2 && kt + kWaves < ntiles) {
+      __builtin_amdgcn_s_waitcnt(kVmcntNoLgkm | vmcnt_bits(2 * C::kHalf));
+    } else {
+      __builtin_amdgcn_s_waitcnt(kVmcntNoLgkm | vmcnt_bits(0));
+    }
+    __builtin_amdgcn_wave_barrier();
+    const char* kt_lds = wave_lds + stage * C::kStageBytes;
+    const char* vt_lds = kt_lds + C::kTile;
+
     // S^T tiles: lane (n, h), register r = score of query row n with key kt*32 + 16h + r.
     f32x16 s[T];
 #pragma unroll
-    for (int tq = 0; tq < T; ++tq) {
-      f32x16 acc = {};
-      if constexpr (BF16) {
-#pragma unroll
-        for (int cc = 0; cc < C::kHalf; ++cc) acc = mfma_bf16(kreg[cc], qop[tq][cc], acc);
-      } else {
-#pragma unroll
-        for (int cc = 0; cc < C::kHalf; ++cc)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc = mfma_f32(__uint_as_float(kreg[cc][e]), __uint_as_float(qop[tq][cc][e]), acc);
-      }
-      s[tq] = acc;
-    }
-    // Stage V: lane (key n, half h) writes its chunks at swizzled positions.
+    for (int tq = 0; tq < T; ++tq) s[tq] = f32x16{};
 #pragma unroll
     for (int cc = 0; cc < C::kHalf; ++cc) {
       const int chunk = h * C::kHalf + cc;
-      st16(vt + n * C::kRowBytes + ((chunk ^ swz(n)) << 4), vreg[cc]);
+      const u32x4 ka = ld16(kt_lds + kj * C::kRowBytes + (kpos(kj, chunk) << 4));
+#pragma unroll
+      for (int tq = 0; tq < T; ++tq) {
+        if constexpr (BF16) {
+          s[tq] = mfma_bf16(ka, qop[tq][cc], s[tq]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            s[tq] = mfma_f32(__uint_as_float(ka[e]), __uint_as_float(qop[tq][cc][e]), s[tq]);
+        }
+      }
     }
-    __builtin_amdgcn_wave_barrier();
-    if (kt + kWaves < ntiles) load_tile(kt + kWaves);
 
     const int kvalid = L - (kt * 32 + 16 * h);          // keys of this lane half that exist
 #pragma unroll
@@ -169,13 +240,16 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T =
       }
       lsum[tq] = fmaf(lsum[tq], alpha, ps);
       m[tq] = mnew;
+      if (__ballot(alpha != 1.0f)) {                     // rescale only when a max moved
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[tq][dt][r] *= alpha;
+          for (int r = 0; r < 16; ++r) o[tq][dt][r] *= alpha;
+      }
 
       if constexpr (BF16) {
-        // B operand of O^T += V^T P^T: k-slot (h, t) of chunk cc is key 16h + 8cc + t.
+        // O^T += V^T P^T. k-slot (h, t) of MFMA cc is key 16h + 8cc + t, for both
+        // operands: P from registers, V^T by transposing reads of the V tile.
         u32x4 pb[2];
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
@@ -183,41 +257,46 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T =
           for (int u = 0; u < 4; ++u)
             pb[cc][u] = f32_to_bf16_bits(p[8 * cc + 2 * u]) |
                         (f32_to_bf16_bits(p[8 * cc + 2 * u + 1]) << 16);
+        const int gi = lane & 15;                        // lane within its 16-lane group
+        u32x2 vt[DT * 4];                                // [dt][cc][sh]
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const int d = 32 * dt + n;                     // A row: output column d
-          const int qd = (d * 2) >> 4, wd = (d * 2) & 15;
+          const int byte = 2 * (32 * dt + 16 * ((lane >> 4) & 1) + 4 * (gi & 3));
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int sh = 0; sh < 2; ++sh) {
+              const int row = 16 * h + 8 * cc + 4 * sh + (gi >> 2);
+              vt[4 * dt + 2 * cc + sh] = lds_read_tr16(vt_lds + row * C::kRowBytes +
+                                                       (vpos(row, byte >> 4) << 4) + (byte & 15));
+            }
+        }
+        lds_wait_tr(vt);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
           for (int cc = 0; cc < 2; ++cc) {
-            u32x4 a;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const int k0 = 16 * h + 8 * cc + 2 * u;
-              const int k1 = k0 + 1;
-              const uint32_t lo = *reinterpret_cast<const uint16_t*>(
-                  vt + k0 * C::kRowBytes + ((qd ^ swz(k0)) << 4) + wd);
-              const uint32_t hi = *reinterpret_cast<const uint16_t*>(
-                  vt + k1 * C::kRowBytes + ((qd ^ swz(k1)) << 4) + wd);
-              a[u] = lo | (hi << 16);
-            }
+            const u32x2 lo = vt[4 * dt + 2 * cc], hi = vt[4 * dt + 2 * cc + 1];
+            const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
             o[tq][dt] = mfma_bf16(a, pb[cc], o[tq][dt]);
           }
-        }
       } else {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const int d = 32 * dt + n;
-          const int qd = (d * 4) >> 4, wd = (d * 4) & 15;
+          const int byte = (32 * dt + n) * 4;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int k = 16 * h + i;
-            const float a = *reinterpret_cast<const float*>(vt + k * C::kRowBytes + ((qd ^ swz(k)) << 4) + wd);
+            const int row = 16 * h + i;
+            const float a = *reinterpret_cast<const float*>(
+                vt_lds + row * C::kRowBytes + (vpos(row, byte >> 4) << 4) + (byte & 15));
             o[tq][dt] = mfma_f32(a, p[i], o[tq][dt]);
           }
         }
       }
     }
     __builtin_amdgcn_wave_barrier();
+    // This wave has consumed the stage: refill it with the tile kStages ahead.
+    if (kt + C::kStages * kWaves < ntiles) issue_tile(kt + C::kStages * kWaves, stage);
   }
 
   // Merge the 4 wave states: out = sum_w e^(m_w - M) O_w / sum_w e^(m_w - M) l_w.
