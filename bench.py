@@ -41,6 +41,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path shards by sequence with no exchange, "
@@ -140,6 +142,14 @@ def main():
                "ms_per_step": round(es_ms, 4),
                "survivor positions/s": round(ec.batch * ec.generated / (es_ms * 1e-3), 1)}
 
+    if args.copy_calibration:
+        src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    roofline["traffic"] = measured_traffic(dom)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, fc, ac)
@@ -156,6 +166,34 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "es_mode": es_mode,
     }
     print(json.dumps(line), flush=True)
+
+
+COPY_CAL_BYTES = 256 << 20
+KERNEL_SOURCES = {"reduced_attention": ["reduced_attention.hip", "bte_device.h"],
+                  "focus_importance_delta": ["focus_delta.hip", "bte_device.h"]}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha1()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "block_token_eviction_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, scaled by a plain copy of known size), or None when the
+    kernel's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_chain_b1024_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_sources_sha1") != kernel_source_hash(kernel):
+        return None
+    return rec.get("traffic_bytes_per_launch")
 
 
 def cpu_baseline(x, fc, ac, budget_s: float = 12.0):
