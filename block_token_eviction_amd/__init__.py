@@ -26,7 +26,7 @@ BTE_F32, BTE_BF16 = 0, 1
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m block_token_eviction_amd.build` (hipcc, gfx950)")
+                      "`python block_token_eviction_amd/build.py` (hipcc, gfx950)")
 lib = ctypes.CDLL(LIB_PATH)
 
 _p, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t

@@ -1,6 +1,7 @@
 """Build libbte.so (all HIP kernels + the C ABI) for gfx950 with hipcc.
 
-Run as ``python -m block_token_eviction_amd.build``. The shared library is
+Run as ``python block_token_eviction_amd/build.py`` (by path: the package itself
+needs the built library to import). The shared library is
 written next to this file; it links only the HIP runtime.
 """
 from __future__ import annotations
