@@ -11,19 +11,23 @@
 // rows); the group's rows are the kept tokens' G query heads that share KV
 // head g (row = token * G + head-in-group), so every K/V byte of the sequence
 // is read once per KV head. The 4 waves split the key tiles (32 keys each)
-// round-robin, each keeping a private flash-style state (running max, sum and
+// round-robin, each keeping a private flash-style state (reference max, sum and
 // output) and the 4 states are merged in LDS in a fixed order at the end: no
 // HBM workspace and no second launch.
 //
 // Per key tile: S^T = K . Q^T on the matrix cores (keys as MFMA rows fed in a
 // permuted order so that lane l owns query column l%32 and the 16 contiguous
 // keys 16*(l/32)..+15), online softmax in fp32 in-lane, then O^T += V^T . P^T
-// on the matrix cores. V must be read key-by-key per output column, so the
-// tile is staged in a per-wave LDS buffer whose 16-byte chunks are XOR-
-// swizzled by key (conflict-free 16-byte writes and 2-byte column reads).
-// K and V tiles are copied from HBM straight into LDS (no registers) into two
-// stages per wave, so the next tile's 16 KB are in flight while the current one
-// is being used.
+// on the matrix cores. K and V tiles are copied from HBM straight into LDS (no
+// registers) into two stages per wave, so the next tile's 16 KB are in flight
+// while the current one is being used; 16-byte chunks are XOR-swizzled by row
+// so that the K-operand reads and the transposing V reads are conflict-free.
+//
+// The softmax shift is a per-row reference max that only moves when a tile's
+// max exceeds it by more than 2^8 in the exp2 domain (so every exponentiated
+// score is at most 256): the shift cancels between numerator and denominator,
+// bf16 keeps the same relative precision at any scale, and the accumulator
+// rescale then runs about once per row instead of on most tiles.
 #include <math.h>
 
 #include "bte_device.h"
@@ -32,6 +36,7 @@ namespace bte {
 namespace {
 
 constexpr int kWaves = 4;
+constexpr float kShiftSlack = 8.0f;   // log2 of the largest exponentiated score
 
 template <int D, bool BF16>
 struct Cfg {
@@ -39,6 +44,7 @@ struct Cfg {
   static constexpr int kRowBytes = D * ES;            // one head's K or V row
   static constexpr int kChunks = kRowBytes / 16;      // 16-byte chunks per row
   static constexpr int kHalf = kChunks / 2;           // chunks per lane half = loads per tile
+  static constexpr int kRpi = 64 / kChunks;           // tile rows per coalesced load
   static constexpr int kTile = 32 * kRowBytes;        // LDS bytes of one K or V tile
   static constexpr int kOStride = D + 1;              // floats per row of the merge buffer
   static constexpr int kMerge = kWaves * 32 * kOStride * 4 + 2 * kWaves * 32 * 4;
@@ -61,9 +67,6 @@ __device__ __forceinline__ int vpos(int row, int c) { return c ^ (((row >> 4) & 
 // lgkmcnt left at their maxima, i.e. not waited on.
 constexpr int kVmcntNoLgkm = (0x7 << 4) | (0xF << 8);
 constexpr int vmcnt_bits(int n) { return (n & 15) | ((n >> 4) << 14); }
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // Transposing LDS read (gfx950): in each 16-lane group, lane i receives element
 // i%4 of the 8 bytes addressed by group lanes i/4, i/4+4, i/4+8, i/4+12.
@@ -98,28 +101,24 @@ __device__ __forceinline__ void lds_wait_tr(u32x2 (&v)[N]) {
   }
 }
 
+__device__ __forceinline__ void copy16_to_lds(const char* src, char* lds_dst) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                   (void __attribute__((address_space(3)))*)lds_dst, 16, 0, 0);
+}
+
+// One workgroup's work: sequence b, KV head g, the T 32-row query tiles from
+// row0 on (each holding at least one real row).
 template <int D, bool BF16, int T>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T == 1 ? 2 : 1))) void attn_kernel(
-    const char* __restrict__ q, const int32_t* __restrict__ count, const int32_t* __restrict__ cu,
+__device__ __forceinline__ void attn_body(
+    char* __restrict__ smem, const char* __restrict__ q, const int32_t* __restrict__ cu,
     const char* __restrict__ cache_k, const char* __restrict__ cache_v,
     const int64_t* __restrict__ seq_start, const int32_t* __restrict__ kv_len,
-    char* __restrict__ out, int hq, int hkv, int n_rg, float c) {
+    char* __restrict__ out, int hq, int hkv, float c, int b, int g, int rows, int row0) {
   using C = Cfg<D, BF16>;
   constexpr int DT = D / 32;                           // 32-wide output column tiles
-  constexpr int RPI = 64 / C::kChunks;                 // tile rows per coalesced load
-  __shared__ __attribute__((aligned(16))) char smem[C::kLds];
-
-  const int rg = blockIdx.x % n_rg;
-  const int bg = blockIdx.x / n_rg;
-  const int g = bg % hkv;
-  const int b = bg / hkv;
   const int G = hq / hkv;
-  const int rows = count[b] * G;
-  const int row0 = rg * 32 * T;
-  if (row0 >= rows) return;
-
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31;
   const int h = lane >> 5;
   const int L = kv_len[b];
@@ -128,6 +127,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T =
   const size_t kv_row = (size_t)hkv * C::kRowBytes;    // bytes per cache position
   const char* kbase = cache_k + (size_t)s0 * kv_row + (size_t)g * C::kRowBytes;
   const char* vbase = cache_v + (size_t)s0 * kv_row + (size_t)g * C::kRowBytes;
+  const float thr = fminf(kShiftSlack / c, 3.0e38f);   // reference-max slack in score units
 
   // Query operands (B of S^T): lane (n, h) holds half h of query row n.
   u32x4 qop[T][C::kHalf];
@@ -158,28 +158,48 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T =
 
   // Tile loads go straight from HBM into LDS (16 bytes per lane, no registers):
   // load i of a tile fills the 1 KB at i*1024, lane l writing byte 16*l of it, i.e.
-  // tile row RPI*i + l/kChunks, LDS chunk l%kChunks. Each lane therefore fetches
-  // the global chunk that the swizzle maps to that LDS chunk. Rows past the
-  // sequence end repeat its last row; their scores are masked below, so they get
-  // probability 0 and a finite V row.
+  // tile row kRpi*i + l/kChunks, LDS chunk l%kChunks. Each lane therefore fetches
+  // the global chunk that the swizzle maps to that LDS chunk. The tile base is
+  // wave-uniform; the per-lane byte offsets within a full tile are fixed.
   const int lrow = lane / C::kChunks;
   const int lslot = lane % C::kChunks;
+  const uint32_t lane_row_off = (uint32_t)(lrow * kv_row);
   auto issue_tile = [&](int kt, int stage) {
     char* kdst = wave_lds + stage * C::kStageBytes;
     char* vdst = kdst + C::kTile;
+    const size_t tile_off = (size_t)kt * 32 * kv_row;
+    const char* kb = kbase + tile_off;
+    const char* vb = vbase + tile_off;
+    if (kt * 32 + 32 <= L) {
 #pragma unroll
-    for (int i = 0; i < C::kHalf; ++i) {
-      const int row = RPI * i + lrow;
-      int key = kt * 32 + row;
-      key = key < L ? key : L - 1;
-      const size_t off = (size_t)key * kv_row;
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(kbase + off + 16 * kpos(row, lslot)),
-          (void __attribute__((address_space(3)))*)(kdst + 1024 * i), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(vbase + off + 16 * vpos(row, lslot)),
-          (void __attribute__((address_space(3)))*)(vdst + 1024 * i), 16, 0, 0);
+      for (int i = 0; i < C::kHalf; ++i) {
+        const int row = C::kRpi * i + lrow;
+        const size_t row_base = (size_t)(C::kRpi * i) * kv_row;      // wave-uniform
+        copy16_to_lds(kb + row_base + (lane_row_off + 16 * kpos(row, lslot)), kdst + 1024 * i);
+        copy16_to_lds(vb + row_base + (lane_row_off + 16 * vpos(row, lslot)), vdst + 1024 * i);
+      }
+    } else {
+      // Last, partial tile: rows past the sequence end repeat its last row.
+      // Their scores are masked below, so they get probability 0 and a finite V row.
+      const int last = L - 1 - kt * 32;
+#pragma unroll
+      for (int i = 0; i < C::kHalf; ++i) {
+        const int row = C::kRpi * i + lrow;
+        const uint32_t roff = (uint32_t)((row < last ? row : last) * kv_row);
+        copy16_to_lds(kb + roff + 16 * kpos(row, lslot), kdst + 1024 * i);
+        copy16_to_lds(vb + roff + 16 * vpos(row, lslot), vdst + 1024 * i);
+      }
     }
+  };
+
+  // Lane part of the V^T transposing reads: k-slot (h, t) of P.V MFMA cc is
+  // key 16h + 8cc + t; in a 16-lane group, lane gi reads row 16h + 8cc + 4sh + gi/4
+  // at column 32dt + 16*((lane/16)%2) + 4*(gi%4).
+  const int gi = lane & 15;                            // lane within its 16-lane group
+  auto vt_off = [&](int dt, int cc, int sh) {
+    const int row = 16 * h + 8 * cc + 4 * sh + (gi >> 2);
+    const int byte = 2 * (32 * dt + 16 * ((lane >> 4) & 1) + 4 * (gi & 3));
+    return row * C::kRowBytes + (vpos(row, byte >> 4) << 4) + (byte & 15);
   };
 
   if (w < ntiles) issue_tile(w, 0);
@@ -217,6 +237,19 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T =
       }
     }
 
+    // V^T operands, shared by the query tiles: k-slot (h, t) of MFMA cc is key
+    // 16h + 8cc + t, for both operands.
+    u32x2 vt[DT * 4];
+    if constexpr (BF16) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int sh = 0; sh < 2; ++sh)
+            vt[4 * dt + 2 * cc + sh] = lds_read_tr16(vt_lds + vt_off(dt, cc, sh));
+    }
+
     const int kvalid = L - (kt * 32 + 16 * h);          // keys of this lane half that exist
 #pragma unroll
     for (int tq = 0; tq < T; ++tq) {
@@ -224,54 +257,38 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T =
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[tq][r] = r < kvalid ? s[tq][r] : -INFINITY;
       }
-      float mt = s[tq][0];
+      float mt = fmaxf(s[tq][0], s[tq][1]);
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[tq][r]);
+      for (int r = 2; r < 16; ++r) mt = fmaxf(mt, s[tq][r]);
       mt = fmaxf(mt, swap_halves(mt));
-      const float mnew = fmaxf(m[tq], mt);
-      const float alpha = fast_exp2((m[tq] - mnew) * c);
-      const float mc = mnew * c;
-      float p[16];
-      float ps = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = fast_exp2(fmaf(s[tq][r], c, -mc));
-        ps += p[r];
-      }
-      lsum[tq] = fmaf(lsum[tq], alpha, ps);
-      m[tq] = mnew;
-      if (__ballot(alpha != 1.0f)) {                     // rescale only when a max moved
+      // Move the reference max only when this tile's max is more than the slack above it.
+      const bool move = mt > m[tq] + thr;
+      const float mnew = move ? mt : m[tq];
+      if (__ballot(move && m[tq] != -INFINITY)) {       // rows with an earlier state
+        const float alpha = move ? fast_exp2((m[tq] - mnew) * c) : 1.0f;
+        lsum[tq] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[tq][dt][r] *= alpha;
       }
+      m[tq] = mnew;
+      const float mc = mnew * c;
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(s[tq][r], c, -mc));
+      float ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ps += p[r];
+      lsum[tq] += ps;
 
       if constexpr (BF16) {
-        // O^T += V^T P^T. k-slot (h, t) of MFMA cc is key 16h + 8cc + t, for both
-        // operands: P from registers, V^T by transposing reads of the V tile.
         u32x4 pb[2];
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            pb[cc][u] = f32_to_bf16_bits(p[8 * cc + 2 * u]) |
-                        (f32_to_bf16_bits(p[8 * cc + 2 * u + 1]) << 16);
-        const int gi = lane & 15;                        // lane within its 16-lane group
-        u32x2 vt[DT * 4];                                // [dt][cc][sh]
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int byte = 2 * (32 * dt + 16 * ((lane >> 4) & 1) + 4 * (gi & 3));
-#pragma unroll
-          for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-            for (int sh = 0; sh < 2; ++sh) {
-              const int row = 16 * h + 8 * cc + 4 * sh + (gi >> 2);
-              vt[4 * dt + 2 * cc + sh] = lds_read_tr16(vt_lds + row * C::kRowBytes +
-                                                       (vpos(row, byte >> 4) << 4) + (byte & 15));
-            }
-        }
-        lds_wait_tr(vt);
+          for (int u = 0; u < 4; ++u) pb[cc][u] = pack_bf16x2(p[8 * cc + 2 * u], p[8 * cc + 2 * u + 1]);
+        if (tq == 0) lds_wait_tr(vt);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -352,8 +369,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T =
         for (int i = 0; i < DP; i += 8) {
           u32x4 v;
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            v[u] = f32_to_bf16_bits(res[i + 2 * u]) | (f32_to_bf16_bits(res[i + 2 * u + 1]) << 16);
+          for (int u = 0; u < 4; ++u) v[u] = pack_bf16x2(res[i + 2 * u], res[i + 2 * u + 1]);
           st16(dst + (part * DP + i) * 2, v);
         }
       } else {
@@ -366,6 +382,27 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T =
       }
     }
   }
+}
+
+template <int D, bool BF16, int T>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T == 1 ? 2 : 1))) void attn_kernel(
+    const char* __restrict__ q, const int32_t* __restrict__ count, const int32_t* __restrict__ cu,
+    const char* __restrict__ cache_k, const char* __restrict__ cache_v,
+    const int64_t* __restrict__ seq_start, const int32_t* __restrict__ kv_len,
+    char* __restrict__ out, int hq, int hkv, int n_rg, float c) {
+  __shared__ __attribute__((aligned(16))) char smem[Cfg<D, BF16>::kLds];
+  const int rg = blockIdx.x % n_rg;
+  const int bg = blockIdx.x / n_rg;
+  const int g = bg % hkv;
+  const int b = bg / hkv;
+  const int rows = count[b] * (hq / hkv);
+  const int row0 = rg * 32 * T;
+  if (row0 >= rows) return;
+  // Workgroup-uniform: skip query tiles that hold no real row.
+  if (T == 2 && rows - row0 > 32)
+    attn_body<D, BF16, T>(smem, q, cu, cache_k, cache_v, seq_start, kv_len, out, hq, hkv, c, b, g, rows, row0);
+  else
+    attn_body<D, BF16, 1>(smem, q, cu, cache_k, cache_v, seq_start, kv_len, out, hq, hkv, c, b, g, rows, row0);
 }
 
 template <int D, bool BF16, int T>
@@ -405,6 +442,7 @@ extern "C" int bte_reduced_attention(const void* q, const int32_t* count, const 
   if (!q || !count || !cu || !cache_k || !cache_v || !seq_start || !kv_len || !out)
     return BTE_ERR_NULL;
   if (batch <= 0 || k_max < 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0) return BTE_ERR_DIM;
+  if (!(scale > 0.f) || !isfinite(scale)) return BTE_ERR_DIM;
   if (head_dim != 64 && head_dim != 128) return BTE_ERR_UNSUPPORTED;
   if (dtype != BTE_F32 && dtype != BTE_BF16) return BTE_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(cache_k) || !aligned16(cache_v) || !aligned16(out))
