@@ -4,7 +4,8 @@ One step = one pass of the FOCUS chain over the batch-1024 workload
 (block 32, 32 query / 8 KV heads, head dim 128, bf16, MaxPool 7, budgets
 K ~ U{4..12}, prefixes ~ U{1024..4096}, hidden 4096), all on one stream:
 
-    importance delta (layers 0/1) -> top-K -> gather -> KV scatter -> reduced attention
+    importance delta (layers 0/1) -> top-K -> gather -> KV scatter
+        -> longest-first attention order -> reduced attention
 
 Prints one JSON line: block tokens/s (batch * block / step time), per-kernel
 average durations from HIP events recorded on the launch stream, the
@@ -69,6 +70,7 @@ def main():
         ("topk_select", lambda: step.select(x["k"])),
         ("gather_rows", lambda: step.gather(x["hidden_rows"])),
         ("kv_scatter", lambda: step.scatter(x["new_k"], x["new_v"], x["row_base"], x["cache_k"], x["cache_v"])),
+        ("attention_order", lambda: step.schedule(x["kv_len"])),
         ("reduced_attention", lambda: step.attend(x["q_kept"], x["cache_k"], x["cache_v"], x["seq_start"], x["kv_len"])),
     ]
     log(f"warmup {args.warmup}")
@@ -104,6 +106,7 @@ def main():
         "topk_select": fc.batch * B * 4 + fc.batch * 4 + fc.batch * (fc.k_hi + 2) * 4,
         "gather_rows": 2 * sum_k * H * es,
         "kv_scatter": 2 * 2 * sum_k * hkv * D * es,
+        "attention_order": 2 * fc.batch * 4,
         "reduced_attention": int(kv_len.sum()) * hkv * D * es * 2 + 2 * sum_k * hq * D * es,
     }
     flops_attn = 0

@@ -19,7 +19,7 @@ import torch
 
 __all__ = ["lib", "LIB_PATH", "BteError", "status_string", "focus_importance_delta",
            "esdllm_score", "topk_select", "gather_rows", "kv_scatter", "reduced_attention",
-           "BTE_F32", "BTE_BF16"]
+           "attention_order", "BTE_F32", "BTE_BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbte.so")
 BTE_F32, BTE_BF16 = 0, 1
@@ -38,7 +38,8 @@ _SIG = {
     "bte_topk_select": ([_p, _p, _p, _p, _p, _i, _i, _i, _p], _i),
     "bte_gather_rows": ([_p, _p, _p, _p, _p, _i, _i, _i, _sz, _p], _i),
     "bte_kv_scatter": ([_p, _p, _p, _p, _p, _p, _i, _p, _p, _p, _i, _i, _sz, _p], _i),
-    "bte_reduced_attention": ([_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p], _i),
+    "bte_reduced_attention": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p], _i),
+    "bte_attention_order": ([_p, _i, _p, _p], _i),
 }
 for _name, (_args, _res) in _SIG.items():
     _fn = getattr(lib, _name)
@@ -180,20 +181,38 @@ def kv_scatter(new_k, new_v, idx, count, cu, row_base, cache_k, cache_v, pos_map
 
 
 def reduced_attention(q, count, cu, cache_k, cache_v, seq_start, kv_len, k_max: int,
-                      scale: float | None = None, out=None):
-    """q [capacity, hq, D], cache [rows, hkv, D] -> out [capacity, hq, D] (rows cu[b]+t written)."""
-    _dev(q, count, cu, cache_k, cache_v, seq_start, kv_len, out)
+                      scale: float | None = None, out=None, order=None):
+    """q [capacity, hq, D], cache [rows, hkv, D] -> out [capacity, hq, D] (rows cu[b]+t written).
+
+    `order` (int32 [batch], e.g. from attention_order) only schedules the work."""
+    _dev(q, count, cu, cache_k, cache_v, seq_start, kv_len, out, order)
     _want(seq_start, torch.int64, "seq_start")
     _want(kv_len, torch.int32, "kv_len")
     hq, d = q.shape[1], q.shape[2]
     hkv = cache_k.shape[1]
     batch = count.shape[0]
     assert cache_v.shape == cache_k.shape and cache_k.dtype == q.dtype
+    if order is not None:
+        _want(order, torch.int32, "order")
+        assert order.shape == (batch,)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     _check("bte_reduced_attention", lib.bte_reduced_attention(
         _ptr(q), _ptr(count), _ptr(cu), _ptr(cache_k), _ptr(cache_v), _ptr(seq_start),
-        _ptr(kv_len), _ptr(out), batch, k_max, hq, hkv, d, float(scale), _dtype(q), _stream()))
+        _ptr(kv_len), _ptr(order), _ptr(out), batch, k_max, hq, hkv, d, float(scale), _dtype(q),
+        _stream()))
+    return out
+
+
+def attention_order(kv_len, out=None):
+    """kv_len int32 [batch] -> order int32 [batch]: sequences by length descending, index ascending."""
+    _dev(kv_len, out)
+    _want(kv_len, torch.int32, "kv_len")
+    batch = kv_len.shape[0]
+    if out is None:
+        out = torch.empty((batch,), dtype=torch.int32, device=kv_len.device)
+    _want(out, torch.int32, "out")
+    _check("bte_attention_order", lib.bte_attention_order(_ptr(kv_len), batch, _ptr(out), _stream()))
     return out

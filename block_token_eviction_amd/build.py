@@ -24,7 +24,10 @@ SOURCES = ["capi.hip", "focus_delta.hip", "esdllm_score.hip", "topk_select.hip",
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
          "-Wall", "-Wno-unused-function",
          # no packed fp32 instructions in generated code
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA accumulators in VGPRs: the softmax and rescale read and write them
+         # with VALU ops, which otherwise cost AGPR<->VGPR copies every tile
+         "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc() -> str:

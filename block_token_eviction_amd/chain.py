@@ -21,8 +21,8 @@ import math
 
 import torch
 
-from . import (esdllm_score, focus_importance_delta, gather_rows, kv_scatter, reduced_attention,
-               topk_select)
+from . import (attention_order, esdllm_score, focus_importance_delta, gather_rows, kv_scatter,
+               reduced_attention, topk_select)
 
 
 class FocusStep:
@@ -37,6 +37,7 @@ class FocusStep:
         self.cu = torch.empty((batch + 1,), **i32)
         self.gathered = torch.empty((batch * k_max, hidden), dtype=dtype, device=device)
         self.out = torch.empty((batch * k_max, hq, head_dim), dtype=dtype, device=device)
+        self.order = torch.empty((batch,), **i32)
 
     def score(self, q0, k0, q1, k1, decoded, pool_kernel):
         return focus_importance_delta(q0, k0, q1, k1, decoded, pool_kernel, out=self.delta)
@@ -50,9 +51,14 @@ class FocusStep:
     def scatter(self, new_k, new_v, row_base, cache_k, cache_v):
         return kv_scatter(new_k, new_v, self.idx, self.count, self.cu, row_base, cache_k, cache_v)
 
+    def schedule(self, kv_len):
+        """Longest-first work order of the step's attention calls (one per step:
+        every layer of the step sees the same lengths)."""
+        return attention_order(kv_len, out=self.order)
+
     def attend(self, q_kept, cache_k, cache_v, seq_start, kv_len):
         return reduced_attention(q_kept, self.count, self.cu, cache_k, cache_v, seq_start, kv_len,
-                                 self.k_max, self.scale, out=self.out)
+                                 self.k_max, self.scale, out=self.out, order=self.order)
 
     def run(self, *, q0, k0, q1, k1, decoded, k, hidden_rows, pool_kernel, new_k, new_v, q_kept,
             cache_k, cache_v, seq_start, kv_len, row_base):
@@ -60,6 +66,7 @@ class FocusStep:
         self.select(k)
         self.gather(hidden_rows)
         self.scatter(new_k, new_v, row_base, cache_k, cache_v)
+        self.schedule(kv_len)
         self.attend(q_kept, cache_k, cache_v, seq_start, kv_len)
         return self.out
 

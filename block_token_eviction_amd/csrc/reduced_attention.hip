@@ -35,10 +35,9 @@
 namespace bte {
 namespace {
 
-constexpr int kWaves = 4;
 constexpr float kShiftSlack = 8.0f;   // log2 of the largest exponentiated score
 
-template <int D, bool BF16>
+template <int D, bool BF16, int kWaves>
 struct Cfg {
   static constexpr int ES = BF16 ? 2 : 4;
   static constexpr int kRowBytes = D * ES;            // one head's K or V row
@@ -48,7 +47,7 @@ struct Cfg {
   static constexpr int kTile = 32 * kRowBytes;        // LDS bytes of one K or V tile
   static constexpr int kOStride = D + 1;              // floats per row of the merge buffer
   static constexpr int kMerge = kWaves * 32 * kOStride * 4 + 2 * kWaves * 32 * 4;
-  // LDS stages per wave (K + V tile each): two when 4 waves fit in 128 KB.
+  // LDS stages per wave (K + V tile each): two when all waves' stages fit in 128 KB.
   static constexpr int kStages = kWaves * 2 * 2 * kTile <= 128 * 1024 ? 2 : 1;
   static constexpr int kStageBytes = 2 * kTile;
   static constexpr int kStage = kWaves * kStages * kStageBytes;
@@ -101,20 +100,26 @@ __device__ __forceinline__ void lds_wait_tr(u32x2 (&v)[N]) {
   }
 }
 
+// Cache-policy operand of the HBM->LDS copies: non-temporal. Every byte of a
+// K/V tile is read exactly once, so the lines need not stay in L2 or the MALL;
+// the hint raises the streaming read rate by about a tenth on MI355X.
+constexpr int kStreamPolicy = 2;
+
 __device__ __forceinline__ void copy16_to_lds(const char* src, char* lds_dst) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                   (void __attribute__((address_space(3)))*)lds_dst, 16, 0, 0);
+                                   (void __attribute__((address_space(3)))*)lds_dst, 16, 0,
+                                   kStreamPolicy);
 }
 
 // One workgroup's work: sequence b, KV head g, the T 32-row query tiles from
 // row0 on (each holding at least one real row).
-template <int D, bool BF16, int T>
+template <int D, bool BF16, int T, int kWaves>
 __device__ __forceinline__ void attn_body(
     char* __restrict__ smem, const char* __restrict__ q, const int32_t* __restrict__ cu,
     const char* __restrict__ cache_k, const char* __restrict__ cache_v,
     const int64_t* __restrict__ seq_start, const int32_t* __restrict__ kv_len,
     char* __restrict__ out, int hq, int hkv, float c, int b, int g, int rows, int row0) {
-  using C = Cfg<D, BF16>;
+  using C = Cfg<D, BF16, kWaves>;
   constexpr int DT = D / 32;                           // 32-wide output column tiles
   const int G = hq / hkv;
   const int lane = threadIdx.x & 63;
@@ -250,13 +255,12 @@ __device__ __forceinline__ void attn_body(
             vt[4 * dt + 2 * cc + sh] = lds_read_tr16(vt_lds + vt_off(dt, cc, sh));
     }
 
-    const int kvalid = L - (kt * 32 + 16 * h);          // keys of this lane half that exist
+    // Keys of this lane half that exist. Padding rows of a partial tile repeat
+    // the sequence's last key, so the row max is exact without masking; only
+    // their probabilities are zeroed below.
+    const int kvalid = L - (kt * 32 + 16 * h);
 #pragma unroll
     for (int tq = 0; tq < T; ++tq) {
-      if (kvalid < 16) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[tq][r] = r < kvalid ? s[tq][r] : -INFINITY;
-      }
       float mt = fmaxf(s[tq][0], s[tq][1]);
 #pragma unroll
       for (int r = 2; r < 16; ++r) mt = fmaxf(mt, s[tq][r]);
@@ -277,17 +281,29 @@ __device__ __forceinline__ void attn_body(
       float p[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(s[tq][r], c, -mc));
+      if (kvalid < 16) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = r < kvalid ? p[r] : 0.f;
+      }
       float ps = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) ps += p[r];
       lsum[tq] += ps;
 
       if constexpr (BF16) {
-        u32x4 pb[2];
+        // P = P_hi + P_lo, both bf16: two products keep P.V accurate to about
+        // 2^-16 relative instead of bf16's 2^-9 (V is exact in bf16).
+        u32x4 ph[2], pl[2];
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-          for (int u = 0; u < 4; ++u) pb[cc][u] = pack_bf16x2(p[8 * cc + 2 * u], p[8 * cc + 2 * u + 1]);
+          for (int u = 0; u < 4; ++u) {
+            const float x0 = p[8 * cc + 2 * u], x1 = p[8 * cc + 2 * u + 1];
+            const uint32_t hi = pack_bf16x2(x0, x1);
+            ph[cc][u] = hi;
+            pl[cc][u] = pack_bf16x2(x0 - __uint_as_float(hi << 16),
+                                    x1 - __uint_as_float(hi & 0xffff0000u));
+          }
         if (tq == 0) lds_wait_tr(vt);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
@@ -295,7 +311,8 @@ __device__ __forceinline__ void attn_body(
           for (int cc = 0; cc < 2; ++cc) {
             const u32x2 lo = vt[4 * dt + 2 * cc], hi = vt[4 * dt + 2 * cc + 1];
             const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-            o[tq][dt] = mfma_bf16(a, pb[cc], o[tq][dt]);
+            o[tq][dt] = mfma_bf16(a, ph[cc], o[tq][dt]);
+            o[tq][dt] = mfma_bf16(a, pl[cc], o[tq][dt]);
           }
       } else {
 #pragma unroll
@@ -336,8 +353,9 @@ __device__ __forceinline__ void attn_body(
         obuf[(w * 32 + n) * C::kOStride + d] = o[tq][dt][r];
       }
     __syncthreads();
-    const int rr = threadIdx.x >> 3;                     // query row of the tile
-    const int part = threadIdx.x & 7;                    // D/8 consecutive columns
+    constexpr int kParts = 2 * kWaves;                   // threads per output row
+    const int rr = threadIdx.x / kParts;                 // query row of the tile
+    const int part = threadIdx.x % kParts;               // D/kParts consecutive columns
     const int rho = row0 + 32 * tq + rr;
     if (rho < rows) {
       float M = -INFINITY;
@@ -354,7 +372,7 @@ __device__ __forceinline__ void attn_body(
       const int tok = rho / G;
       const int head = g * G + (rho - tok * G);
       char* dst = out + (((size_t)(cub + tok)) * hq + head) * C::kRowBytes;
-      constexpr int DP = D / 8;
+      constexpr int DP = D / kParts;
       float res[DP];
 #pragma unroll
       for (int i = 0; i < DP; ++i) {
@@ -384,60 +402,153 @@ __device__ __forceinline__ void attn_body(
   }
 }
 
-template <int D, bool BF16, int T>
+// Workgroup x runs on XCD x % 8 (MI355X dispatches workgroups round-robin over
+// its 8 XCDs). The mapping below puts all KV heads (and row groups) of one
+// sequence on one XCD, one after another, so the 256-byte head slices of each
+// cache row are fetched together; sequences go round-robin over the XCDs in
+// the given order.
+constexpr int kXcds = 8;
+
+template <int D, bool BF16, int T, int kWaves>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T == 1 ? 2 : 1))) void attn_kernel(
     const char* __restrict__ q, const int32_t* __restrict__ count, const int32_t* __restrict__ cu,
     const char* __restrict__ cache_k, const char* __restrict__ cache_v,
     const int64_t* __restrict__ seq_start, const int32_t* __restrict__ kv_len,
-    char* __restrict__ out, int hq, int hkv, int n_rg, float c) {
-  __shared__ __attribute__((aligned(16))) char smem[Cfg<D, BF16>::kLds];
-  const int rg = blockIdx.x % n_rg;
-  const int bg = blockIdx.x / n_rg;
-  const int g = bg % hkv;
-  const int b = bg / hkv;
+    const int32_t* __restrict__ order, char* __restrict__ out, int batch, int hq, int hkv,
+    int n_rg, float c) {
+  __shared__ __attribute__((aligned(16))) char smem[Cfg<D, BF16, kWaves>::kLds];
+  const int per_seq = hkv * n_rg;                      // workgroups per sequence
+  const int slot = blockIdx.x / kXcds;
+  const int grp = slot / per_seq;
+  const int r = kXcds * grp + (int)(blockIdx.x % kXcds);  // position in the processing order
+  if (r >= batch) return;
+  const int j = slot - grp * per_seq;
+  const int g = j / n_rg;
+  const int rg = j - g * n_rg;
+  // Workgroups start in index order, so taking the sequences in the caller's
+  // order (longest first) keeps long items out of the tail. An entry outside
+  // [0, batch) is clamped: a bad order gives wrong results, never a stray access.
+  const int b = order ? min(max(order[r], 0), batch - 1) : r;
   const int rows = count[b] * (hq / hkv);
   const int row0 = rg * 32 * T;
   if (row0 >= rows) return;
   // Workgroup-uniform: skip query tiles that hold no real row.
   if (T == 2 && rows - row0 > 32)
-    attn_body<D, BF16, T>(smem, q, cu, cache_k, cache_v, seq_start, kv_len, out, hq, hkv, c, b, g, rows, row0);
+    attn_body<D, BF16, T, kWaves>(smem, q, cu, cache_k, cache_v, seq_start, kv_len, out, hq, hkv, c, b, g, rows, row0);
   else
-    attn_body<D, BF16, 1>(smem, q, cu, cache_k, cache_v, seq_start, kv_len, out, hq, hkv, c, b, g, rows, row0);
+    attn_body<D, BF16, 1, kWaves>(smem, q, cu, cache_k, cache_v, seq_start, kv_len, out, hq, hkv, c, b, g, rows, row0);
 }
 
-template <int D, bool BF16, int T>
-hipError_t launch(const void* q, const int32_t* count, const int32_t* cu, const void* ck,
-                  const void* cv, const int64_t* ss, const int32_t* kl, void* out, int batch,
-                  int k_max, int hq, int hkv, float c, hipStream_t stream) {
-  const int G = hq / hkv;
-  const long rows = (long)k_max * G;
-  const int n_rg = (int)((rows + 32 * T - 1) / (32 * T));
-  const long grid = (long)batch * hkv * n_rg;
+struct AttnArgs {
+  const void* q;
+  const int32_t* count;
+  const int32_t* cu;
+  const void* ck;
+  const void* cv;
+  const int64_t* ss;
+  const int32_t* kl;
+  const int32_t* order;
+  void* out;
+  int batch, k_max, hq, hkv;
+  float c;
+};
+
+template <int D, bool BF16, int T, int kWaves>
+hipError_t launch(const AttnArgs& a, hipStream_t stream) {
+  const long rows = (long)a.k_max * (a.hq / a.hkv);
+  const long n_rg = (rows + 32 * T - 1) / (32 * T);
+  const long grid = (long)((a.batch + kXcds - 1) / kXcds) * kXcds * a.hkv * n_rg;
   if (grid > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_kernel<D, BF16, T>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream,
-                     (const char*)q, count, cu, (const char*)ck, (const char*)cv, ss, kl,
-                     (char*)out, hq, hkv, n_rg, c);
+  hipLaunchKernelGGL((attn_kernel<D, BF16, T, kWaves>), dim3((unsigned)grid), dim3(64 * kWaves), 0,
+                     stream, (const char*)a.q, a.count, a.cu, (const char*)a.ck, (const char*)a.cv,
+                     a.ss, a.kl, a.order, (char*)a.out, a.batch, a.hq, a.hkv, (int)n_rg, a.c);
   return hipGetLastError();
 }
 
-template <int D, bool BF16>
-hipError_t launch_t(const void* q, const int32_t* count, const int32_t* cu, const void* ck,
-                    const void* cv, const int64_t* ss, const int32_t* kl, void* out, int batch,
-                    int k_max, int hq, int hkv, float c, hipStream_t stream) {
-  const long rows = (long)k_max * (hq / hkv);
-  if (rows > 32)
-    return launch<D, BF16, 2>(q, count, cu, ck, cv, ss, kl, out, batch, k_max, hq, hkv, c, stream);
-  return launch<D, BF16, 1>(q, count, cu, ck, cv, ss, kl, out, batch, k_max, hq, hkv, c, stream);
+// Waves per workgroup. Several waves split one item's keys (merged in LDS);
+// that shortens each item, which matters when there are few items or no
+// longest-first order (long items would otherwise finish last). With many
+// items in longest-first order, one wave per item (four workgroups per CU, no
+// merge) streams best.
+inline int waves_for(long items, bool ordered) {
+  if (ordered) return items >= 4096 ? 1 : items >= 1024 ? 2 : 4;
+  return items >= 2048 ? 2 : 4;
+}
+
+template <int D>
+hipError_t launch_bf16(const AttnArgs& a, hipStream_t stream) {
+  const long rows = (long)a.k_max * (a.hq / a.hkv);
+  const int T = rows > 32 ? 2 : 1;
+  const long items = (long)a.batch * a.hkv * ((rows + 32 * T - 1) / (32 * T));
+  const int nw = waves_for(items, a.order != nullptr);
+  if (T == 2) {
+    if (nw == 1) return launch<D, true, 2, 1>(a, stream);
+    if (nw == 2) return launch<D, true, 2, 2>(a, stream);
+    return launch<D, true, 2, 4>(a, stream);
+  }
+  if (nw == 1) return launch<D, true, 1, 1>(a, stream);
+  if (nw == 2) return launch<D, true, 1, 2>(a, stream);
+  return launch<D, true, 1, 4>(a, stream);
+}
+
+// Descending-length processing order: one workgroup sorts (length desc, index
+// asc) keys in LDS with a bitonic network.
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderMax = 16384;
+
+__global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __restrict__ kv_len,
+                                                             int batch, int n_pad,
+                                                             int32_t* __restrict__ order) {
+  extern __shared__ uint64_t keys[];
+  for (int i = threadIdx.x; i < n_pad; i += kOrderThreads) {
+    uint64_t k = ~0ull;
+    if (i < batch) {
+      const uint32_t len = (uint32_t)max(kv_len[i], 0);
+      k = ((uint64_t)(0xffffffffu - len) << 32) | (uint32_t)i;
+    }
+    keys[i] = k;
+  }
+  __syncthreads();
+  for (int k = 2; k <= n_pad; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int i = threadIdx.x; i < n_pad; i += kOrderThreads) {
+        const int ixj = i ^ jj;
+        if (ixj > i) {
+          const uint64_t x = keys[i], y = keys[ixj];
+          const bool up = (i & k) == 0;
+          if ((x > y) == up) {
+            keys[i] = y;
+            keys[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < batch; i += kOrderThreads) order[i] = (int32_t)(uint32_t)keys[i];
 }
 
 }  // namespace
 }  // namespace bte
 
+extern "C" int bte_attention_order(const int32_t* kv_len, int batch, int32_t* order_out,
+                                   hipStream_t stream) {
+  using namespace bte;
+  if (!kv_len || !order_out) return BTE_ERR_NULL;
+  if (batch <= 0 || batch > kOrderMax) return BTE_ERR_DIM;
+  int n_pad = 1;
+  while (n_pad < batch) n_pad <<= 1;
+  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), (size_t)n_pad * sizeof(uint64_t),
+                     stream, kv_len, batch, n_pad, order_out);
+  return hipGetLastError() == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
+}
+
 extern "C" int bte_reduced_attention(const void* q, const int32_t* count, const int32_t* cu,
                                      const void* cache_k, const void* cache_v,
-                                     const int64_t* seq_start, const int32_t* kv_len, void* out,
-                                     int batch, int k_max, int hq, int hkv, int head_dim,
-                                     float scale, bte_dtype dtype, hipStream_t stream) {
+                                     const int64_t* seq_start, const int32_t* kv_len,
+                                     const int32_t* order, void* out, int batch, int k_max, int hq,
+                                     int hkv, int head_dim, float scale, bte_dtype dtype,
+                                     hipStream_t stream) {
   using namespace bte;
   if (!q || !count || !cu || !cache_k || !cache_v || !seq_start || !kv_len || !out)
     return BTE_ERR_NULL;
@@ -448,16 +559,13 @@ extern "C" int bte_reduced_attention(const void* q, const int32_t* count, const 
   if (!aligned16(q) || !aligned16(cache_k) || !aligned16(cache_v) || !aligned16(out))
     return BTE_ERR_ALIGN;
   if (k_max == 0) return BTE_OK;
-  const float c = scale * kLog2e;
+  const AttnArgs a{q, count, cu, cache_k, cache_v, seq_start, kv_len, order, out,
+                   batch, k_max, hq, hkv, scale * kLog2e};
   hipError_t e;
   if (dtype == BTE_BF16)
-    e = head_dim == 128
-            ? launch_t<128, true>(q, count, cu, cache_k, cache_v, seq_start, kv_len, out, batch, k_max, hq, hkv, c, stream)
-            : launch_t<64, true>(q, count, cu, cache_k, cache_v, seq_start, kv_len, out, batch, k_max, hq, hkv, c, stream);
-  else
-    e = head_dim == 128
-            ? launch_t<128, false>(q, count, cu, cache_k, cache_v, seq_start, kv_len, out, batch, k_max, hq, hkv, c, stream)
-            : launch_t<64, false>(q, count, cu, cache_k, cache_v, seq_start, kv_len, out, batch, k_max, hq, hkv, c, stream);
+    e = head_dim == 128 ? launch_bf16<128>(a, stream) : launch_bf16<64>(a, stream);
+  else  // fp32 operands take twice the registers: 32 query rows per workgroup only
+    e = head_dim == 128 ? launch<128, false, 1, 4>(a, stream) : launch<64, false, 1, 4>(a, stream);
   if (e == hipErrorInvalidValue) return BTE_ERR_DIM;
   return e == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
 }

@@ -166,21 +166,45 @@ int bte_kv_scatter(const void* new_k, const void* new_v, const int32_t* idx, con
  *   s_j = scale * q[r,h,:] . cache_k[seq_start[b] + j, g, :],  j < kv_len[b]
  *   out[r,h,:] = sum_j softmax(s)_j * cache_v[seq_start[b] + j, g, :]
  * No mask: each kept query sees the whole prefix and the whole block.
- * Softmax and accumulation in float32; with BTE_BF16, the probabilities are
- * rounded to bf16 for the P.V product and out is rounded once to bf16.
+ * Softmax and accumulation in float32; with BTE_BF16 the P.V product takes
+ * the probabilities as a sum of two bf16 parts (hi + lo, about 16 significant
+ * bits) and out is rounded once to bf16.
  *
  *   q, out [>= cu[batch], hq, head_dim] dtype
  *   cache_k, cache_v [rows, hkv, head_dim] dtype
  *   count [batch], cu [batch + 1] int32; seq_start [batch] int64;
  *   kv_len [batch] int32 (>= 1 for every sequence with count > 0)
+ *   order [batch] int32 or NULL: the sequences in the order their work is
+ *     started, normally from bte_attention_order (longest first). It only
+ *     schedules: any permutation of 0..batch-1 gives the same results. An
+ *     entry outside [0, batch) is clamped into it (wrong results, no stray
+ *     memory access).
+ *   scale > 0 and finite (1/sqrt(head_dim) for the standard attention)
  * Limits: head_dim in {64, 128}; hq % hkv == 0.
- * Errors: NULL -> BTE_ERR_NULL; sizes <= 0, k_max < 0 or hq % hkv != 0 ->
- * BTE_ERR_DIM; head_dim or dtype unsupported -> BTE_ERR_UNSUPPORTED.
+ * Errors: NULL -> BTE_ERR_NULL; sizes <= 0, k_max < 0, hq % hkv != 0 or a
+ * scale that is not positive and finite -> BTE_ERR_DIM; head_dim or dtype
+ * unsupported -> BTE_ERR_UNSUPPORTED; q, caches or out not 16-byte aligned ->
+ * BTE_ERR_ALIGN.
  */
 int bte_reduced_attention(const void* q, const int32_t* count, const int32_t* cu,
                           const void* cache_k, const void* cache_v, const int64_t* seq_start,
-                          const int32_t* kv_len, void* out, int batch, int k_max, int hq, int hkv,
-                          int head_dim, float scale, bte_dtype dtype, hipStream_t stream);
+                          const int32_t* kv_len, const int32_t* order, void* out, int batch,
+                          int k_max, int hq, int hkv, int head_dim, float scale, bte_dtype dtype,
+                          hipStream_t stream);
+
+/*
+ * Work order for bte_reduced_attention: order_out[0..batch-1] = the sequence
+ * indices sorted by kv_len descending, ties by index ascending. Starting the
+ * longest sequences first keeps them out of the kernel's tail (greedy
+ * longest-processing-time scheduling); the lengths are the same for every
+ * layer of a denoising step, so one call serves all of the step's attention
+ * calls. Negative lengths count as 0.
+ *
+ *   kv_len [batch] int32; order_out [batch] int32 (4 byte alignment each)
+ * Limits: 1 <= batch <= 16384.
+ * Errors: NULL -> BTE_ERR_NULL; batch out of range -> BTE_ERR_DIM.
+ */
+int bte_attention_order(const int32_t* kv_len, int batch, int32_t* order_out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

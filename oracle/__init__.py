@@ -16,6 +16,8 @@ operations of the path, written from the pages' definitions:
   exact KV cache (ES-dLLM notes page, key design 2; FOCUS paper App. E.2.4).
 * ``reduced_attention`` — attention of the kept queries over prefix plus
   block KV (FOCUS paper Section 2, Section 4.2; App. E.2.4).
+* ``attention_order`` — the longest-first work order the GPU attention is
+  scheduled by (a scheduling helper, not part of the method).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package. The product path
@@ -31,7 +33,8 @@ from .esdllm import esdllm_score
 from .selection import topk_select
 from .rows import gather_rows, kv_scatter
 from .attention import reduced_attention
+from .schedule import attention_order
 
 __all__ = ["block_scores", "maxpool_keys", "softmax_keys", "importance",
            "focus_importance_delta", "esdllm_score", "topk_select", "gather_rows",
-           "kv_scatter", "reduced_attention"]
+           "kv_scatter", "reduced_attention", "attention_order"]

@@ -25,7 +25,7 @@ def declared():
 
 def test_every_declared_symbol_is_exported():
     names = declared()
-    assert len(names) == 8
+    assert len(names) == 9
     for name in names:
         assert hasattr(lib, name), name
 
@@ -95,7 +95,9 @@ def test_rows_errors():
 
 def test_attention_errors():
     f = lib.bte_reduced_attention
-    args = [FAKE] * 8 + [4, 8, 32, 8, 128, 0.088, 1, None]
+    # q, count, cu, cache_k, cache_v, seq_start, kv_len, order, out, batch, k_max, hq, hkv,
+    # head_dim, scale, dtype, stream
+    args = [FAKE] * 9 + [4, 8, 32, 8, 128, 0.088, 1, None]
 
     def call(**kw):
         a = list(args)
@@ -103,11 +105,24 @@ def test_attention_errors():
             a[int(i[1:])] = v
         return f(*a)
     assert call(a0=None) == NULL
-    assert call(a7=None) == NULL
-    assert call(a8=0) == DIM
-    assert call(a9=-1) == DIM
-    assert call(a10=30) == DIM
-    assert call(a12=96) == UNSUP
-    assert call(a14=3) == UNSUP
+    assert call(a8=None) == NULL
+    assert call(a9=0) == DIM
+    assert call(a10=-1) == DIM
+    assert call(a11=30) == DIM
+    assert call(a14=0.0) == DIM
+    assert call(a14=-0.1) == DIM
+    assert call(a14=float("inf")) == DIM
+    assert call(a14=float("nan")) == DIM
+    assert call(a13=96) == UNSUP
+    assert call(a15=3) == UNSUP
     assert call(a3=MIS) == ALIGN
-    assert call(a9=0) == OK
+    assert call(a10=0) == OK                  # nothing kept: no launch
+    assert call(a7=None, a10=0) == OK         # the order is optional
+
+
+def test_attention_order_errors():
+    f = lib.bte_attention_order
+    assert f(None, 4, FAKE, None) == NULL
+    assert f(FAKE, 4, None, None) == NULL
+    assert f(FAKE, 0, FAKE, None) == DIM
+    assert f(FAKE, 16385, FAKE, None) == DIM

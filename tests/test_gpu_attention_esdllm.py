@@ -17,13 +17,15 @@ def _bte():
     return bte
 
 
-def _attn(cfg, ai=None, rows=None):
+def _attn(cfg, ai=None, rows=None, ordered=False):
     bte = _bte()
     ai = ai if ai is not None else W.attention_inputs(cfg)
     g = dev(ai)
-    say(f"attention {cfg.name} batch={cfg.batch} hq={cfg.hq} hkv={cfg.hkv} D={cfg.head_dim} k_max={ai['k_max']}")
+    say(f"attention {cfg.name} batch={cfg.batch} hq={cfg.hq} hkv={cfg.hkv} D={cfg.head_dim} "
+        f"k_max={ai['k_max']} ordered={ordered}")
+    order = bte.attention_order(g["kv_len"]) if ordered else None
     out = bte.reduced_attention(g["q"], g["count"], g["cu"], g["cache_k"], g["cache_v"],
-                                g["seq_start"], g["kv_len"], ai["k_max"])
+                                g["seq_start"], g["kv_len"], ai["k_max"], order=order)
     torch.cuda.synchronize()
     f64 = W.to_f64
     ref = oracle.reduced_attention(f64(ai["q"]), ai["count"].numpy(), ai["cu"].numpy(),
@@ -61,8 +63,53 @@ CASES = [
 
 
 @pytest.mark.parametrize("cfg", CASES, ids=[c.name for c in CASES])
-def test_attention_edge_cases(cfg):
-    _attn(cfg)
+@pytest.mark.parametrize("ordered", [False, True], ids=["index_order", "longest_first"])
+def test_attention_edge_cases(cfg, ordered):
+    _attn(cfg, ordered=ordered)
+
+
+# Enough (sequence, KV head) items that the launch takes one wave per item
+# (with a longest-first order) or two (without); budgets 4..12 kept rows give
+# workgroups of one and of two 32-row query tiles. Short prefixes keep the
+# float64 oracle fast.
+MANY = [
+    W.AttnCfg("many_items", seed=61, batch=600, kept=None, k_lo=0, k_hi=12, hq=32, hkv=8,
+              head_dim=128, prefix_lo=1, prefix_hi=200),
+    W.AttnCfg("many_items_d64", seed=62, batch=520, kept=None, k_lo=1, k_hi=16, hq=32, hkv=8,
+              head_dim=64, prefix_lo=30, prefix_hi=90),
+]
+
+
+@pytest.mark.parametrize("cfg", MANY, ids=[c.name for c in MANY])
+@pytest.mark.parametrize("ordered", [False, True], ids=["index_order", "longest_first"])
+def test_attention_many_items(cfg, ordered):
+    _attn(cfg, ordered=ordered)
+
+
+@pytest.mark.parametrize("batch", [1, 7, 1024, 5000, 16384])
+def test_attention_order_matches_oracle(batch):
+    bte = _bte()
+    lens = np.random.default_rng(batch).integers(-3, 300, batch).astype(np.int32)   # ties, negatives
+    say(f"attention_order batch={batch}")
+    got = bte.attention_order(torch.from_numpy(lens).cuda()).cpu().numpy()
+    np.testing.assert_array_equal(got, oracle.attention_order(lens))
+
+
+def test_attention_order_only_schedules():
+    """Two different orders (same launch shape) give bit-identical outputs."""
+    bte = _bte()
+    cfg = W.AttnCfg("perm", seed=63, batch=300, kept=None, k_lo=2, k_hi=12, prefix_lo=10,
+                    prefix_hi=400)
+    ai = W.attention_inputs(cfg)
+    g = dev(ai)
+    say("attention order invariance")
+    lpt = bte.attention_order(g["kv_len"])
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(cfg.batch).astype(np.int32)).cuda()
+    outs = [bte.reduced_attention(g["q"], g["count"], g["cu"], g["cache_k"], g["cache_v"],
+                                  g["seq_start"], g["kv_len"], ai["k_max"], order=o)
+            for o in (lpt, perm)]
+    n = int(ai["cu"][-1])
+    assert torch.equal(outs[0][:n], outs[1][:n])
 
 
 def test_attention_kv_len_one_is_v0_exactly():

@@ -111,3 +111,28 @@ def test_attention_key_permutation_invariance():
         perm[ss[b]:ss[b] + L[b]] = ss[b] + np.random.default_rng(b).permutation(L[b])
     got = oracle.reduced_attention(q, count, cu, ck[perm], cv[perm], ss, L, hq, hkv, 0.25)
     np.testing.assert_allclose(got, base, rtol=1e-11, atol=1e-13)
+
+
+def test_attention_order_brute_force():
+    """The order is the unique permutation with non-increasing lengths whose
+    equal-length runs are in ascending index order: found here by enumerating
+    every permutation of small inputs (ties, zeros and a negative length)."""
+    import itertools
+    cases = [[3], [1, 1, 1], [2, 5, 5, 0], [-4, 0, 7, 7, 1], [9, 2, 9, 2, 9, 4]]
+    for lens in cases:
+        eff = [max(v, 0) for v in lens]
+        valid = [p for p in itertools.permutations(range(len(lens)))
+                 if all(eff[p[i]] > eff[p[i + 1]] or (eff[p[i]] == eff[p[i + 1]] and p[i] < p[i + 1])
+                        for i in range(len(p) - 1))]
+        assert len(valid) == 1
+        np.testing.assert_array_equal(oracle.attention_order(np.array(lens, np.int32)), valid[0])
+
+
+def test_attention_order_invariants():
+    lens = np.random.default_rng(8).integers(1, 50, 3000).astype(np.int32)
+    o = oracle.attention_order(lens)
+    assert sorted(o.tolist()) == list(range(lens.size))
+    d = lens[o]
+    assert np.all(d[:-1] >= d[1:])
+    tie = d[:-1] == d[1:]
+    assert np.all(o[:-1][tie] < o[1:][tie])
