@@ -57,6 +57,12 @@ __device__ __forceinline__ float swap_halves(float v) { return __shfl_xor(v, 32,
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt left at their maxima, i.e. not waited on. Used to wait for all but
+// the newest N HBM->LDS copies of a wave.
+constexpr int kVmcntNoLgkm = (0x7 << 4) | (0xF << 8);
+constexpr int vmcnt_bits(int n) { return (n & 15) | ((n >> 4) << 14); }
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace bte

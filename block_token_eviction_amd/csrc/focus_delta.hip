@@ -6,10 +6,14 @@
 //   dI[j]   = I_1[j] - I_0[j], -inf where decoded.
 //
 // Work layout: one workgroup per sequence, one wave per KV-head group g
-// (looping when there are more groups than waves). A wave keeps the group's
-// key tiles of both layers in registers and streams the G query-head tiles of
-// each layer through a 2-deep register ring, so that the next 8 KB tile is in
-// flight while one is being reduced.
+// (looping when there are more groups than waves). A wave streams the tiles
+// of its group, 32 rows each (K of layer 0, K of layer 1, then the Q tiles of
+// the G query heads, layers interleaved), from HBM straight into a two-stage
+// LDS ring with coalesced non-temporal copies (whole rows, no registers), so
+// the next tile is in flight while one is used. Key tiles are copied from LDS
+// into registers once per group; query tiles are read from LDS as MFMA
+// operands. 16-byte chunks of a tile row are XOR-swizzled by the row so that
+// the operand reads spread over the LDS banks.
 //
 // Score tile: S^T = K . Q^T on the matrix cores, keys as MFMA rows and query
 // rows as MFMA columns. Key row m of the MFMA is fed from block key
@@ -27,23 +31,36 @@
 namespace bte {
 namespace {
 
-constexpr int kRing = 2;
+// One tile: 32 rows of D elements. Copied 16 bytes per lane, kRpi rows per
+// wave-wide copy; a lane's MFMA operand is half a row (kHalf chunks).
+template <int D, bool BF16>
+struct Tile {
+  static constexpr int kRowBytes = D * (BF16 ? 2 : 4);
+  static constexpr int kChunks = kRowBytes / 16;
+  static constexpr int kHalf = kChunks / 2;
+  static constexpr int kRpi = 64 / kChunks;
+  static constexpr int kCopies = 32 / kRpi;           // wave-wide copies per tile
+  static constexpr int kBytes = 32 * kRowBytes;
+};
 
-// This lane's half of one D-element row: elements [h*D/2, (h+1)*D/2).
+// LDS position of 16-byte chunk c of tile row `row`.
+__device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7); }
+
+// Cache policy of the HBM->LDS copies: non-temporal (every byte is read once).
+constexpr int kStreamPolicy = 2;
+
+// This lane's MFMA operand: half h of one tile row, as kHalf 16-byte chunks.
 template <int D, bool BF16>
 struct HalfRow {
-  static constexpr int kBytes = BF16 ? D : 2 * D;
-  static constexpr int kN = kBytes / 16;
-  u32x4 v[kN];
+  u32x4 v[Tile<D, BF16>::kHalf];
 };
 
 template <int D, bool BF16>
-__device__ __forceinline__ void load_half(HalfRow<D, BF16>& r, const char* row, int h, bool valid) {
-  const char* p = row + h * HalfRow<D, BF16>::kBytes;
+__device__ __forceinline__ void read_half(HalfRow<D, BF16>& r, const char* tile, int row, int h) {
+  using Tl = Tile<D, BF16>;
 #pragma unroll
-  for (int c = 0; c < HalfRow<D, BF16>::kN; ++c) {
-    r.v[c] = valid ? ld16(p + 16 * c) : u32x4{0u, 0u, 0u, 0u};
-  }
+  for (int c = 0; c < Tl::kHalf; ++c)
+    r.v[c] = ld16(tile + row * Tl::kRowBytes + (swz(row, h * Tl::kHalf + c) << 4));
 }
 
 // S^T tile (32 keys x 32 query rows): contraction over the lane-halves' D/2
@@ -54,10 +71,10 @@ __device__ __forceinline__ f32x16 score_tile(const HalfRow<D, BF16>& k, const Ha
   f32x16 acc = {};
   if constexpr (BF16) {
 #pragma unroll
-    for (int c = 0; c < HalfRow<D, BF16>::kN; ++c) acc = mfma_bf16(k.v[c], q.v[c], acc);
+    for (int c = 0; c < Tile<D, BF16>::kHalf; ++c) acc = mfma_bf16(k.v[c], q.v[c], acc);
   } else {
 #pragma unroll
-    for (int c = 0; c < HalfRow<D, BF16>::kN; ++c)
+    for (int c = 0; c < Tile<D, BF16>::kHalf; ++c)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         acc = mfma_f32(__uint_as_float(k.v[c][e]), __uint_as_float(q.v[c][e]), acc);
@@ -162,75 +179,107 @@ __device__ __forceinline__ void pool_softmax_accumulate(const f32x16& s, int h, 
   for (int r = 0; r < 16; ++r) acc[r] = fmaf(e[r], inv, acc[r]);
 }
 
-template <int D, bool BF16, int R>
-__global__ __launch_bounds__(512) void focus_delta_kernel(
+// Copies tile t of KV group g of sequence b into LDS at dst: t = 0, 1 -> K of
+// layer 0, 1; t = 2 + 2e + l -> Q of query head e of the group, layer l. Lane
+// (lrow, lslot) copies chunk swz(row, lslot) of row kRpi*i + lrow to LDS chunk
+// lslot of that row, for each of the kCopies wave-wide copies i. Rows past the
+// block repeat its last row (their scores are masked).
+template <int D, bool BF16>
+__device__ __forceinline__ void issue_tile(const char* __restrict__ q0, const char* __restrict__ k0,
+                                           const char* __restrict__ q1, const char* __restrict__ k1,
+                                           int b, int B, int hq, int hkv, int g, int t, char* dst,
+                                           int lrow, int lslot) {
+  using Tl = Tile<D, BF16>;
+  const char* src;
+  uint32_t stride;
+  if (t < 2) {
+    src = (t ? k1 : k0) + ((size_t)b * B * hkv + g) * Tl::kRowBytes;
+    stride = (uint32_t)hkv * Tl::kRowBytes;
+  } else {
+    const int e = (t - 2) >> 1;
+    src = ((t & 1) ? q1 : q0) + ((size_t)b * B * hq + (size_t)g * (hq / hkv) + e) * Tl::kRowBytes;
+    stride = (uint32_t)hq * Tl::kRowBytes;
+  }
+#pragma unroll
+  for (int i = 0; i < Tl::kCopies; ++i) {
+    const int row = Tl::kRpi * i + lrow;
+    const int srow = row < B ? row : B - 1;
+    __builtin_amdgcn_global_load_lds(
+        (const void __attribute__((address_space(1)))*)(src + srow * stride + 16 * swz(row, lslot)),
+        (void __attribute__((address_space(3)))*)(dst + 1024 * i), 16, 0, kStreamPolicy);
+  }
+}
+
+template <int D, bool BF16, int R, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void focus_delta_kernel(
     const char* __restrict__ q0, const char* __restrict__ k0, const char* __restrict__ q1,
     const char* __restrict__ k1, const uint8_t* __restrict__ decoded, float* __restrict__ out,
     int B, int hq, int hkv, int rt_r, float c) {
-  constexpr int ES = BF16 ? 2 : 4;
+  using Tl = Tile<D, BF16>;
   using Row = HalfRow<D, BF16>;
-  __shared__ float red[16][2][32];
+  // Two LDS stages per wave when they fit in 128 KB.
+  constexpr int kStages = kWaves * 2 * Tl::kBytes <= 128 * 1024 ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) char ring[kWaves * kStages * Tl::kBytes];
+  __shared__ float red[kWaves][2][32];
 
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31;
   const int h = lane >> 5;
   const int G = hq / hkv;
-  const size_t qrow = (size_t)hq * D * ES;
-  const size_t krow = (size_t)hkv * D * ES;
   const int kj = 16 * ((n >> 2) & 1) + (n & 3) + 4 * (n >> 3);
-  const bool kvalid = kj < B;
   const bool qvalid = n < B;
-  const char* qbase0 = q0 + ((size_t)b * B + n) * qrow;
-  const char* qbase1 = q1 + ((size_t)b * B + n) * qrow;
+  char* wring = ring + w * kStages * Tl::kBytes;
 
+  // Tile t of group gi (this wave's gi-th group): t = 0, 1 -> K of layer 0, 1;
+  // t = 2 + 2e + l -> Q of head e of the group, layer l.
+  const int ngroups = (hkv - w + kWaves - 1) / kWaves;
+  const int per_group = 2 + 2 * G;
+  const int ntiles = ngroups * per_group;
+  const int lrow = lane / Tl::kChunks;
+  const int lslot = lane % Tl::kChunks;
   float acc0[16], acc1[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
 
-  for (int g = w; g < hkv; g += nw) {
-    Row K0, K1;
-    load_half<D, BF16>(K0, k0 + ((size_t)b * B + kj) * krow + (size_t)g * D * ES, h, kvalid);
-    load_half<D, BF16>(K1, k1 + ((size_t)b * B + kj) * krow + (size_t)g * D * ES, h, kvalid);
-    // Query tiles in the order (head e, layer l) = (0,0), (0,1), (1,0), ...
-    const int ntile = 2 * G;
-    auto qtile = [&](Row& dst, int t) {
-      if (t < ntile) {
-        const size_t off = (size_t)(g * G + (t >> 1)) * D * ES;
-        load_half<D, BF16>(dst, ((t & 1) ? qbase1 : qbase0) + off, h, qvalid);
-      }
-    };
-    Row ring[kRing];
-#pragma unroll
-    for (int s = 0; s < kRing; ++s) qtile(ring[s], s);
-
-    auto step = [&](Row& slot, int t) {
-      if (t < ntile) {
-        if (t & 1) {
-          f32x16 s = score_tile<D, BF16>(K1, slot);
-          if (B < 32) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[r] = (16 * h + r < B) ? s[r] : -INFINITY;
-          }
-          qtile(slot, t + kRing);
-          pool_softmax_accumulate<R>(s, h, rt_r, B, c, qvalid, acc1);
-        } else {
-          f32x16 s = score_tile<D, BF16>(K0, slot);
-          if (B < 32) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[r] = (16 * h + r < B) ? s[r] : -INFINITY;
-          }
-          qtile(slot, t + kRing);
-          pool_softmax_accumulate<R>(s, h, rt_r, B, c, qvalid, acc0);
-        }
-      }
-    };
-    for (int t = 0; t < ntile; t += kRing) {
-#pragma unroll
-      for (int u = 0; u < kRing; ++u) step(ring[u], t + u);
+  auto issue = [&](int tile, int stage) __attribute__((always_inline)) {
+    const int gi = tile / per_group;
+    issue_tile<D, BF16>(q0, k0, q1, k1, b, B, hq, hkv, w + gi * kWaves, tile - gi * per_group,
+                        wring + stage * Tl::kBytes, lrow, lslot);
+  };
+  Row K0, K1;
+  if (ntiles > 0) issue(0, 0);
+  if (kStages == 2 && ntiles > 1) issue(1, 1);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int stage = kStages == 2 ? (tile & 1) : 0;
+    if (kStages == 2 && tile + 1 < ntiles) {
+      __builtin_amdgcn_s_waitcnt(kVmcntNoLgkm | vmcnt_bits(Tl::kCopies));
+    } else {
+      __builtin_amdgcn_s_waitcnt(kVmcntNoLgkm | vmcnt_bits(0));
     }
+    __builtin_amdgcn_wave_barrier();
+    const char* src = wring + stage * Tl::kBytes;
+    const int t = tile % per_group;
+    if (t < 2) {
+      if (t == 0) read_half<D, BF16>(K0, src, kj, h);
+      else read_half<D, BF16>(K1, src, kj, h);
+    } else {
+      Row Q;
+      read_half<D, BF16>(Q, src, n, h);
+      f32x16 s;
+      if (t & 1) s = score_tile<D, BF16>(K1, Q);
+      else s = score_tile<D, BF16>(K0, Q);
+      if (B < 32) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = (16 * h + r < B) ? s[r] : -INFINITY;
+      }
+      if (t & 1) pool_softmax_accumulate<R>(s, h, rt_r, B, c, qvalid, acc1);
+      else pool_softmax_accumulate<R>(s, h, rt_r, B, c, qvalid, acc0);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // The stage has been read into registers: refill it kStages tiles ahead.
+    if (tile + kStages < ntiles) issue(tile + kStages, stage);
   }
 
   // Sum over the 32 query rows held by each lane half (fixed butterfly order).
@@ -253,7 +302,7 @@ __global__ __launch_bounds__(512) void focus_delta_kernel(
   if (threadIdx.x < B) {
     const int j = threadIdx.x;
     float i0 = 0.f, i1 = 0.f;
-    for (int v = 0; v < nw; ++v) {
+    for (int v = 0; v < kWaves; ++v) {
       i0 += red[v][0][j];
       i1 += red[v][1][j];
     }
@@ -261,15 +310,25 @@ __global__ __launch_bounds__(512) void focus_delta_kernel(
   }
 }
 
+template <int D, bool BF16, int R, int kWaves>
+hipError_t launch_w(const void* q0, const void* k0, const void* q1, const void* k1,
+                    const uint8_t* decoded, float* out, int batch, int B, int hq, int hkv, int rt_r,
+                    float c, hipStream_t stream) {
+  hipLaunchKernelGGL((focus_delta_kernel<D, BF16, R, kWaves>), dim3(batch), dim3(64 * kWaves), 0,
+                     stream, (const char*)q0, (const char*)k0, (const char*)q1, (const char*)k1,
+                     decoded, out, B, hq, hkv, rt_r, c);
+  return hipGetLastError();
+}
+
+// One wave per KV group, at most 8 (a wave loops over groups beyond that).
 template <int D, bool BF16, int R>
 hipError_t launch_r(const void* q0, const void* k0, const void* q1, const void* k1,
                     const uint8_t* decoded, float* out, int batch, int B, int hq, int hkv, int rt_r,
                     float c, hipStream_t stream) {
-  const int waves = hkv < 8 ? hkv : 8;
-  hipLaunchKernelGGL((focus_delta_kernel<D, BF16, R>), dim3(batch), dim3(64 * waves), 0, stream,
-                     (const char*)q0, (const char*)k0, (const char*)q1, (const char*)k1, decoded,
-                     out, B, hq, hkv, rt_r, c);
-  return hipGetLastError();
+  if (hkv >= 8) return launch_w<D, BF16, R, 8>(q0, k0, q1, k1, decoded, out, batch, B, hq, hkv, rt_r, c, stream);
+  if (hkv >= 4) return launch_w<D, BF16, R, 4>(q0, k0, q1, k1, decoded, out, batch, B, hq, hkv, rt_r, c, stream);
+  if (hkv >= 2) return launch_w<D, BF16, R, 2>(q0, k0, q1, k1, decoded, out, batch, B, hq, hkv, rt_r, c, stream);
+  return launch_w<D, BF16, R, 1>(q0, k0, q1, k1, decoded, out, batch, B, hq, hkv, rt_r, c, stream);
 }
 
 template <int D, bool BF16>

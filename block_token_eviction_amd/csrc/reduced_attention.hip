@@ -62,11 +62,6 @@ struct Cfg {
 __device__ __forceinline__ int kpos(int row, int c) { return c ^ (row & 7); }
 __device__ __forceinline__ int vpos(int row, int c) { return c ^ (((row >> 4) & 1) << 2); }
 
-// s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14; expcnt and
-// lgkmcnt left at their maxima, i.e. not waited on.
-constexpr int kVmcntNoLgkm = (0x7 << 4) | (0xF << 8);
-constexpr int vmcnt_bits(int n) { return (n & 15) | ((n >> 4) << 14); }
-
 // Transposing LDS read (gfx950): in each 16-lane group, lane i receives element
 // i%4 of the 8 bytes addressed by group lanes i/4, i/4+4, i/4+8, i/4+12.
 // Issued as inline asm so that the compiler does not order it behind the
