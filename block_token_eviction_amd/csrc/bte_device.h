@@ -62,6 +62,8 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // the newest N HBM->LDS copies of a wave.
 constexpr int kVmcntNoLgkm = (0x7 << 4) | (0xF << 8);
 constexpr int vmcnt_bits(int n) { return (n & 15) | ((n >> 4) << 14); }
+// s_waitcnt immediate waiting for all LDS reads (lgkmcnt 0) and nothing else.
+constexpr int kLgkm0 = 0xF | (0x7 << 4) | (0x3 << 14);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

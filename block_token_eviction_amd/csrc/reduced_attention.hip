@@ -20,8 +20,10 @@
 // keys 16*(l/32)..+15), online softmax in fp32 in-lane, then O^T += V^T . P^T
 // on the matrix cores. K and V tiles are copied from HBM straight into LDS (no
 // registers) into two stages per wave, so the next tile's 16 KB are in flight
-// while the current one is being used; 16-byte chunks are XOR-swizzled by row
-// so that the K-operand reads and the transposing V reads are conflict-free.
+// while the current one is being used; a stage's K half is refilled as soon as
+// the scores are computed, its V half after P.V. 16-byte chunks are XOR-
+// swizzled by row so that the K-operand reads and the transposing V reads are
+// conflict-free.
 //
 // The softmax shift is a per-row reference max that only moves when a tile's
 // max exceeds it by more than 2^8 in the exp2 domain (so every exponentiated
@@ -164,32 +166,34 @@ __device__ __forceinline__ void attn_body(
   const int lrow = lane / C::kChunks;
   const int lslot = lane % C::kChunks;
   const uint32_t lane_row_off = (uint32_t)(lrow * kv_row);
-  auto issue_tile = [&](int kt, int stage) {
-    char* kdst = wave_lds + stage * C::kStageBytes;
-    char* vdst = kdst + C::kTile;
-    const size_t tile_off = (size_t)kt * 32 * kv_row;
-    const char* kb = kbase + tile_off;
-    const char* vb = vbase + tile_off;
+  // Copies the K (which = 0) or V (which = 1) half of key tile kt into `stage`.
+  auto issue_half = [&](int kt, int stage, int which) {
+    char* dst = wave_lds + stage * C::kStageBytes + which * C::kTile;
+    const char* base = (which ? vbase : kbase) + (size_t)kt * 32 * kv_row;
     if (kt * 32 + 32 <= L) {
 #pragma unroll
       for (int i = 0; i < C::kHalf; ++i) {
         const int row = C::kRpi * i + lrow;
         const size_t row_base = (size_t)(C::kRpi * i) * kv_row;      // wave-uniform
-        copy16_to_lds(kb + row_base + (lane_row_off + 16 * kpos(row, lslot)), kdst + 1024 * i);
-        copy16_to_lds(vb + row_base + (lane_row_off + 16 * vpos(row, lslot)), vdst + 1024 * i);
+        const int chunk = which ? vpos(row, lslot) : kpos(row, lslot);
+        copy16_to_lds(base + row_base + (lane_row_off + 16 * chunk), dst + 1024 * i);
       }
     } else {
       // Last, partial tile: rows past the sequence end repeat its last row.
-      // Their scores are masked below, so they get probability 0 and a finite V row.
+      // They get probability 0 below and a finite V row.
       const int last = L - 1 - kt * 32;
 #pragma unroll
       for (int i = 0; i < C::kHalf; ++i) {
         const int row = C::kRpi * i + lrow;
         const uint32_t roff = (uint32_t)((row < last ? row : last) * kv_row);
-        copy16_to_lds(kb + roff + 16 * kpos(row, lslot), kdst + 1024 * i);
-        copy16_to_lds(vb + roff + 16 * vpos(row, lslot), vdst + 1024 * i);
+        const int chunk = which ? vpos(row, lslot) : kpos(row, lslot);
+        copy16_to_lds(base + roff + 16 * chunk, dst + 1024 * i);
       }
     }
+  };
+  auto issue_tile = [&](int kt, int stage) {
+    issue_half(kt, stage, 0);
+    issue_half(kt, stage, 1);
   };
 
   // Lane part of the V^T transposing reads: k-slot (h, t) of P.V MFMA cc is
@@ -235,6 +239,14 @@ __device__ __forceinline__ void attn_body(
             s[tq] = mfma_f32(__uint_as_float(ka[e]), __uint_as_float(qop[tq][cc][e]), s[tq]);
         }
       }
+    }
+
+    // The K half of the stage is consumed: refill it with tile kt + kStages*kWaves
+    // now (the V half follows after P.V), once the operand reads have landed.
+    const int refill = kt + C::kStages * kWaves;
+    if (refill < ntiles) {
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      issue_half(refill, stage, 0);
     }
 
     // V^T operands, shared by the query tiles: k-slot (h, t) of MFMA cc is key
@@ -324,8 +336,8 @@ __device__ __forceinline__ void attn_body(
       }
     }
     __builtin_amdgcn_wave_barrier();
-    // This wave has consumed the stage: refill it with the tile kStages ahead.
-    if (kt + C::kStages * kWaves < ntiles) issue_tile(kt + C::kStages * kWaves, stage);
+    // The V half is consumed too: refill it.
+    if (refill < ntiles) issue_half(refill, stage, 1);
   }
 
   // Merge the 4 wave states: out = sum_w e^(m_w - M) O_w / sum_w e^(m_w - M) l_w.
@@ -486,41 +498,83 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t stream) {
   return launch<D, true, 1, 4>(a, stream);
 }
 
-// Descending-length processing order: one workgroup sorts (length desc, index
-// asc) keys in LDS with a bitonic network.
+// Descending-length processing order: one workgroup sorts 64-bit keys
+// (length descending, index ascending) with a bitonic network. Thread t holds
+// the E keys t*E .. t*E+E-1 in registers: exchange distances below E stay in
+// the thread, below 64*E in the wave (lane shuffles), larger ones go through
+// LDS between barriers.
 constexpr int kOrderThreads = 1024;
 constexpr int kOrderMax = 16384;
 
+__device__ __forceinline__ uint64_t order_key(const int32_t* kv_len, int i, int batch) {
+  if (i >= batch) return ~0ull;                                  // padding sorts last
+  const uint32_t len = (uint32_t)max(kv_len[i], 0);
+  return ((uint64_t)(0xffffffffu - len) << 32) | (uint32_t)i;
+}
+
+// New value of key x at position i after the compare-exchange with partner
+// position i ^ j holding y, in the bitonic merge of size k (ascending where
+// i & k == 0).
+__device__ __forceinline__ uint64_t bitonic_pick(uint64_t x, uint64_t y, int i, int j, int k) {
+  const bool lower = (i & j) == 0;
+  const bool up = (i & k) == 0;
+  const uint64_t lo = x < y ? x : y, hi = x < y ? y : x;
+  return lower == up ? lo : hi;
+}
+
+template <int E>
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __restrict__ kv_len,
                                                              int batch, int n_pad,
                                                              int32_t* __restrict__ order) {
-  extern __shared__ uint64_t keys[];
-  for (int i = threadIdx.x; i < n_pad; i += kOrderThreads) {
-    uint64_t k = ~0ull;
-    if (i < batch) {
-      const uint32_t len = (uint32_t)max(kv_len[i], 0);
-      k = ((uint64_t)(0xffffffffu - len) << 32) | (uint32_t)i;
-    }
-    keys[i] = k;
-  }
-  __syncthreads();
+  __shared__ uint64_t xch[E * kOrderThreads];
+  const int t = threadIdx.x;
+  const int nthreads = n_pad / E;
+  const bool active = t < nthreads;
+  uint64_t v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) v[e] = order_key(kv_len, t * E + e, batch);
   for (int k = 2; k <= n_pad; k <<= 1) {
-    for (int jj = k >> 1; jj > 0; jj >>= 1) {
-      for (int i = threadIdx.x; i < n_pad; i += kOrderThreads) {
-        const int ixj = i ^ jj;
-        if (ixj > i) {
-          const uint64_t x = keys[i], y = keys[ixj];
-          const bool up = (i & k) == 0;
-          if ((x > y) == up) {
-            keys[i] = y;
-            keys[ixj] = x;
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j < E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int pe = e ^ j;
+          if (pe > e) {
+            const int i = t * E + e;
+            const uint64_t x = v[e], y = v[pe];
+            v[e] = bitonic_pick(x, y, i, j, k);
+            v[pe] = bitonic_pick(y, x, i ^ j, j, k);
+          }
+        }
+      } else if (j < 64 * E) {
+        const int lj = j / E;                                    // partner lane distance
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint64_t y = __shfl_xor(v[e], lj, kWave);
+          v[e] = bitonic_pick(v[e], y, t * E + e, j, k);
+        }
+      } else {
+        __syncthreads();
+        if (active) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) xch[t * E + e] = v[e];
+        }
+        __syncthreads();
+        if (active) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const int i = t * E + e;
+            v[e] = bitonic_pick(v[e], xch[i ^ j], i, j, k);
           }
         }
       }
-      __syncthreads();
     }
   }
-  for (int i = threadIdx.x; i < batch; i += kOrderThreads) order[i] = (int32_t)(uint32_t)keys[i];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = t * E + e;
+    if (active && i < batch) order[i] = (int32_t)(uint32_t)v[e];
+  }
 }
 
 }  // namespace
@@ -531,10 +585,17 @@ extern "C" int bte_attention_order(const int32_t* kv_len, int batch, int32_t* or
   using namespace bte;
   if (!kv_len || !order_out) return BTE_ERR_NULL;
   if (batch <= 0 || batch > kOrderMax) return BTE_ERR_DIM;
-  int n_pad = 1;
+  int n_pad = 64;
   while (n_pad < batch) n_pad <<= 1;
-  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), (size_t)n_pad * sizeof(uint64_t),
-                     stream, kv_len, batch, n_pad, order_out);
+  const int e = n_pad > kOrderThreads ? n_pad / kOrderThreads : 1;
+  const int threads = n_pad / e;
+  switch (e) {
+    case 1: hipLaunchKernelGGL(order_kernel<1>, dim3(1), dim3(threads), 0, stream, kv_len, batch, n_pad, order_out); break;
+    case 2: hipLaunchKernelGGL(order_kernel<2>, dim3(1), dim3(threads), 0, stream, kv_len, batch, n_pad, order_out); break;
+    case 4: hipLaunchKernelGGL(order_kernel<4>, dim3(1), dim3(threads), 0, stream, kv_len, batch, n_pad, order_out); break;
+    case 8: hipLaunchKernelGGL(order_kernel<8>, dim3(1), dim3(threads), 0, stream, kv_len, batch, n_pad, order_out); break;
+    default: hipLaunchKernelGGL(order_kernel<16>, dim3(1), dim3(threads), 0, stream, kv_len, batch, n_pad, order_out); break;
+  }
   return hipGetLastError() == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
 }
 

@@ -86,7 +86,7 @@ def test_attention_many_items(cfg, ordered):
     _attn(cfg, ordered=ordered)
 
 
-@pytest.mark.parametrize("batch", [1, 7, 1024, 5000, 16384])
+@pytest.mark.parametrize("batch", [1, 7, 64, 65, 1000, 1024, 2000, 3000, 5000, 16384])
 def test_attention_order_matches_oracle(batch):
     bte = _bte()
     lens = np.random.default_rng(batch).integers(-3, 300, batch).astype(np.int32)   # ties, negatives
