@@ -6,10 +6,13 @@
 // FOCUS paper App. E.2.4, sparse cache fill at processing indices):
 //   cache[row_base[b] + pos(b, t)] = new[cu[b] + t],  pos = idx or pos_map[b, idx]
 //
-// Both are pure byte copies of 16-byte-aligned rows. The per-sequence counts
-// live on the device, so the grid covers the upper bound batch * k_max rows
-// and a workgroup whose slot t >= count[b] exits at once. Each thread moves up
-// to kUnroll 16-byte chunks per pass with all loads issued before the stores.
+// Both are pure byte copies of 16-byte-aligned rows, with non-temporal hints
+// (every byte is touched once) and kUnroll chunks in flight per thread, all
+// loads issued before the stores. The per-sequence counts live on the device,
+// so grids are sized from k_max and surplus workgroups exit at once. The
+// gather (hidden rows, 8 KB at the workloads) takes one workgroup per row;
+// the scatter (K/V rows of a few KB) treats a sequence's kept rows as one flat
+// space of count[b] * chunks-per-row chunks split over n_split workgroups.
 #include "bte_device.h"
 
 namespace bte {
@@ -17,10 +20,65 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
+constexpr int kPass = kThreads * kUnroll;   // chunks one workgroup moves per pass
 
-__device__ __forceinline__ void copy_row(const char* __restrict__ s, char* __restrict__ d,
-                                         size_t chunks) {
-  for (size_t base = 0; base < chunks; base += (size_t)kThreads * kUnroll) {
+// Row and chunk of flat chunk index c, with chunks per row cpr and its float
+// reciprocal (exact after the +-1 correction for c < 2^24).
+__device__ __forceinline__ void split_chunk(uint32_t c, uint32_t cpr, float inv_cpr, uint32_t& row,
+                                            uint32_t& chunk) {
+  uint32_t t = (uint32_t)((float)c * inv_cpr);
+  if (t * cpr > c) --t;
+  if ((t + 1) * cpr <= c) ++t;
+  row = t;
+  chunk = c - t * cpr;
+}
+
+// Copies chunks [lo, hi) of the flat space: row t's source is src_row(t) and
+// its destination dst_row(t) (byte pointers).
+template <class SrcRow, class DstRow>
+__device__ __forceinline__ void copy_range(uint32_t lo, uint32_t hi, uint32_t cpr, float inv_cpr,
+                                           SrcRow src_row, DstRow dst_row) {
+  for (uint32_t base = lo; base < hi; base += kPass) {
+    u32x4 v[kUnroll];
+    char* d[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t c = base + u * kThreads + threadIdx.x;
+      d[u] = nullptr;
+      if (c < hi) {
+        uint32_t t, ch;
+        split_chunk(c, cpr, inv_cpr, t, ch);
+        v[u] = ld16_stream(src_row(t) + 16 * (size_t)ch);
+        d[u] = dst_row(t) + 16 * (size_t)ch;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (d[u])
+        __builtin_nontemporal_store(v[u], (__attribute__((address_space(1))) u32x4*)d[u]);
+  }
+}
+
+// This workgroup's share [lo, hi) of sequence b's `total` chunks, `per` each.
+__device__ __forceinline__ bool share(uint32_t total, uint32_t per, uint32_t s, uint32_t& lo,
+                                      uint32_t& hi) {
+  lo = s * per;
+  hi = min(total, lo + per);
+  return lo < hi;
+}
+
+// Gather: one workgroup per (sequence, slot t < k_max); a slot past count[b]
+// exits. Large rows (hidden states) give every thread whole chunks of one row.
+__global__ __launch_bounds__(kThreads) void gather_rows_kernel(
+    const char* __restrict__ src, const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
+    const int32_t* __restrict__ cu, char* __restrict__ dst, int n, int k_max, size_t row_bytes) {
+  const int b = blockIdx.x / k_max;
+  const int t = blockIdx.x - b * k_max;
+  if (t >= count[b]) return;
+  const char* s = src + ((size_t)b * n + idx[(size_t)b * k_max + t]) * row_bytes;
+  char* d = dst + ((size_t)cu[b] + t) * row_bytes;
+  const size_t chunks = row_bytes / 16;
+  for (size_t base = 0; base < chunks; base += kPass) {
     u32x4 v[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -35,32 +93,50 @@ __device__ __forceinline__ void copy_row(const char* __restrict__ s, char* __res
   }
 }
 
-__global__ __launch_bounds__(kThreads) void gather_rows_kernel(
-    const char* __restrict__ src, const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
-    const int32_t* __restrict__ cu, char* __restrict__ dst, int n, int k_max, size_t row_bytes) {
-  const int b = blockIdx.x / k_max;
-  const int t = blockIdx.x - b * k_max;
-  if (t >= count[b]) return;
-  const int j = idx[(size_t)b * k_max + t];
-  copy_row(src + ((size_t)b * n + j) * row_bytes, dst + ((size_t)cu[b] + t) * row_bytes,
-           row_bytes / 16);
-}
-
 __global__ __launch_bounds__(kThreads) void scatter_rows_kernel(
     const char* __restrict__ new_k, const char* __restrict__ new_v, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ count, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ pos_map, int n, const int64_t* __restrict__ row_base,
-    char* __restrict__ cache_k, char* __restrict__ cache_v, int k_max, size_t row_bytes) {
-  const int b = blockIdx.x / k_max;
-  const int t = blockIdx.x - b * k_max;
-  if (t >= count[b]) return;
-  const int j = idx[(size_t)b * k_max + t];
-  const int64_t pos = pos_map ? pos_map[(size_t)b * n + j] : j;
-  const size_t dst_row = (size_t)(row_base[b] + pos);
-  const size_t src_row = (size_t)cu[b] + t;
-  const char* s = blockIdx.y == 0 ? new_k : new_v;
-  char* d = blockIdx.y == 0 ? cache_k : cache_v;
-  copy_row(s + src_row * row_bytes, d + dst_row * row_bytes, row_bytes / 16);
+    char* __restrict__ cache_k, char* __restrict__ cache_v, int k_max, size_t row_bytes,
+    int n_split, uint32_t per, float inv_cpr) {
+  const int b = blockIdx.x / n_split;
+  const uint32_t s = blockIdx.x - b * n_split;
+  const uint32_t cpr = (uint32_t)(row_bytes / 16);
+  uint32_t lo, hi;
+  if (!share((uint32_t)count[b] * cpr, per, s, lo, hi)) return;
+  const int32_t* ib = idx + (size_t)b * k_max;
+  const int32_t* pm = pos_map ? pos_map + (size_t)b * n : nullptr;
+  const int64_t rb = row_base[b];
+  const char* sb = (blockIdx.y == 0 ? new_k : new_v) + (size_t)cu[b] * row_bytes;
+  char* cache = blockIdx.y == 0 ? cache_k : cache_v;
+  copy_range(lo, hi, cpr, inv_cpr, [&](uint32_t t) { return sb + (size_t)t * row_bytes; },
+             [&](uint32_t t) {
+               const int j = ib[t];
+               const int64_t pos = pm ? pm[j] : j;
+               return cache + (size_t)(rb + pos) * row_bytes;
+             });
+}
+
+// Workgroups per sequence: at most 4 passes each, and enough of them that a
+// small batch still spreads over the GPU.
+struct Split {
+  int n_split;
+  uint32_t per;
+  bool ok;
+};
+
+Split plan(int batch, int k_max, size_t row_bytes) {
+  const uint64_t cpr = row_bytes / 16;
+  const uint64_t chunks = (uint64_t)k_max * cpr;            // largest flat space of a sequence
+  if (chunks >= (1u << 24)) return {0, 0, false};
+  uint64_t n_split = (chunks + 4 * kPass - 1) / (4 * kPass);
+  const uint64_t want = (2048 + batch - 1) / batch;          // aim at >= 2048 workgroups
+  const uint64_t most = (chunks + kThreads - 1) / kThreads;  // but >= one chunk per thread each
+  n_split = n_split > (want < most ? want : most) ? n_split : (want < most ? want : most);
+  if (n_split < 1) n_split = 1;
+  const uint64_t per = (chunks + n_split - 1) / n_split;
+  if ((uint64_t)batch * n_split > 0x7fffffffu) return {0, 0, false};
+  return {(int)n_split, (uint32_t)per, true};
 }
 
 }  // namespace
@@ -92,10 +168,11 @@ extern "C" int bte_kv_scatter(const void* new_k, const void* new_v, const int32_
   if (row_bytes % 16 != 0 || !aligned16(new_k) || !aligned16(cache_k)) return BTE_ERR_ALIGN;
   if (new_v && (!aligned16(new_v) || !aligned16(cache_v))) return BTE_ERR_ALIGN;
   if (k_max == 0) return BTE_OK;
-  const size_t grid = (size_t)batch * (size_t)k_max;
-  if (grid > 0x7fffffffu) return BTE_ERR_DIM;
-  hipLaunchKernelGGL(scatter_rows_kernel, dim3((unsigned)grid, new_v ? 2 : 1), dim3(kThreads), 0,
-                     stream, (const char*)new_k, (const char*)new_v, idx, count, cu, pos_map, n,
-                     row_base, (char*)cache_k, (char*)cache_v, k_max, row_bytes);
+  const Split sp = plan(batch, k_max, row_bytes);
+  if (!sp.ok) return BTE_ERR_DIM;
+  hipLaunchKernelGGL(scatter_rows_kernel, dim3((unsigned)(batch * sp.n_split), new_v ? 2 : 1),
+                     dim3(kThreads), 0, stream, (const char*)new_k, (const char*)new_v, idx, count,
+                     cu, pos_map, n, row_base, (char*)cache_k, (char*)cache_v, k_max, row_bytes,
+                     sp.n_split, sp.per, 1.0f / (float)(row_bytes / 16));
   return hipGetLastError() == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
 }
