@@ -18,6 +18,11 @@ operations of the path, written from the pages' definitions:
   block KV (FOCUS paper Section 2, Section 4.2; App. E.2.4).
 * ``attention_order`` — the longest-first work order the GPU attention is
   scheduled by (a scheduling helper, not part of the method).
+* ``focus_budget``, ``history_update`` — FOCUS dynamic budget K and its
+  per-sequence history (FOCUS notes page, key design 2; FOCUS paper
+  Section 4.1, App. E.3.1).
+* ``focus_select`` — top-K plus FOCUS's structural constraints (AR-context,
+  placeholder integrity, |S| >= 1; FOCUS paper Section 4.2, App. E.2.2).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package. The product path
@@ -30,11 +35,13 @@ closed forms, hand-worked examples, library routines and invariants.
 from .focus import (block_scores, maxpool_keys, softmax_keys, importance,
                     focus_importance_delta)
 from .esdllm import esdllm_score
-from .selection import topk_select
+from .selection import topk_select, focus_select
+from .budget import focus_budget, history_update
 from .rows import gather_rows, kv_scatter
 from .attention import reduced_attention
 from .schedule import attention_order
 
 __all__ = ["block_scores", "maxpool_keys", "softmax_keys", "importance",
            "focus_importance_delta", "esdllm_score", "topk_select", "gather_rows",
-           "kv_scatter", "reduced_attention", "attention_order"]
+           "kv_scatter", "reduced_attention", "attention_order", "focus_budget",
+           "history_update", "focus_select"]

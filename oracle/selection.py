@@ -37,3 +37,60 @@ def topk_select(scores, k, k_max: int):
     cu = np.zeros(batch + 1, dtype=np.int32)
     cu[1:] = np.cumsum(count)
     return idx, count, cu
+
+
+def focus_select(delta, k, decoded, rightmost_processed):
+    """The kept index set S of FOCUS token eviction, per sequence.
+
+    Followed: FOCUS paper Section 4.2 (top-K masked tokens by delta, then two
+    structural constraints: AR-context preservation keeps each candidate's
+    immediate predecessor; placeholder integrity keeps the unprocessed masked
+    tokens preceding any selected candidate); App. E.2.2 (the same
+    constraints in one kernel, placeholder integrity as retaining tokens up
+    to the maximum selected index, and |S| >= 1); App. E.3.1
+    (rightmost_processed = max(previous, the position processed now)); FOCUS
+    notes page, key design 3.
+
+    Readings: candidates are the top-K of the eligible (not decoded, not NaN,
+    not -inf) positions in the top-K order of ``topk_select``; the
+    predecessor i-1 of every candidate i >= 1 is kept whatever its state;
+    placeholders are the masked positions j with rightmost_processed < j <
+    max(candidates); if S is still empty, it holds the single first position
+    of the order (score descending, index ascending) over all positions,
+    with -inf ranked above NaN; the new rightmost_processed is
+    max(old, max(S)).
+
+    delta [batch, B] float; k [batch] int; decoded [batch, B] bool;
+    rightmost_processed [batch] int -> (idx [batch, B] int32 ascending,
+    -1 padded; count [batch]; cu [batch + 1]; new rightmost_processed).
+    """
+    delta = np.asarray(delta)
+    dec = np.asarray(decoded).astype(bool)
+    batch, block = delta.shape
+    idx = np.full((batch, block), -1, dtype=np.int32)
+    count = np.zeros(batch, dtype=np.int32)
+    rp_new = np.asarray(rightmost_processed, dtype=np.int32).copy()
+    for b in range(batch):
+        row = [float(x) for x in delta[b]]
+        elig = [j for j in range(block)
+                if not dec[b, j] and not math.isnan(row[j]) and row[j] > -math.inf]
+        ranked = sorted(elig, key=lambda j: (-row[j], j))
+        keff = min(max(int(k[b]), 0), len(ranked))
+        cand = ranked[:keff]
+        s = set(cand)
+        s.update(i - 1 for i in cand if i >= 1)
+        if cand:
+            rp = int(rightmost_processed[b])
+            s.update(j for j in range(rp + 1, max(cand)) if not dec[b, j])
+        if not s:
+            def rank_key(j):
+                x = row[j]
+                return (1, j) if math.isnan(x) else (0, -x, j)
+            s = {min(range(block), key=rank_key)}
+        chosen = sorted(s)
+        idx[b, :len(chosen)] = chosen
+        count[b] = len(chosen)
+        rp_new[b] = max(int(rightmost_processed[b]), chosen[-1])
+    cu = np.zeros(batch + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(count)
+    return idx, count, cu, rp_new
