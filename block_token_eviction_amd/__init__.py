@@ -19,7 +19,8 @@ import torch
 
 __all__ = ["lib", "LIB_PATH", "BteError", "status_string", "focus_importance_delta",
            "esdllm_score", "topk_select", "gather_rows", "kv_scatter", "reduced_attention",
-           "attention_order", "BTE_F32", "BTE_BF16"]
+           "attention_order", "focus_budget", "focus_history_update", "focus_select",
+           "BTE_F32", "BTE_BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbte.so")
 BTE_F32, BTE_BF16 = 0, 1
@@ -40,6 +41,9 @@ _SIG = {
     "bte_kv_scatter": ([_p, _p, _p, _p, _p, _p, _i, _p, _p, _p, _i, _i, _sz, _p], _i),
     "bte_reduced_attention": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p], _i),
     "bte_attention_order": ([_p, _i, _p, _p], _i),
+    "bte_focus_budget": ([_p, _p, _p, _f, _i, _p, _i, _i, _p], _i),
+    "bte_focus_history_update": ([_p, _p, _p, _p, _i, _i, _p], _i),
+    "bte_focus_select": ([_p, _p, _p, _p, _p, _p, _p, _i, _i, _p], _i),
 }
 for _name, (_args, _res) in _SIG.items():
     _fn = getattr(lib, _name)
@@ -216,3 +220,57 @@ def attention_order(kv_len, out=None):
     _want(out, torch.int32, "out")
     _check("bte_attention_order", lib.bte_attention_order(_ptr(kv_len), batch, _ptr(out), _stream()))
     return out
+
+
+def focus_budget(delta, token_sum, total_steps, alpha: float, threshold_mode: int = 0, out=None):
+    """delta f32 [batch, B], token_sum/total_steps int32 [batch] -> K int32 [batch]."""
+    _dev(delta, token_sum, total_steps, out)
+    _want(delta, torch.float32, "delta")
+    _want(token_sum, torch.int32, "token_sum")
+    _want(total_steps, torch.int32, "total_steps")
+    batch, block = delta.shape
+    assert token_sum.shape == (batch,) and total_steps.shape == (batch,)
+    if out is None:
+        out = torch.empty((batch,), dtype=torch.int32, device=delta.device)
+    _want(out, torch.int32, "out")
+    _check("bte_focus_budget", lib.bte_focus_budget(
+        _ptr(delta), _ptr(token_sum), _ptr(total_steps), float(alpha), int(threshold_mode),
+        _ptr(out), batch, block, _stream()))
+    return out
+
+
+def focus_history_update(decoded_prev, decoded_now, token_sum, total_steps):
+    """In place: token_sum += newly decoded positions, total_steps += 1."""
+    _dev(decoded_prev, decoded_now, token_sum, total_steps)
+    _want(decoded_prev, torch.uint8, "decoded_prev")
+    _want(decoded_now, torch.uint8, "decoded_now")
+    _want(token_sum, torch.int32, "token_sum")
+    _want(total_steps, torch.int32, "total_steps")
+    batch, block = decoded_now.shape
+    assert decoded_prev.shape == (batch, block)
+    _check("bte_focus_history_update", lib.bte_focus_history_update(
+        _ptr(decoded_prev), _ptr(decoded_now), _ptr(token_sum), _ptr(total_steps), batch, block,
+        _stream()))
+    return token_sum, total_steps
+
+
+def focus_select(delta, k, decoded, rightmost_processed, idx=None, count=None, cu=None):
+    """Top-K + AR-context + placeholder integrity + |S| >= 1.
+    -> (idx int32 [batch, B], count [batch], cu [batch + 1]); rightmost_processed updated in place."""
+    _dev(delta, k, decoded, rightmost_processed, idx, count, cu)
+    _want(delta, torch.float32, "delta")
+    _want(k, torch.int32, "k")
+    _want(decoded, torch.uint8, "decoded")
+    _want(rightmost_processed, torch.int32, "rightmost_processed")
+    batch, block = delta.shape
+    dev = delta.device
+    if idx is None:
+        idx = torch.empty((batch, block), dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty((batch,), dtype=torch.int32, device=dev)
+    if cu is None:
+        cu = torch.empty((batch + 1,), dtype=torch.int32, device=dev)
+    _check("bte_focus_select", lib.bte_focus_select(
+        _ptr(delta), _ptr(k), _ptr(decoded), _ptr(rightmost_processed), _ptr(idx), _ptr(count),
+        _ptr(cu), batch, block, _stream()))
+    return idx, count, cu

@@ -16,6 +16,8 @@
 // A second single-workgroup kernel turns the per-row counts into the
 // exclusive prefix sum cu[]; both run on the caller's stream, with no host
 // synchronisation.
+#include <math.h>
+
 #include "bte_device.h"
 
 namespace bte {
@@ -109,6 +111,155 @@ __global__ __launch_bounds__(1024) void exclusive_scan_kernel(const int32_t* __r
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// FOCUS dynamic budget (FOCUS notes page, key design 2; FOCUS paper Section
+// 4.1 and App. E.3.2):  K = min(B, max(ceil(alpha * N_bar), N_sigma)).
+// One thread per sequence; the integer-deciding arithmetic is float64 with a
+// fixed ascending summation order and no contraction, so the result is the
+// same on every run and matches a plain float64 evaluation of the same steps.
+// N_sigma counts masked positions (finite delta) with delta >= sigma (mode 0:
+// tested exactly as delta >= 0 and delta^2 >= variance) or delta > mu + sigma
+// (mode 1, App. E.2.2: d = delta - mu > 0 and d^2 > variance); mu and the
+// variance are the population ones over the masked positions.
+__global__ __launch_bounds__(256) void focus_budget_kernel(
+    const float* __restrict__ delta, const int32_t* __restrict__ token_sum,
+    const int32_t* __restrict__ total_steps, double alpha, int mode, int32_t* __restrict__ k_out,
+    int batch, int B) {
+#pragma clang fp contract(off)
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= batch) return;
+  const float* row = delta + (size_t)b * B;
+  int n = 0;
+  double total = 0.0;
+  for (int j = 0; j < B; ++j) {
+    const float x = row[j];
+    if (isfinite(x)) {
+      total += (double)x;
+      ++n;
+    }
+  }
+  int nsig = 0;
+  if (n > 0) {
+    const double mu = total / (double)n;
+    double ss = 0.0;
+    for (int j = 0; j < B; ++j) {
+      const float x = row[j];
+      if (isfinite(x)) {
+        const double d = (double)x - mu;
+        ss += d * d;
+      }
+    }
+    const double var = ss / (double)n;
+    for (int j = 0; j < B; ++j) {
+      const float x = row[j];
+      if (!isfinite(x)) continue;
+      if (mode == 0) {
+        const double xd = (double)x;
+        nsig += (xd >= 0.0 && xd * xd >= var) ? 1 : 0;
+      } else {
+        const double d = (double)x - mu;
+        nsig += (d > 0.0 && d * d > var) ? 1 : 0;
+      }
+    }
+  }
+  const int steps = total_steps[b];
+  const double nbar = steps > 0 ? (double)token_sum[b] / (double)steps : 1.0;
+  const double kh = ceil(alpha * nbar);
+  const int khist = kh >= (double)B ? B : (kh <= 0.0 ? 0 : (int)kh);
+  const int k = khist > nsig ? khist : nsig;
+  k_out[b] = k < B ? k : B;
+}
+
+// Per-sequence decoding history (FOCUS paper App. E.3.1): positions decoded
+// now but not before are added to token_sum; total_steps advances by one.
+__global__ __launch_bounds__(256) void history_update_kernel(
+    const uint8_t* __restrict__ prev, const uint8_t* __restrict__ now,
+    int32_t* __restrict__ token_sum, int32_t* __restrict__ total_steps, int batch, int B) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= batch) return;
+  int n = 0;
+  for (int j = 0; j < B; ++j) n += (now[(size_t)b * B + j] && !prev[(size_t)b * B + j]) ? 1 : 0;
+  token_sum[b] += n;
+  total_steps[b] += 1;
+}
+
+// FOCUS token eviction with its structural constraints in one pass (FOCUS
+// paper Section 4.2 and App. E.2.2). One wave per sequence, lane j = block
+// position (B <= 64):
+//   candidates: the top-K eligible positions (not decoded, finite delta), in
+//     the top-K order above (exact rank, ties to the lower index);
+//   AR context: the predecessor i-1 of every candidate i;
+//   placeholder integrity: every masked position j with
+//     rightmost_processed < j < max(candidates);
+//   |S| >= 1: an empty set takes the first position of the order over all
+//     positions (-inf above NaN).
+// Writes S ascending (-1 padded to B), |S|, and rightmost_processed =
+// max(previous, max(S)) (App. E.3.1).
+__global__ __launch_bounds__(256) void focus_select_kernel(
+    const float* __restrict__ delta, const int32_t* __restrict__ kbud,
+    const uint8_t* __restrict__ decoded, int32_t* __restrict__ rightmost,
+    int32_t* __restrict__ idx_out, int32_t* __restrict__ count_out, int batch, int B) {
+  __shared__ uint32_t keys[4][kWave];
+  const int slot = threadIdx.x / kWave;
+  const int j = threadIdx.x % kWave;
+  const int b = blockIdx.x * 4 + slot;
+  const bool row_ok = b < batch;
+  const bool pos_ok = row_ok && j < B;
+  const float x = pos_ok ? delta[(size_t)b * B + j] : __builtin_nanf("");
+  const bool dec = pos_ok ? decoded[(size_t)b * B + j] != 0 : true;
+  const uint32_t key = (pos_ok && !dec) ? order_key(x) : 0u;
+  keys[slot][j] = key;
+  __syncthreads();
+  if (!row_ok) return;
+
+  const int n_elig = __popcll(__ballot(key != 0u));
+  int keff = kbud[b];
+  keff = keff < 0 ? 0 : (keff < n_elig ? keff : n_elig);
+  int rank = 0;
+  for (int i = 0; i < B; ++i) {
+    const uint32_t o = keys[slot][i];
+    rank += (o > key) | ((o == key) & (i < j));
+  }
+  const bool cand = key != 0u && rank < keff;
+  const uint64_t cm = __ballot(cand);
+  const int maxc = cm ? 63 - __clzll(cm) : -1;
+  const int rp = rightmost[b];
+  const bool pred = j + 1 < B && ((cm >> (j + 1)) & 1ull);
+  const bool hold = pos_ok && !dec && j > rp && j < maxc;
+  bool in_s = pos_ok && (cand || pred || hold);
+  uint64_t sm = __ballot(in_s);
+  if (sm == 0) {
+    // First position of the order over all positions: largest order key with
+    // -inf included and NaN lowest, ties to the lower index.
+    uint32_t k2 = 0u;
+    if (pos_ok && !(x != x)) {
+      uint32_t u = __float_as_uint(x);
+      if ((u << 1) == 0u) u = 0u;
+      k2 = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    }
+    uint64_t best = pos_ok ? (((uint64_t)k2 << 32) | (uint32_t)(kWave - 1 - j)) : 0ull;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const uint64_t o = __shfl_xor(best, d, kWave);
+      best = o > best ? o : best;
+    }
+    in_s = pos_ok && j == kWave - 1 - (int)(uint32_t)best;
+    sm = __ballot(in_s);
+  }
+  const int cnt = __popcll(sm);
+  const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(sm >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)sm, 0u));
+  int32_t* row = idx_out + (size_t)b * B;
+  if (in_s) row[pos] = j;
+  for (int t = cnt + j; t < B; t += kWave) row[t] = -1;
+  if (j == 0) {
+    count_out[b] = cnt;
+    const int top = 63 - __clzll(sm);
+    rightmost[b] = rp > top ? rp : top;
+  }
+}
+
 }  // namespace
 }  // namespace bte
 
@@ -129,6 +280,45 @@ extern "C" int bte_topk_select(const float* scores, const int32_t* k, int32_t* i
     hipLaunchKernelGGL(topk_kernel<1024>, dim3(batch), dim3(1024), 0, stream, scores, k, idx,
                        count_out, batch, n, k_max);
   }
+  if (hipGetLastError() != hipSuccess) return BTE_ERR_LAUNCH;
+  hipLaunchKernelGGL(exclusive_scan_kernel, dim3(1), dim3(1024), 0, stream, count_out, cu_out, batch);
+  return hipGetLastError() == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
+}
+
+extern "C" int bte_focus_budget(const float* delta, const int32_t* token_sum,
+                                const int32_t* total_steps, float alpha, int threshold_mode,
+                                int32_t* k_out, int batch, int block, hipStream_t stream) {
+  using namespace bte;
+  if (!delta || !token_sum || !total_steps || !k_out) return BTE_ERR_NULL;
+  if (batch <= 0 || block < 1 || block > 1024) return BTE_ERR_DIM;
+  if (!(alpha >= 0.f) || !isfinite(alpha) || (threshold_mode != 0 && threshold_mode != 1))
+    return BTE_ERR_DIM;
+  hipLaunchKernelGGL(focus_budget_kernel, dim3((batch + 255) / 256), dim3(256), 0, stream, delta,
+                     token_sum, total_steps, (double)alpha, threshold_mode, k_out, batch, block);
+  return hipGetLastError() == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
+}
+
+extern "C" int bte_focus_history_update(const uint8_t* decoded_prev, const uint8_t* decoded_now,
+                                        int32_t* token_sum, int32_t* total_steps, int batch,
+                                        int block, hipStream_t stream) {
+  using namespace bte;
+  if (!decoded_prev || !decoded_now || !token_sum || !total_steps) return BTE_ERR_NULL;
+  if (batch <= 0 || block < 1 || block > 1024) return BTE_ERR_DIM;
+  hipLaunchKernelGGL(history_update_kernel, dim3((batch + 255) / 256), dim3(256), 0, stream,
+                     decoded_prev, decoded_now, token_sum, total_steps, batch, block);
+  return hipGetLastError() == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
+}
+
+extern "C" int bte_focus_select(const float* delta, const int32_t* k, const uint8_t* decoded,
+                                int32_t* rightmost_processed, int32_t* idx_out, int32_t* count_out,
+                                int32_t* cu_out, int batch, int block, hipStream_t stream) {
+  using namespace bte;
+  if (!delta || !k || !decoded || !rightmost_processed || !idx_out || !count_out || !cu_out)
+    return BTE_ERR_NULL;
+  if (batch <= 0 || block < 1) return BTE_ERR_DIM;
+  if (block > kWave) return BTE_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(focus_select_kernel, dim3((batch + 3) / 4), dim3(256), 0, stream, delta, k,
+                     decoded, rightmost_processed, idx_out, count_out, batch, block);
   if (hipGetLastError() != hipSuccess) return BTE_ERR_LAUNCH;
   hipLaunchKernelGGL(exclusive_scan_kernel, dim3(1), dim3(1024), 0, stream, count_out, cu_out, batch);
   return hipGetLastError() == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;

@@ -117,6 +117,71 @@ int bte_topk_select(const float* scores, const int32_t* k, int32_t* idx_out, int
                     int32_t* cu_out, int batch, int n, int k_max, hipStream_t stream);
 
 /*
+ * FOCUS dynamic budget (FOCUS notes page, key design 2, and its worked
+ * example; FOCUS paper Section 4.1, App. E.3.2):
+ *   k_out[b] = min(block, max(ceil(alpha * N_bar), N_sigma))
+ * with N_bar = token_sum[b] / total_steps[b] (1 when total_steps[b] == 0)
+ * and N_sigma the number of masked positions (finite delta; decoded ones
+ * carry -INFINITY) whose delta passes the threshold: threshold_mode 0 ->
+ * delta >= sigma (the notes page's budget and App. D), threshold_mode 1 ->
+ * delta > mu + sigma (App. E.2.2's selection kernel). mu and sigma are the
+ * population mean and standard deviation over the block's masked positions.
+ * The integer-deciding arithmetic is float64 in a fixed order (ascending
+ * position, no contraction) and "delta >= sigma" is tested exactly as
+ * delta >= 0 and delta^2 >= variance, so results are reproducible bit for
+ * bit.
+ *
+ *   delta [batch, block] float32 (as written by bte_focus_importance_delta)
+ *   token_sum, total_steps [batch] int32; k_out [batch] int32
+ * Limits: 1 <= block <= 1024; alpha >= 0 and finite (the pages use alpha > 1).
+ * Errors: NULL -> BTE_ERR_NULL; sizes, alpha or threshold_mode out of range
+ * -> BTE_ERR_DIM.
+ */
+int bte_focus_budget(const float* delta, const int32_t* token_sum, const int32_t* total_steps,
+                     float alpha, int threshold_mode, int32_t* k_out, int batch, int block,
+                     hipStream_t stream);
+
+/*
+ * Per-sequence decoding history update (FOCUS paper App. E.3.1; the
+ * in-loop state update of App. E.3.4): token_sum[b] += number of positions
+ * decoded in decoded_now but not in decoded_prev; total_steps[b] += 1.
+ *
+ *   decoded_prev, decoded_now [batch, block] uint8 (nonzero = decoded)
+ *   token_sum, total_steps [batch] int32, updated in place
+ * Errors: NULL -> BTE_ERR_NULL; batch <= 0 or block out of [1, 1024] ->
+ * BTE_ERR_DIM.
+ */
+int bte_focus_history_update(const uint8_t* decoded_prev, const uint8_t* decoded_now,
+                             int32_t* token_sum, int32_t* total_steps, int batch, int block,
+                             hipStream_t stream);
+
+/*
+ * FOCUS token eviction with its structural constraints (FOCUS paper Section
+ * 4.2 and App. E.2.2; FOCUS notes page, key design 3). Per sequence:
+ *   C = the top-k[b] eligible positions (not decoded, delta neither NaN nor
+ *       -INFINITY), ranked as in bte_topk_select;
+ *   S = C + {i - 1 : i in C, i >= 1}                   (AR-context)
+ *         + {j masked : rightmost_processed[b] < j < max(C)}
+ *                                                      (placeholder integrity)
+ *   if S is empty: S = {the first position of that ranking over all
+ *       positions, -INFINITY above NaN}                 (|S| >= 1)
+ *   rightmost_processed[b] = max(rightmost_processed[b], max(S))
+ * idx_out[b] holds S ascending, padded with -1 to `block`; count_out[b] =
+ * |S|; cu_out is the exclusive prefix sum of the counts.
+ *
+ *   delta [batch, block] float32; k [batch] int32; decoded [batch, block]
+ *   uint8; rightmost_processed [batch] int32 (in/out, -1 at a block's
+ *   start); idx_out [batch, block], count_out [batch], cu_out [batch + 1]
+ *   int32
+ * Limits: 1 <= block <= 64.
+ * Errors: NULL -> BTE_ERR_NULL; batch <= 0 or block < 1 -> BTE_ERR_DIM;
+ * block > 64 -> BTE_ERR_UNSUPPORTED.
+ */
+int bte_focus_select(const float* delta, const int32_t* k, const uint8_t* decoded,
+                     int32_t* rightmost_processed, int32_t* idx_out, int32_t* count_out,
+                     int32_t* cu_out, int batch, int block, hipStream_t stream);
+
+/*
  * Gather-compaction of kept rows (FOCUS paper Section 4.2: H_reduced = H at
  * the kept index set; App. E.2.3: destinations from a prefix sum):
  *   dst[cu[b] + t, :] = src[b, idx[b,t], :]   for t < count[b]

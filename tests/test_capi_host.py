@@ -25,7 +25,7 @@ def declared():
 
 def test_every_declared_symbol_is_exported():
     names = declared()
-    assert len(names) == 9
+    assert len(names) == 12
     for name in names:
         assert hasattr(lib, name), name
 
@@ -126,3 +126,20 @@ def test_attention_order_errors():
     assert f(FAKE, 4, None, None) == NULL
     assert f(FAKE, 0, FAKE, None) == DIM
     assert f(FAKE, 16385, FAKE, None) == DIM
+
+
+def test_budget_select_errors():
+    f = lib.bte_focus_budget
+    assert f(None, FAKE, FAKE, 1.5, 0, FAKE, 4, 32, None) == NULL
+    assert f(FAKE, FAKE, FAKE, 1.5, 0, FAKE, 0, 32, None) == DIM
+    assert f(FAKE, FAKE, FAKE, 1.5, 0, FAKE, 4, 0, None) == DIM
+    assert f(FAKE, FAKE, FAKE, -1.0, 0, FAKE, 4, 32, None) == DIM
+    assert f(FAKE, FAKE, FAKE, float("nan"), 0, FAKE, 4, 32, None) == DIM
+    assert f(FAKE, FAKE, FAKE, 1.5, 2, FAKE, 4, 32, None) == DIM
+    h = lib.bte_focus_history_update
+    assert h(FAKE, None, FAKE, FAKE, 4, 32, None) == NULL
+    assert h(FAKE, FAKE, FAKE, FAKE, 4, 0, None) == DIM
+    s = lib.bte_focus_select
+    assert s(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 4, 32, None) == NULL
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 32, None) == DIM
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 65, None) == UNSUP
