@@ -23,6 +23,8 @@ operations of the path, written from the pages' definitions:
   Section 4.1, App. E.3.1).
 * ``focus_select`` — top-K plus FOCUS's structural constraints (AR-context,
   placeholder integrity, |S| >= 1; FOCUS paper Section 4.2, App. E.2.2).
+* ``kv_scatter_paged``, ``reduced_attention_paged`` — the same scatter and
+  attention on a paged KV pool through a page table (FOCUS paper App. E.2.4).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package. The product path
@@ -40,8 +42,10 @@ from .budget import focus_budget, history_update
 from .rows import gather_rows, kv_scatter
 from .attention import reduced_attention
 from .schedule import attention_order
+from .paged import kv_scatter_paged, reduced_attention_paged, physical_row
 
 __all__ = ["block_scores", "maxpool_keys", "softmax_keys", "importance",
            "focus_importance_delta", "esdllm_score", "topk_select", "gather_rows",
            "kv_scatter", "reduced_attention", "attention_order", "focus_budget",
-           "history_update", "focus_select"]
+           "history_update", "focus_select", "kv_scatter_paged", "reduced_attention_paged",
+           "physical_row"]

@@ -136,3 +136,54 @@ def test_attention_order_invariants():
     assert np.all(d[:-1] >= d[1:])
     tie = d[:-1] == d[1:]
     assert np.all(o[:-1][tie] < o[1:][tie])
+
+
+def _paged_layout(r, kv_len, page_size, extra_pages=3):
+    """A random page table over a pool with spare pages, and the pool filled so
+    that every sequence reads the contiguous rows it stands for."""
+    need = [(int(L) + page_size - 1) // page_size for L in kv_len]
+    max_pages = max(need)
+    n_pages = sum(need) + extra_pages
+    perm = r.permutation(n_pages)
+    bt = np.full((len(kv_len), max_pages), -1, np.int32)
+    at = 0
+    for b, n in enumerate(need):
+        bt[b, :n] = perm[at:at + n]
+        at += n
+    return bt, n_pages
+
+
+def test_paged_attention_equals_contiguous():
+    """Through a shuffled page table, paged attention is the contiguous one
+    bit for bit (same rows, same order, same float64 steps)."""
+    hq, hkv, D = 8, 2, 16
+    q, count, cu, ck, cv, ss, L = _attn_case(9, hq=hq, hkv=hkv, D=D)
+    r = np.random.default_rng(10)
+    for P in (1, 2, 4, 16):
+        bt, n_pages = _paged_layout(r, L, P)
+        pk = r.standard_normal((n_pages * P, hkv, D))      # garbage in unused rows
+        pv = r.standard_normal((n_pages * P, hkv, D))
+        for b in range(len(L)):
+            for p in range(int(L[b])):
+                row = oracle.physical_row(bt, b, p, P)
+                pk[row], pv[row] = ck[ss[b] + p], cv[ss[b] + p]
+        want = oracle.reduced_attention(q, count, cu, ck, cv, ss, L, hq, hkv, 0.25)
+        got = oracle.reduced_attention_paged(q, count, cu, pk, pv, bt, P, L, hq, hkv, 0.25)
+        np.testing.assert_array_equal(got, want)
+
+
+def test_paged_scatter_hand_example():
+    # page size 2, sequence 0 owns pages [3, 0], sequence 1 owns page [1]; pool of 4 pages
+    bt = np.array([[3, 0], [1, -1]], np.int32)
+    cache = np.arange(8 * 2, dtype=np.int32).reshape(8, 2)
+    new = np.array([[100, 101], [102, 103], [104, 105]], np.int32)
+    idx = np.array([[0, 2], [1, -1]], np.int32)
+    count = np.array([2, 1], np.int32)
+    cu = np.array([0, 2, 3], np.int32)
+    pos_base = np.array([1, 0], np.int32)
+    # seq 0: logical 1 -> page 3 row 1 = 7; logical 3 -> page 0 row 1 = 1
+    # seq 1: logical 1 -> page 1 row 1 = 3
+    k2, _ = oracle.kv_scatter_paged(new, new, idx, count, cu, pos_base, bt, 2, cache, cache)
+    want = cache.copy()
+    want[7], want[1], want[3] = new[0], new[1], new[2]
+    np.testing.assert_array_equal(k2, want)
