@@ -19,7 +19,8 @@ import torch
 
 __all__ = ["lib", "LIB_PATH", "BteError", "status_string", "focus_importance_delta",
            "esdllm_score", "topk_select", "gather_rows", "kv_scatter", "reduced_attention",
-           "attention_order", "focus_budget", "focus_history_update", "focus_select",
+           "attention_order", "reduced_attention_paged", "kv_scatter_paged", "focus_budget",
+           "focus_history_update", "focus_select",
            "BTE_F32", "BTE_BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbte.so")
@@ -41,6 +42,10 @@ _SIG = {
     "bte_kv_scatter": ([_p, _p, _p, _p, _p, _p, _i, _p, _p, _p, _i, _i, _sz, _p], _i),
     "bte_reduced_attention": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p], _i),
     "bte_attention_order": ([_p, _i, _p, _p], _i),
+    "bte_reduced_attention_paged": ([_p, _p, _p, _p, _p, _p, _i, _i, _p, _p, _p, _i, _i, _i, _i, _i,
+                                     _f, _i, _p], _i),
+    "bte_kv_scatter_paged": ([_p, _p, _p, _p, _p, _p, _i, _p, _p, _i, _i, _p, _p, _i, _i, _sz, _p],
+                             _i),
     "bte_focus_budget": ([_p, _p, _p, _f, _i, _p, _i, _i, _p], _i),
     "bte_focus_history_update": ([_p, _p, _p, _p, _i, _i, _p], _i),
     "bte_focus_select": ([_p, _p, _p, _p, _p, _p, _p, _i, _i, _p], _i),
@@ -274,3 +279,45 @@ def focus_select(delta, k, decoded, rightmost_processed, idx=None, count=None, c
         _ptr(delta), _ptr(k), _ptr(decoded), _ptr(rightmost_processed), _ptr(idx), _ptr(count),
         _ptr(cu), batch, block, _stream()))
     return idx, count, cu
+
+
+def reduced_attention_paged(q, count, cu, cache_k, cache_v, block_table, page_size: int, kv_len,
+                            k_max: int, scale: float | None = None, out=None, order=None):
+    """q [capacity, hq, D]; page pool cache [n_pages * page_size, hkv, D];
+    block_table int32 [batch, max_pages] -> out [capacity, hq, D]."""
+    _dev(q, count, cu, cache_k, cache_v, block_table, kv_len, out, order)
+    _want(block_table, torch.int32, "block_table")
+    _want(kv_len, torch.int32, "kv_len")
+    hq, d = q.shape[1], q.shape[2]
+    hkv = cache_k.shape[1]
+    batch = count.shape[0]
+    assert cache_v.shape == cache_k.shape and cache_k.dtype == q.dtype
+    assert block_table.shape[0] == batch
+    if order is not None:
+        _want(order, torch.int32, "order")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _check("bte_reduced_attention_paged", lib.bte_reduced_attention_paged(
+        _ptr(q), _ptr(count), _ptr(cu), _ptr(cache_k), _ptr(cache_v), _ptr(block_table),
+        block_table.shape[1], page_size, _ptr(kv_len), _ptr(order), _ptr(out), batch, k_max, hq,
+        hkv, d, float(scale), _dtype(q), _stream()))
+    return out
+
+
+def kv_scatter_paged(new_k, new_v, idx, count, cu, pos_base, block_table, page_size: int,
+                     cache_k, cache_v, pos_map=None):
+    """Write new_k/new_v rows cu[b]+t to the pool rows of logical positions pos_base[b] + pos."""
+    _dev(new_k, new_v, idx, count, cu, pos_base, block_table, cache_k, cache_v, pos_map)
+    _want(pos_base, torch.int32, "pos_base")
+    _want(block_table, torch.int32, "block_table")
+    batch, k_max = idx.shape
+    row_bytes = cache_k[0].numel() * cache_k.element_size()
+    assert new_k[0].numel() * new_k.element_size() == row_bytes
+    n = 0 if pos_map is None else pos_map.shape[1]
+    _check("bte_kv_scatter_paged", lib.bte_kv_scatter_paged(
+        _ptr(new_k), _ptr(new_v), _ptr(idx), _ptr(count), _ptr(cu), _ptr(pos_map), n,
+        _ptr(pos_base), _ptr(block_table), block_table.shape[1], page_size, _ptr(cache_k),
+        _ptr(cache_v), batch, k_max, row_bytes, _stream()))
+    return cache_k, cache_v

@@ -108,13 +108,33 @@ __device__ __forceinline__ void copy16_to_lds(const char* src, char* lds_dst) {
                                    kStreamPolicy);
 }
 
+// Where sequence b's KV rows are: contiguous from seq_start[b], or (kPaged)
+// logical position p in row block_table[b][p >> lg_page] * page + p % page of
+// a page pool.
+struct KvMap {
+  const int64_t* seq_start;
+  const int32_t* block_table;
+  int max_pages;
+  int lg_page;
+};
+
+// KV layouts: contiguous; paged with the sequence's page-table row staged in
+// LDS at workgroup start (a page lookup is then an LDS read); paged with
+// lookups from memory, for tables longer than the LDS copy. A lookup from
+// memory in front of a copy needs an s_waitcnt vmcnt(0) to use its value,
+// which also waits for every copy in flight: that variant is correct but
+// serialises the pipeline, so it is a separate kernel and the host picks it
+// only when a table has more than kPageCache entries.
+enum { kContig = 0, kPagedLds = 1, kPagedMem = 2 };
+constexpr int kPageCache = 2048;
+
 // One workgroup's work: sequence b, KV head g, the T 32-row query tiles from
 // row0 on (each holding at least one real row).
-template <int D, bool BF16, int T, int kWaves>
+template <int D, bool BF16, int T, int kWaves, int kPaged>
 __device__ __forceinline__ void attn_body(
-    char* __restrict__ smem, const char* __restrict__ q, const int32_t* __restrict__ cu,
-    const char* __restrict__ cache_k, const char* __restrict__ cache_v,
-    const int64_t* __restrict__ seq_start, const int32_t* __restrict__ kv_len,
+    char* __restrict__ smem, const int32_t* __restrict__ pages, const char* __restrict__ q,
+    const int32_t* __restrict__ cu, const char* __restrict__ cache_k,
+    const char* __restrict__ cache_v, const KvMap& map, const int32_t* __restrict__ kv_len,
     char* __restrict__ out, int hq, int hkv, float c, int b, int g, int rows, int row0) {
   using C = Cfg<D, BF16, kWaves>;
   constexpr int DT = D / 32;                           // 32-wide output column tiles
@@ -124,11 +144,22 @@ __device__ __forceinline__ void attn_body(
   const int n = lane & 31;
   const int h = lane >> 5;
   const int L = kv_len[b];
-  const int64_t s0 = seq_start[b];
   const int cub = cu[b];
   const size_t kv_row = (size_t)hkv * C::kRowBytes;    // bytes per cache position
-  const char* kbase = cache_k + (size_t)s0 * kv_row + (size_t)g * C::kRowBytes;
-  const char* vbase = cache_v + (size_t)s0 * kv_row + (size_t)g * C::kRowBytes;
+  const size_t seq_off = kPaged != kContig ? 0 : (size_t)map.seq_start[b] * kv_row;
+  const char* kbase = cache_k + seq_off + (size_t)g * C::kRowBytes;
+  const char* vbase = cache_v + seq_off + (size_t)g * C::kRowBytes;
+  const int32_t* bt = kPaged != kContig ? map.block_table + (size_t)b * map.max_pages : nullptr;
+  // Cache row (relative to the bases) of logical KV position p.
+  auto kv_pos_row = [&](int p) -> size_t {
+    if constexpr (kPaged == kContig) {
+      return (size_t)p;
+    } else {
+      const int lg = map.lg_page;
+      const int page = kPaged == kPagedLds ? pages[p >> lg] : bt[p >> lg];
+      return ((size_t)page << lg) + (size_t)(p & ((1 << lg) - 1));
+    }
+  };
   const float thr = fminf(kShiftSlack / c, 3.0e38f);   // reference-max slack in score units
 
   // Query operands (B of S^T): lane (n, h) holds half h of query row n.
@@ -167,14 +198,16 @@ __device__ __forceinline__ void attn_body(
   const int lslot = lane % C::kChunks;
   const uint32_t lane_row_off = (uint32_t)(lrow * kv_row);
   // Copies the K (which = 0) or V (which = 1) half of key tile kt into `stage`.
+  // A full tile's copies each cover kRpi consecutive rows that share one page
+  // (pages hold a multiple of kRpi rows), so each copy has a wave-uniform base.
   auto issue_half = [&](int kt, int stage, int which) {
     char* dst = wave_lds + stage * C::kStageBytes + which * C::kTile;
-    const char* base = (which ? vbase : kbase) + (size_t)kt * 32 * kv_row;
+    const char* base = which ? vbase : kbase;
     if (kt * 32 + 32 <= L) {
 #pragma unroll
       for (int i = 0; i < C::kHalf; ++i) {
         const int row = C::kRpi * i + lrow;
-        const size_t row_base = (size_t)(C::kRpi * i) * kv_row;      // wave-uniform
+        const size_t row_base = kv_pos_row(kt * 32 + C::kRpi * i) * kv_row;   // wave-uniform
         const int chunk = which ? vpos(row, lslot) : kpos(row, lslot);
         copy16_to_lds(base + row_base + (lane_row_off + 16 * chunk), dst + 1024 * i);
       }
@@ -185,9 +218,9 @@ __device__ __forceinline__ void attn_body(
 #pragma unroll
       for (int i = 0; i < C::kHalf; ++i) {
         const int row = C::kRpi * i + lrow;
-        const uint32_t roff = (uint32_t)((row < last ? row : last) * kv_row);
+        const size_t prow = kv_pos_row(kt * 32 + (row < last ? row : last));
         const int chunk = which ? vpos(row, lslot) : kpos(row, lslot);
-        copy16_to_lds(base + roff + 16 * chunk, dst + 1024 * i);
+        copy16_to_lds(base + prow * kv_row + 16 * chunk, dst + 1024 * i);
       }
     }
   };
@@ -416,14 +449,14 @@ __device__ __forceinline__ void attn_body(
 // the given order.
 constexpr int kXcds = 8;
 
-template <int D, bool BF16, int T, int kWaves>
+template <int D, bool BF16, int T, int kWaves, int kPaged>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T == 1 ? 2 : 1))) void attn_kernel(
     const char* __restrict__ q, const int32_t* __restrict__ count, const int32_t* __restrict__ cu,
-    const char* __restrict__ cache_k, const char* __restrict__ cache_v,
-    const int64_t* __restrict__ seq_start, const int32_t* __restrict__ kv_len,
-    const int32_t* __restrict__ order, char* __restrict__ out, int batch, int hq, int hkv,
-    int n_rg, float c) {
+    const char* __restrict__ cache_k, const char* __restrict__ cache_v, KvMap map,
+    const int32_t* __restrict__ kv_len, const int32_t* __restrict__ order, char* __restrict__ out,
+    int batch, int hq, int hkv, int n_rg, float c) {
   __shared__ __attribute__((aligned(16))) char smem[Cfg<D, BF16, kWaves>::kLds];
+  __shared__ int32_t pages[kPaged == kPagedLds ? kPageCache : 1];
   const int per_seq = hkv * n_rg;                      // workgroups per sequence
   const int slot = blockIdx.x / kXcds;
   const int grp = slot / per_seq;
@@ -439,11 +472,19 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T =
   const int rows = count[b] * (hq / hkv);
   const int row0 = rg * 32 * T;
   if (row0 >= rows) return;
+  if constexpr (kPaged == kPagedLds) {
+    const int n_pages = min((kv_len[b] + (1 << map.lg_page) - 1) >> map.lg_page, map.max_pages);
+    const int32_t* bt = map.block_table + (size_t)b * map.max_pages;
+    for (int i = threadIdx.x; i < n_pages; i += 64 * kWaves) pages[i] = bt[i];
+    __syncthreads();
+  }
   // Workgroup-uniform: skip query tiles that hold no real row.
   if (T == 2 && rows - row0 > 32)
-    attn_body<D, BF16, T, kWaves>(smem, q, cu, cache_k, cache_v, seq_start, kv_len, out, hq, hkv, c, b, g, rows, row0);
+    attn_body<D, BF16, T, kWaves, kPaged>(smem, pages, q, cu, cache_k, cache_v, map, kv_len, out,
+                                          hq, hkv, c, b, g, rows, row0);
   else
-    attn_body<D, BF16, 1, kWaves>(smem, q, cu, cache_k, cache_v, seq_start, kv_len, out, hq, hkv, c, b, g, rows, row0);
+    attn_body<D, BF16, 1, kWaves, kPaged>(smem, pages, q, cu, cache_k, cache_v, map, kv_len, out,
+                                          hq, hkv, c, b, g, rows, row0);
 }
 
 struct AttnArgs {
@@ -452,7 +493,7 @@ struct AttnArgs {
   const int32_t* cu;
   const void* ck;
   const void* cv;
-  const int64_t* ss;
+  KvMap map;
   const int32_t* kl;
   const int32_t* order;
   void* out;
@@ -460,15 +501,16 @@ struct AttnArgs {
   float c;
 };
 
-template <int D, bool BF16, int T, int kWaves>
+template <int D, bool BF16, int T, int kWaves, int kPaged>
 hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   const long rows = (long)a.k_max * (a.hq / a.hkv);
   const long n_rg = (rows + 32 * T - 1) / (32 * T);
   const long grid = (long)((a.batch + kXcds - 1) / kXcds) * kXcds * a.hkv * n_rg;
   if (grid > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_kernel<D, BF16, T, kWaves>), dim3((unsigned)grid), dim3(64 * kWaves), 0,
-                     stream, (const char*)a.q, a.count, a.cu, (const char*)a.ck, (const char*)a.cv,
-                     a.ss, a.kl, a.order, (char*)a.out, a.batch, a.hq, a.hkv, (int)n_rg, a.c);
+  hipLaunchKernelGGL((attn_kernel<D, BF16, T, kWaves, kPaged>), dim3((unsigned)grid),
+                     dim3(64 * kWaves), 0, stream, (const char*)a.q, a.count, a.cu,
+                     (const char*)a.ck, (const char*)a.cv, a.map, a.kl, a.order, (char*)a.out,
+                     a.batch, a.hq, a.hkv, (int)n_rg, a.c);
   return hipGetLastError();
 }
 
@@ -482,20 +524,33 @@ inline int waves_for(long items, bool ordered) {
   return items >= 2048 ? 2 : 4;
 }
 
-template <int D>
+template <int D, int kPaged>
 hipError_t launch_bf16(const AttnArgs& a, hipStream_t stream) {
   const long rows = (long)a.k_max * (a.hq / a.hkv);
   const int T = rows > 32 ? 2 : 1;
   const long items = (long)a.batch * a.hkv * ((rows + 32 * T - 1) / (32 * T));
   const int nw = waves_for(items, a.order != nullptr);
   if (T == 2) {
-    if (nw == 1) return launch<D, true, 2, 1>(a, stream);
-    if (nw == 2) return launch<D, true, 2, 2>(a, stream);
-    return launch<D, true, 2, 4>(a, stream);
+    if (nw == 1) return launch<D, true, 2, 1, kPaged>(a, stream);
+    if (nw == 2) return launch<D, true, 2, 2, kPaged>(a, stream);
+    return launch<D, true, 2, 4, kPaged>(a, stream);
   }
-  if (nw == 1) return launch<D, true, 1, 1>(a, stream);
-  if (nw == 2) return launch<D, true, 1, 2>(a, stream);
-  return launch<D, true, 1, 4>(a, stream);
+  if (nw == 1) return launch<D, true, 1, 1, kPaged>(a, stream);
+  if (nw == 2) return launch<D, true, 1, 2, kPaged>(a, stream);
+  return launch<D, true, 1, 4, kPaged>(a, stream);
+}
+
+// Shared by the contiguous and paged entry points.
+template <int kPaged>
+int attention(const AttnArgs& a, int head_dim, bte_dtype dtype, hipStream_t stream) {
+  hipError_t e;
+  if (dtype == BTE_BF16)
+    e = head_dim == 128 ? launch_bf16<128, kPaged>(a, stream) : launch_bf16<64, kPaged>(a, stream);
+  else  // fp32 operands take twice the registers: 32 query rows per workgroup only
+    e = head_dim == 128 ? launch<128, false, 1, 4, kPaged>(a, stream)
+                        : launch<64, false, 1, 4, kPaged>(a, stream);
+  if (e == hipErrorInvalidValue) return BTE_ERR_DIM;
+  return e == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
 }
 
 // Descending-length processing order: one workgroup sorts 64-bit keys
@@ -599,6 +654,22 @@ extern "C" int bte_attention_order(const int32_t* kv_len, int batch, int32_t* or
   return hipGetLastError() == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
 }
 
+// Host-side checks common to both attention entry points.
+static int attention_args_ok(const void* q, const int32_t* count, const int32_t* cu,
+                             const void* cache_k, const void* cache_v, const int32_t* kv_len,
+                             const void* out, int batch, int k_max, int hq, int hkv, int head_dim,
+                             float scale, bte_dtype dtype) {
+  using namespace bte;
+  if (!q || !count || !cu || !cache_k || !cache_v || !kv_len || !out) return BTE_ERR_NULL;
+  if (batch <= 0 || k_max < 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0) return BTE_ERR_DIM;
+  if (!(scale > 0.f) || !isfinite(scale)) return BTE_ERR_DIM;
+  if (head_dim != 64 && head_dim != 128) return BTE_ERR_UNSUPPORTED;
+  if (dtype != BTE_F32 && dtype != BTE_BF16) return BTE_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(cache_k) || !aligned16(cache_v) || !aligned16(out))
+    return BTE_ERR_ALIGN;
+  return BTE_OK;
+}
+
 extern "C" int bte_reduced_attention(const void* q, const int32_t* count, const int32_t* cu,
                                      const void* cache_k, const void* cache_v,
                                      const int64_t* seq_start, const int32_t* kv_len,
@@ -606,22 +677,35 @@ extern "C" int bte_reduced_attention(const void* q, const int32_t* count, const 
                                      int hkv, int head_dim, float scale, bte_dtype dtype,
                                      hipStream_t stream) {
   using namespace bte;
-  if (!q || !count || !cu || !cache_k || !cache_v || !seq_start || !kv_len || !out)
-    return BTE_ERR_NULL;
-  if (batch <= 0 || k_max < 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0) return BTE_ERR_DIM;
-  if (!(scale > 0.f) || !isfinite(scale)) return BTE_ERR_DIM;
-  if (head_dim != 64 && head_dim != 128) return BTE_ERR_UNSUPPORTED;
-  if (dtype != BTE_F32 && dtype != BTE_BF16) return BTE_ERR_UNSUPPORTED;
-  if (!aligned16(q) || !aligned16(cache_k) || !aligned16(cache_v) || !aligned16(out))
-    return BTE_ERR_ALIGN;
+  if (!seq_start) return BTE_ERR_NULL;
+  const int st = attention_args_ok(q, count, cu, cache_k, cache_v, kv_len, out, batch, k_max, hq,
+                                   hkv, head_dim, scale, dtype);
+  if (st != BTE_OK || k_max == 0) return st;
+  const AttnArgs a{q, count, cu, cache_k, cache_v, KvMap{seq_start, nullptr, 0, 0}, kv_len, order,
+                   out, batch, k_max, hq, hkv, scale * kLog2e};
+  return attention<kContig>(a, head_dim, dtype, stream);
+}
+
+extern "C" int bte_reduced_attention_paged(const void* q, const int32_t* count, const int32_t* cu,
+                                           const void* cache_k, const void* cache_v,
+                                           const int32_t* block_table, int max_pages,
+                                           int page_size, const int32_t* kv_len,
+                                           const int32_t* order, void* out, int batch, int k_max,
+                                           int hq, int hkv, int head_dim, float scale,
+                                           bte_dtype dtype, hipStream_t stream) {
+  using namespace bte;
+  if (!block_table) return BTE_ERR_NULL;
+  const int st = attention_args_ok(q, count, cu, cache_k, cache_v, kv_len, out, batch, k_max, hq,
+                                   hkv, head_dim, scale, dtype);
+  if (st != BTE_OK) return st;
+  if (max_pages <= 0) return BTE_ERR_DIM;
+  if (page_size < 8 || page_size > (1 << 20) || (page_size & (page_size - 1)) != 0)
+    return BTE_ERR_UNSUPPORTED;
   if (k_max == 0) return BTE_OK;
-  const AttnArgs a{q, count, cu, cache_k, cache_v, seq_start, kv_len, order, out,
-                   batch, k_max, hq, hkv, scale * kLog2e};
-  hipError_t e;
-  if (dtype == BTE_BF16)
-    e = head_dim == 128 ? launch_bf16<128>(a, stream) : launch_bf16<64>(a, stream);
-  else  // fp32 operands take twice the registers: 32 query rows per workgroup only
-    e = head_dim == 128 ? launch<128, false, 1, 4>(a, stream) : launch<64, false, 1, 4>(a, stream);
-  if (e == hipErrorInvalidValue) return BTE_ERR_DIM;
-  return e == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
+  int lg = 0;
+  while ((1 << lg) < page_size) ++lg;
+  const AttnArgs a{q, count, cu, cache_k, cache_v, KvMap{nullptr, block_table, max_pages, lg},
+                   kv_len, order, out, batch, k_max, hq, hkv, scale * kLog2e};
+  return max_pages <= kPageCache ? attention<kPagedLds>(a, head_dim, dtype, stream)
+                                  : attention<kPagedMem>(a, head_dim, dtype, stream);
 }

@@ -93,12 +93,24 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(
   }
 }
 
+// Scatter destination: contiguous (row_base[b] + pos) or, with a page table,
+// logical position pos_base[b] + pos at row block_table[b][p >> lg] * page +
+// p % page of the page pool.
+struct ScatterMap {
+  const int64_t* row_base;
+  const int32_t* pos_base;
+  const int32_t* block_table;
+  int max_pages;
+  int lg_page;
+};
+
+template <bool kPaged>
 __global__ __launch_bounds__(kThreads) void scatter_rows_kernel(
     const char* __restrict__ new_k, const char* __restrict__ new_v, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ count, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ pos_map, int n, const int64_t* __restrict__ row_base,
-    char* __restrict__ cache_k, char* __restrict__ cache_v, int k_max, size_t row_bytes,
-    int n_split, uint32_t per, float inv_cpr) {
+    const int32_t* __restrict__ pos_map, int n, ScatterMap map, char* __restrict__ cache_k,
+    char* __restrict__ cache_v, int k_max, size_t row_bytes, int n_split, uint32_t per,
+    float inv_cpr) {
   const int b = blockIdx.x / n_split;
   const uint32_t s = blockIdx.x - b * n_split;
   const uint32_t cpr = (uint32_t)(row_bytes / 16);
@@ -106,14 +118,20 @@ __global__ __launch_bounds__(kThreads) void scatter_rows_kernel(
   if (!share((uint32_t)count[b] * cpr, per, s, lo, hi)) return;
   const int32_t* ib = idx + (size_t)b * k_max;
   const int32_t* pm = pos_map ? pos_map + (size_t)b * n : nullptr;
-  const int64_t rb = row_base[b];
+  const int64_t rb = kPaged ? (int64_t)map.pos_base[b] : map.row_base[b];
+  const int32_t* bt = kPaged ? map.block_table + (size_t)b * map.max_pages : nullptr;
   const char* sb = (blockIdx.y == 0 ? new_k : new_v) + (size_t)cu[b] * row_bytes;
   char* cache = blockIdx.y == 0 ? cache_k : cache_v;
   copy_range(lo, hi, cpr, inv_cpr, [&](uint32_t t) { return sb + (size_t)t * row_bytes; },
              [&](uint32_t t) {
                const int j = ib[t];
-               const int64_t pos = pm ? pm[j] : j;
-               return cache + (size_t)(rb + pos) * row_bytes;
+               const int64_t p = rb + (pm ? pm[j] : j);
+               size_t row = (size_t)p;
+               if constexpr (kPaged) {
+                 const int lg = map.lg_page;
+                 row = ((size_t)bt[p >> lg] << lg) + (size_t)(p & ((1 << lg) - 1));
+               }
+               return cache + row * row_bytes;
              });
 }
 
@@ -157,22 +175,66 @@ extern "C" int bte_gather_rows(const void* src, const int32_t* idx, const int32_
   return hipGetLastError() == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
 }
 
+static int scatter_args_ok(const void* new_k, const void* new_v, const int32_t* idx,
+                           const int32_t* count, const int32_t* cu, const int32_t* pos_map, int n,
+                           const void* cache_k, const void* cache_v, int batch, int k_max,
+                           size_t row_bytes) {
+  using namespace bte;
+  if (!new_k || !idx || !count || !cu || !cache_k) return BTE_ERR_NULL;
+  if ((new_v == nullptr) != (cache_v == nullptr)) return BTE_ERR_NULL;
+  if (batch <= 0 || k_max < 0 || row_bytes == 0 || (pos_map && n <= 0)) return BTE_ERR_DIM;
+  if (row_bytes % 16 != 0 || !aligned16(new_k) || !aligned16(cache_k)) return BTE_ERR_ALIGN;
+  if (new_v && (!aligned16(new_v) || !aligned16(cache_v))) return BTE_ERR_ALIGN;
+  return BTE_OK;
+}
+
+template <bool kPaged>
+static int scatter_launch(const void* new_k, const void* new_v, const int32_t* idx,
+                          const int32_t* count, const int32_t* cu, const int32_t* pos_map, int n,
+                          bte::ScatterMap map, void* cache_k, void* cache_v, int batch, int k_max,
+                          size_t row_bytes, hipStream_t stream) {
+  using namespace bte;
+  const Split sp = plan(batch, k_max, row_bytes);
+  if (!sp.ok) return BTE_ERR_DIM;
+  hipLaunchKernelGGL(scatter_rows_kernel<kPaged>, dim3((unsigned)(batch * sp.n_split), new_v ? 2 : 1),
+                     dim3(kThreads), 0, stream, (const char*)new_k, (const char*)new_v, idx, count,
+                     cu, pos_map, n, map, (char*)cache_k, (char*)cache_v, k_max, row_bytes,
+                     sp.n_split, sp.per, 1.0f / (float)(row_bytes / 16));
+  return hipGetLastError() == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
+}
+
 extern "C" int bte_kv_scatter(const void* new_k, const void* new_v, const int32_t* idx,
                               const int32_t* count, const int32_t* cu, const int32_t* pos_map,
                               int n, const int64_t* row_base, void* cache_k, void* cache_v,
                               int batch, int k_max, size_t row_bytes, hipStream_t stream) {
   using namespace bte;
-  if (!new_k || !idx || !count || !cu || !row_base || !cache_k) return BTE_ERR_NULL;
-  if ((new_v == nullptr) != (cache_v == nullptr)) return BTE_ERR_NULL;
-  if (batch <= 0 || k_max < 0 || row_bytes == 0 || (pos_map && n <= 0)) return BTE_ERR_DIM;
-  if (row_bytes % 16 != 0 || !aligned16(new_k) || !aligned16(cache_k)) return BTE_ERR_ALIGN;
-  if (new_v && (!aligned16(new_v) || !aligned16(cache_v))) return BTE_ERR_ALIGN;
+  if (!row_base) return BTE_ERR_NULL;
+  const int st = scatter_args_ok(new_k, new_v, idx, count, cu, pos_map, n, cache_k, cache_v, batch,
+                                 k_max, row_bytes);
+  if (st != BTE_OK || k_max == 0) return st;
+  return scatter_launch<false>(new_k, new_v, idx, count, cu, pos_map, n,
+                               ScatterMap{row_base, nullptr, nullptr, 0, 0}, cache_k, cache_v,
+                               batch, k_max, row_bytes, stream);
+}
+
+extern "C" int bte_kv_scatter_paged(const void* new_k, const void* new_v, const int32_t* idx,
+                                    const int32_t* count, const int32_t* cu,
+                                    const int32_t* pos_map, int n, const int32_t* pos_base,
+                                    const int32_t* block_table, int max_pages, int page_size,
+                                    void* cache_k, void* cache_v, int batch, int k_max,
+                                    size_t row_bytes, hipStream_t stream) {
+  using namespace bte;
+  if (!pos_base || !block_table) return BTE_ERR_NULL;
+  const int st = scatter_args_ok(new_k, new_v, idx, count, cu, pos_map, n, cache_k, cache_v, batch,
+                                 k_max, row_bytes);
+  if (st != BTE_OK) return st;
+  if (max_pages <= 0) return BTE_ERR_DIM;
+  if (page_size < 1 || page_size > (1 << 20) || (page_size & (page_size - 1)) != 0)
+    return BTE_ERR_UNSUPPORTED;
   if (k_max == 0) return BTE_OK;
-  const Split sp = plan(batch, k_max, row_bytes);
-  if (!sp.ok) return BTE_ERR_DIM;
-  hipLaunchKernelGGL(scatter_rows_kernel, dim3((unsigned)(batch * sp.n_split), new_v ? 2 : 1),
-                     dim3(kThreads), 0, stream, (const char*)new_k, (const char*)new_v, idx, count,
-                     cu, pos_map, n, row_base, (char*)cache_k, (char*)cache_v, k_max, row_bytes,
-                     sp.n_split, sp.per, 1.0f / (float)(row_bytes / 16));
-  return hipGetLastError() == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
+  int lg = 0;
+  while ((1 << lg) < page_size) ++lg;
+  return scatter_launch<true>(new_k, new_v, idx, count, cu, pos_map, n,
+                              ScatterMap{nullptr, pos_base, block_table, max_pages, lg}, cache_k,
+                              cache_v, batch, k_max, row_bytes, stream);
 }

@@ -222,6 +222,28 @@ int bte_kv_scatter(const void* new_k, const void* new_v, const int32_t* idx, con
                    hipStream_t stream);
 
 /*
+ * The KV scatter on a paged cache (FOCUS paper App. E.2.4: sparse KV cache
+ * filling writes the processed positions' K/V to their physical offsets in
+ * the PagedAttention pool). As bte_kv_scatter, with the destination of kept
+ * row t of sequence b at logical position p = pos_base[b] + pos (pos = idx
+ * or pos_map[b, idx]) being pool row
+ *   block_table[b, p / page_size] * page_size + p % page_size.
+ *
+ *   cache_k, cache_v [n_pages * page_size, row_bytes] (the page pool)
+ *   pos_base [batch] int32; block_table [batch, max_pages] int32
+ * Limits: page_size a power of two; rows distinct; entries of block_table
+ * that are read must be valid pages (device contract).
+ * Errors: as bte_kv_scatter; NULL pos_base/block_table -> BTE_ERR_NULL;
+ * max_pages <= 0 -> BTE_ERR_DIM; page_size not a power of two ->
+ * BTE_ERR_UNSUPPORTED.
+ */
+int bte_kv_scatter_paged(const void* new_k, const void* new_v, const int32_t* idx,
+                         const int32_t* count, const int32_t* cu, const int32_t* pos_map, int n,
+                         const int32_t* pos_base, const int32_t* block_table, int max_pages,
+                         int page_size, void* cache_k, void* cache_v, int batch, int k_max,
+                         size_t row_bytes, hipStream_t stream);
+
+/*
  * Reduced-query GQA attention of the kept rows over prefix + block
  * (FOCUS paper Section 2 / Table 2 KV-cache attention over the exact cache,
  * Section 4.2: later layers run only on the kept rows, evicted tokens stay as
@@ -256,6 +278,28 @@ int bte_reduced_attention(const void* q, const int32_t* count, const int32_t* cu
                           const int32_t* kv_len, const int32_t* order, void* out, int batch,
                           int k_max, int hq, int hkv, int head_dim, float scale, bte_dtype dtype,
                           hipStream_t stream);
+
+/*
+ * Reduced-query attention over a paged KV cache (FOCUS paper App. E.2.4:
+ * ragged attention over the PagedAttention pool). As bte_reduced_attention,
+ * with sequence b's logical KV position p (p < kv_len[b]) read from pool row
+ *   block_table[b, p / page_size] * page_size + p % page_size.
+ * Same arithmetic and launch as the contiguous call: results are bitwise
+ * those of the contiguous call on the rows the table maps to.
+ *
+ *   cache_k, cache_v [n_pages * page_size, hkv, head_dim] dtype
+ *   block_table [batch, max_pages] int32 (entries < ceil(kv_len/page_size)
+ *   read; they must be valid pages: device contract)
+ * Limits: page_size a power of two, 8 <= page_size <= 2^20.
+ * Errors: as bte_reduced_attention; NULL block_table -> BTE_ERR_NULL;
+ * max_pages <= 0 -> BTE_ERR_DIM; page_size out of range -> BTE_ERR_UNSUPPORTED.
+ */
+int bte_reduced_attention_paged(const void* q, const int32_t* count, const int32_t* cu,
+                                const void* cache_k, const void* cache_v,
+                                const int32_t* block_table, int max_pages, int page_size,
+                                const int32_t* kv_len, const int32_t* order, void* out, int batch,
+                                int k_max, int hq, int hkv, int head_dim, float scale,
+                                bte_dtype dtype, hipStream_t stream);
 
 /*
  * Work order for bte_reduced_attention: order_out[0..batch-1] = the sequence

@@ -25,7 +25,7 @@ def declared():
 
 def test_every_declared_symbol_is_exported():
     names = declared()
-    assert len(names) == 12
+    assert len(names) == 14
     for name in names:
         assert hasattr(lib, name), name
 
@@ -143,3 +143,28 @@ def test_budget_select_errors():
     assert s(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 4, 32, None) == NULL
     assert s(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 32, None) == DIM
     assert s(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 65, None) == UNSUP
+
+
+def test_paged_errors():
+    f = lib.bte_reduced_attention_paged
+    # q, count, cu, ck, cv, block_table, max_pages, page_size, kv_len, order, out, batch, k_max,
+    # hq, hkv, head_dim, scale, dtype, stream
+    args = [FAKE] * 6 + [4, 64] + [FAKE] * 3 + [4, 8, 32, 8, 128, 0.088, 1, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a5=None) == NULL
+    assert call(a0=None) == NULL
+    assert call(a6=0) == DIM
+    assert call(a7=48) == UNSUP
+    assert call(a7=4) == UNSUP
+    assert call(a16=0.0) == DIM
+    assert call(a12=0) == OK
+    s = lib.bte_kv_scatter_paged
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None, FAKE, 4, 16, FAKE, FAKE, 2, 8, 2048, None) == NULL
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, 0, 16, FAKE, FAKE, 2, 8, 2048, None) == DIM
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, 4, 12, FAKE, FAKE, 2, 8, 2048, None) == UNSUP
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, 4, 16, FAKE, FAKE, 2, 0, 2048, None) == OK

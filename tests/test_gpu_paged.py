@@ -1,0 +1,117 @@
+"""GPU parity of the paged KV scatter and paged reduced attention: bitwise
+equal to the contiguous kernels on the rows a shuffled page table maps to,
+and within tolerance of the oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from helpers import assert_close, dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _bte():
+    import block_token_eviction_amd as bte
+    return bte
+
+
+def _page_table(kv_len, page_size, seed, spare=5):
+    """Shuffled pages: block_table [batch, max_pages] (-1 past a sequence's
+    pages) and, for every pool row, the contiguous cache row it holds (-1 if
+    none)."""
+    r = np.random.default_rng(seed)
+    kv_len = np.asarray(kv_len, np.int64)
+    need = (kv_len + page_size - 1) // page_size
+    n_pages = int(need.sum()) + spare
+    perm = r.permutation(n_pages).astype(np.int32)
+    bt = np.full((len(kv_len), int(need.max())), -1, np.int32)
+    src = np.full(n_pages * page_size, -1, np.int64)
+    seq_start = np.concatenate([[0], np.cumsum(kv_len)[:-1]])
+    at = 0
+    for b in range(len(kv_len)):
+        pages = perm[at:at + need[b]]
+        at += need[b]
+        bt[b, :need[b]] = pages
+        p = np.arange(kv_len[b])
+        src[pages[p // page_size].astype(np.int64) * page_size + p % page_size] = seq_start[b] + p
+    return bt, src, n_pages
+
+
+def _pool(cache, src, n_pages, page_size):
+    pool = torch.randn((n_pages * page_size,) + tuple(cache.shape[1:]), device=cache.device).to(cache.dtype)
+    have = torch.from_numpy(np.flatnonzero(src >= 0)).to(cache.device)
+    pool[have] = cache[torch.from_numpy(src[src >= 0]).to(cache.device)]
+    return pool
+
+
+CFGS = [
+    (W.ATTN_B256, 64),
+    (W.ATTN_B256, 16),
+    (W.AttnCfg("paged_small", seed=71, batch=9, kept=None, k_lo=0, k_hi=12, hq=32, hkv=8,
+               head_dim=128, prefix_lo=1, prefix_hi=300), 8),
+    (W.AttnCfg("paged_d64", seed=72, batch=600, kept=None, k_lo=1, k_hi=16, hq=32, hkv=8,
+               head_dim=64, prefix_lo=30, prefix_hi=200), 256),
+    (W.AttnCfg("paged_f32", seed=73, batch=5, kept=4, hq=8, hkv=2, head_dim=128, dtype=W.F32,
+               prefix_lo=40, prefix_hi=150), 32),
+    # more than 2048 pages per sequence: page entries are read from memory
+    (W.AttnCfg("paged_long_table", seed=74, batch=3, kept=5, hq=8, hkv=2, head_dim=128,
+               prefix_lo=16600, prefix_hi=17000), 8),
+]
+
+
+@pytest.mark.parametrize("cfg,page", CFGS, ids=[f"{c.name}-p{p}" for c, p in CFGS])
+@pytest.mark.parametrize("ordered", [False, True], ids=["index_order", "longest_first"])
+def test_paged_attention(cfg, page, ordered):
+    bte = _bte()
+    ai = W.attention_inputs(cfg)
+    g = dev(ai)
+    bt, src, n_pages = _page_table(ai["kv_len"].numpy(), page, seed=cfg.seed)
+    say(f"paged attention {cfg.name} page={page} ordered={ordered}")
+    pk, pv = _pool(g["cache_k"], src, n_pages, page), _pool(g["cache_v"], src, n_pages, page)
+    order = bte.attention_order(g["kv_len"]) if ordered else None
+    out_p = bte.reduced_attention_paged(g["q"], g["count"], g["cu"], pk, pv,
+                                        torch.from_numpy(bt).cuda(), page, g["kv_len"],
+                                        ai["k_max"], order=order)
+    out_c = bte.reduced_attention(g["q"], g["count"], g["cu"], g["cache_k"], g["cache_v"],
+                                  g["seq_start"], g["kv_len"], ai["k_max"], order=order)
+    n = int(ai["cu"][-1])
+    assert torch.equal(out_p[:n], out_c[:n])
+    if ai["rows"] > 200_000:
+        return        # the contiguous kernel is checked against the oracle at this size
+    ref = oracle.reduced_attention_paged(W.to_f64(ai["q"]), ai["count"].numpy(), ai["cu"].numpy(),
+                                         W.to_f64(pk), W.to_f64(pv), bt, page,
+                                         ai["kv_len"].numpy(), cfg.hq, cfg.hkv,
+                                         1.0 / math.sqrt(cfg.head_dim))
+    assert_close(out_p[:n].cpu().double().numpy(), ref[:n], cfg.name)
+
+
+@pytest.mark.parametrize("page", [1, 16, 64])
+def test_paged_scatter(page):
+    bte = _bte()
+    cfg = W.ATTN_B256
+    ai = W.attention_inputs(cfg)
+    g = dev(ai)
+    bt, src, n_pages = _page_table(ai["kv_len"].numpy(), page, seed=page)
+    say(f"paged scatter page={page}")
+    pk, pv = _pool(g["cache_k"], src, n_pages, page), _pool(g["cache_v"], src, n_pages, page)
+    pk0, pv0 = pk.clone(), pv.clone()
+    pos_base = ai["prefix"].to(torch.int32).cuda()
+    bte.kv_scatter_paged(g["new_k"], g["new_v"], g["idx"], g["count"], g["cu"], pos_base,
+                         torch.from_numpy(bt).cuda(), page, pk, pv)
+    # the oracle on the same pool
+    bits = lambda t: t.cpu().view(torch.int16).numpy()
+    rk, rv = oracle.kv_scatter_paged(bits(ai["new_k"]), bits(ai["new_v"]), ai["idx"].numpy(),
+                                     ai["count"].numpy(), ai["cu"].numpy(), ai["prefix"].numpy(),
+                                     bt, page, bits(pk0), bits(pv0))
+    np.testing.assert_array_equal(pk.cpu().view(torch.int16).numpy(), rk)
+    np.testing.assert_array_equal(pv.cpu().view(torch.int16).numpy(), rv)
+    # and the contiguous scatter lands the same bytes on the rows the table maps to
+    ck, cv = g["cache_k"].clone(), g["cache_v"].clone()
+    bte.kv_scatter(g["new_k"], g["new_v"], g["idx"], g["count"], g["cu"], g["row_base"], ck, cv)
+    have = torch.from_numpy(np.flatnonzero(src >= 0)).cuda()
+    back = torch.from_numpy(src[src >= 0]).cuda()
+    assert torch.equal(pk[have], ck[back]) and torch.equal(pv[have], cv[back])
