@@ -25,6 +25,10 @@ operations of the path, written from the pages' definitions:
   placeholder integrity, |S| >= 1; FOCUS paper Section 4.2, App. E.2.2).
 * ``kv_scatter_paged``, ``reduced_attention_paged`` — the same scatter and
   attention on a paged KV pool through a page table (FOCUS paper App. E.2.4).
+* ``commit_mask`` — the neighbour-aware delayed commit of block KV states
+  (FOCUS paper Section 4.3, App. E.3.1, App. E.3.3).
+* ``gather_rows_multi`` — several row tensors compacted with one index set
+  (FOCUS paper App. E.2.3).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package. The product path
@@ -39,7 +43,8 @@ from .focus import (block_scores, maxpool_keys, softmax_keys, importance,
 from .esdllm import esdllm_score
 from .selection import topk_select, focus_select
 from .budget import focus_budget, history_update
-from .rows import gather_rows, kv_scatter
+from .rows import gather_rows, gather_rows_multi, kv_scatter
+from .cache_state import commit_mask
 from .attention import reduced_attention
 from .schedule import attention_order
 from .paged import kv_scatter_paged, reduced_attention_paged, physical_row
@@ -48,4 +53,4 @@ __all__ = ["block_scores", "maxpool_keys", "softmax_keys", "importance",
            "focus_importance_delta", "esdllm_score", "topk_select", "gather_rows",
            "kv_scatter", "reduced_attention", "attention_order", "focus_budget",
            "history_update", "focus_select", "kv_scatter_paged", "reduced_attention_paged",
-           "physical_row"]
+           "physical_row", "commit_mask", "gather_rows_multi"]

@@ -37,6 +37,13 @@ def gather_rows(src: np.ndarray, idx, count, cu) -> np.ndarray:
     return d.view(src.dtype).reshape((total,) + src.shape[2:])
 
 
+def gather_rows_multi(srcs, idx, count, cu):
+    """Each src [batch, n, ...] gathered with the same index set (FOCUS paper
+    App. E.2.3: hidden states, residual, RoPE positions and cache indices are
+    compacted together)."""
+    return [gather_rows(s, idx, count, cu) for s in srcs]
+
+
 def kv_scatter(new_k: np.ndarray, new_v: np.ndarray, idx, count, cu, row_base,
                cache_k: np.ndarray, cache_v: np.ndarray, pos_map=None):
     """Returns updated copies (cache_k', cache_v'); the inputs are not modified."""

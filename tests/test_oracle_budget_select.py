@@ -113,3 +113,39 @@ def test_select_properties_random():
             assert len(S) == 1
         assert len(S) >= 1 and cnt[0] == len(S) and cu[1] == cnt[0]
         assert rpn[0] == max(rp, max(S))
+
+
+def test_commit_mask_truth_table():
+    """Every (decoded, cached) state of a 3-position block, against the rule
+    written out position by position."""
+    import itertools
+    for bits in itertools.product([0, 1], repeat=6):
+        dec = np.array([bits[:3]], bool)
+        cac = np.array([bits[3:]], bool)
+        commit, new, done = oracle.commit_mask(dec, cac)
+        d, c = dec[0], cac[0]
+        want = [not c[0] and d[0] and d[1],
+                not c[1] and d[1] and d[2],
+                not c[2] and d[2] and d[0] and d[1]]        # last: whole block decoded
+        assert commit[0].tolist() == want, bits
+        assert new[0].tolist() == [bool(x or y) for x, y in zip(c, want)]
+        assert done[0] == int(all(new[0]))
+
+
+def test_commit_mask_hand_example():
+    # decoded 1 1 0 1 1 (right neighbours: 1 0 1 1 -, whole block not decoded)
+    commit, new, done = oracle.commit_mask(np.array([[1, 1, 0, 1, 1]], bool),
+                                           np.array([[0, 0, 0, 0, 0]], bool))
+    assert commit[0].tolist() == [True, False, False, True, False] and done[0] == 0
+    commit, new, done = oracle.commit_mask(np.array([[1, 1, 1, 1, 1]], bool), new)
+    assert commit[0].tolist() == [False, True, True, False, True] and done[0] == 1
+
+
+def test_gather_multi_matches_single():
+    r = np.random.default_rng(12)
+    idx, cnt, cu = oracle.topk_select(r.standard_normal((4, 9)), [3, 0, 9, 5], 9)
+    srcs = [r.standard_normal((4, 9, 6)), r.integers(0, 100, (4, 9)).astype(np.int32),
+            r.integers(0, 9, (4, 9, 2)).astype(np.int64)]
+    outs = oracle.gather_rows_multi(srcs, idx, cnt, cu)
+    for s, o in zip(srcs, outs):
+        np.testing.assert_array_equal(o, np.concatenate([s[b, idx[b, :cnt[b]]] for b in range(4)]))
