@@ -20,7 +20,7 @@ import torch
 __all__ = ["lib", "LIB_PATH", "BteError", "status_string", "focus_importance_delta",
            "esdllm_score", "topk_select", "gather_rows", "kv_scatter", "reduced_attention",
            "attention_order", "reduced_attention_paged", "kv_scatter_paged", "focus_budget",
-           "focus_history_update", "focus_select",
+           "focus_history_update", "focus_select", "focus_commit_mask", "gather_rows_multi",
            "BTE_F32", "BTE_BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbte.so")
@@ -49,6 +49,8 @@ _SIG = {
     "bte_focus_budget": ([_p, _p, _p, _f, _i, _p, _i, _i, _p], _i),
     "bte_focus_history_update": ([_p, _p, _p, _p, _i, _i, _p], _i),
     "bte_focus_select": ([_p, _p, _p, _p, _p, _p, _p, _i, _i, _p], _i),
+    "bte_focus_commit_mask": ([_p, _p, _p, _p, _i, _i, _p], _i),
+    "bte_gather_rows_multi": ([_p, _i, _p, _p, _p, _i, _i, _i, _p], _i),
 }
 for _name, (_args, _res) in _SIG.items():
     _fn = getattr(lib, _name)
@@ -321,3 +323,47 @@ def kv_scatter_paged(new_k, new_v, idx, count, cu, pos_base, block_table, page_s
         _ptr(pos_base), _ptr(block_table), block_table.shape[1], page_size, _ptr(cache_k),
         _ptr(cache_v), batch, k_max, row_bytes, _stream()))
     return cache_k, cache_v
+
+
+def focus_commit_mask(decoded, cached, commit=None, block_done=None):
+    """decoded uint8 [batch, B], cached uint8 [batch, B] (updated in place)
+    -> (commit uint8 [batch, B], block_done int32 [batch])."""
+    _dev(decoded, cached, commit, block_done)
+    _want(decoded, torch.uint8, "decoded")
+    _want(cached, torch.uint8, "cached")
+    batch, block = decoded.shape
+    assert cached.shape == (batch, block)
+    if commit is None:
+        commit = torch.empty_like(decoded)
+    if block_done is None:
+        block_done = torch.empty((batch,), dtype=torch.int32, device=decoded.device)
+    _check("bte_focus_commit_mask", lib.bte_focus_commit_mask(
+        _ptr(decoded), _ptr(cached), _ptr(commit), _ptr(block_done), batch, block, _stream()))
+    return commit, block_done
+
+
+class _RowsTensor(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_void_p), ("dst", ctypes.c_void_p), ("row_bytes", ctypes.c_size_t)]
+
+
+def gather_rows_multi(srcs, idx, count, cu, outs=None):
+    """Each src [batch, n, ...] compacted with the same index set in one launch;
+    returns the outputs [batch * k_max, ...] (rows cu[b]+t written)."""
+    _dev(idx, count, cu, *srcs)
+    batch, k_max = idx.shape
+    n = srcs[0].shape[1]
+    if outs is None:
+        outs = [torch.empty((batch * k_max,) + tuple(s.shape[2:]), dtype=s.dtype, device=s.device)
+                for s in srcs]
+    _dev(*outs)
+    descs = []
+    for s_, o in zip(srcs, outs):
+        assert s_.shape[:2] == (batch, n) and o.dtype == s_.dtype
+        rb = s_[0, 0].numel() * s_.element_size()
+        assert o[0].numel() * o.element_size() == rb
+        descs.append(_RowsTensor(s_.data_ptr(), o.data_ptr(), rb))
+    arr = (_RowsTensor * len(descs))(*descs)
+    _check("bte_gather_rows_multi", lib.bte_gather_rows_multi(
+        ctypes.cast(arr, ctypes.c_void_p), len(descs), _ptr(idx), _ptr(count), _ptr(cu), batch, n,
+        k_max, _stream()))
+    return outs

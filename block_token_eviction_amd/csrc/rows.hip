@@ -21,6 +21,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
 constexpr int kPass = kThreads * kUnroll;   // chunks one workgroup moves per pass
+constexpr int kMaxTensors = 8;             // tensors of one multi-row gather
 
 // Row and chunk of flat chunk index c, with chunks per row cpr and its float
 // reciprocal (exact after the +-1 correction for c < 2^24).
@@ -89,6 +90,40 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(
     for (int u = 0; u < kUnroll; ++u) {
       const size_t c = base + (size_t)u * kThreads + threadIdx.x;
       if (c < chunks) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(d + 16 * c));
+    }
+  }
+}
+
+// Several row tensors compacted with one index set in one launch (FOCUS paper
+// App. E.2.3: hidden states, residual, RoPE positions and cache indices).
+// One workgroup per (sequence, slot); each tensor's row is copied in 16-byte
+// chunks when its size and pointers allow, else in 4-byte words.
+struct MultiRows {
+  const char* src[kMaxTensors];
+  char* dst[kMaxTensors];
+  uint32_t row_bytes[kMaxTensors];
+  uint32_t wide[kMaxTensors];
+  int n_tensors;
+};
+
+__global__ __launch_bounds__(kThreads) void gather_multi_kernel(
+    MultiRows m, const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
+    const int32_t* __restrict__ cu, int n, int k_max) {
+  const int b = blockIdx.x / k_max;
+  const int t = blockIdx.x - b * k_max;
+  if (t >= count[b]) return;
+  const size_t src_row = (size_t)b * n + idx[(size_t)b * k_max + t];
+  const size_t dst_row = (size_t)cu[b] + t;
+  for (int k = 0; k < m.n_tensors; ++k) {
+    const size_t rb = m.row_bytes[k];
+    const char* s = m.src[k] + src_row * rb;
+    char* d = m.dst[k] + dst_row * rb;
+    if (m.wide[k]) {
+      for (size_t c = threadIdx.x; c < rb / 16; c += kThreads)
+        __builtin_nontemporal_store(ld16_stream(s + 16 * c), reinterpret_cast<u32x4*>(d + 16 * c));
+    } else {
+      for (size_t c = threadIdx.x; c < rb / 4; c += kThreads)
+        reinterpret_cast<uint32_t*>(d)[c] = reinterpret_cast<const uint32_t*>(s)[c];
     }
   }
 }
@@ -237,4 +272,32 @@ extern "C" int bte_kv_scatter_paged(const void* new_k, const void* new_v, const 
   return scatter_launch<true>(new_k, new_v, idx, count, cu, pos_map, n,
                               ScatterMap{nullptr, pos_base, block_table, max_pages, lg}, cache_k,
                               cache_v, batch, k_max, row_bytes, stream);
+}
+
+extern "C" int bte_gather_rows_multi(const bte_rows_tensor* tensors, int n_tensors,
+                                     const int32_t* idx, const int32_t* count, const int32_t* cu,
+                                     int batch, int n, int k_max, hipStream_t stream) {
+  using namespace bte;
+  if (!tensors || !idx || !count || !cu) return BTE_ERR_NULL;
+  if (n_tensors < 1 || n_tensors > kMaxTensors || batch <= 0 || n <= 0 || k_max < 0)
+    return BTE_ERR_DIM;
+  MultiRows m{};
+  m.n_tensors = n_tensors;
+  for (int k = 0; k < n_tensors; ++k) {
+    const bte_rows_tensor& t = tensors[k];
+    if (!t.src || !t.dst) return BTE_ERR_NULL;
+    if (t.row_bytes == 0 || t.row_bytes > 0xffffffffu) return BTE_ERR_DIM;
+    if (t.row_bytes % 4 != 0 || ((uintptr_t)t.src & 3u) || ((uintptr_t)t.dst & 3u))
+      return BTE_ERR_ALIGN;
+    m.src[k] = (const char*)t.src;
+    m.dst[k] = (char*)t.dst;
+    m.row_bytes[k] = (uint32_t)t.row_bytes;
+    m.wide[k] = (t.row_bytes % 16 == 0 && aligned16(t.src) && aligned16(t.dst)) ? 1u : 0u;
+  }
+  if (k_max == 0) return BTE_OK;
+  const size_t grid = (size_t)batch * (size_t)k_max;
+  if (grid > 0x7fffffffu) return BTE_ERR_DIM;
+  hipLaunchKernelGGL(gather_multi_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, m, idx,
+                     count, cu, n, k_max);
+  return hipGetLastError() == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
 }

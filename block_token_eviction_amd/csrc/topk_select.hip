@@ -260,6 +260,36 @@ __global__ __launch_bounds__(256) void focus_select_kernel(
   }
 }
 
+
+// Neighbour-aware delayed commit of block KV states (FOCUS paper Section 4.3,
+// App. E.3.1, App. E.3.3). One thread per sequence: position i commits in
+// this step if it is not cached yet and both it and its right neighbour are
+// decoded (the block's last position: once the whole block is decoded).
+// `cached` is updated in place; block_done = every position cached.
+__global__ __launch_bounds__(256) void commit_mask_kernel(const uint8_t* __restrict__ decoded,
+                                                          uint8_t* __restrict__ cached,
+                                                          uint8_t* __restrict__ commit,
+                                                          int32_t* __restrict__ block_done,
+                                                          int batch, int B) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= batch) return;
+  const uint8_t* d = decoded + (size_t)b * B;
+  uint8_t* c = cached + (size_t)b * B;
+  uint8_t* o = commit + (size_t)b * B;
+  bool whole = true;
+  for (int j = 0; j < B; ++j) whole = whole && d[j] != 0;
+  bool done = true;
+  for (int j = 0; j < B; ++j) {
+    const bool right = j + 1 < B ? d[j + 1] != 0 : whole;
+    const bool was = c[j] != 0;
+    const bool now = !was && d[j] != 0 && right;
+    o[j] = now ? 1 : 0;
+    if (now) c[j] = 1;
+    done = done && (was || now);
+  }
+  if (block_done) block_done[b] = done ? 1 : 0;
+}
+
 }  // namespace
 }  // namespace bte
 
@@ -321,5 +351,16 @@ extern "C" int bte_focus_select(const float* delta, const int32_t* k, const uint
                      decoded, rightmost_processed, idx_out, count_out, batch, block);
   if (hipGetLastError() != hipSuccess) return BTE_ERR_LAUNCH;
   hipLaunchKernelGGL(exclusive_scan_kernel, dim3(1), dim3(1024), 0, stream, count_out, cu_out, batch);
+  return hipGetLastError() == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
+}
+
+extern "C" int bte_focus_commit_mask(const uint8_t* decoded, uint8_t* cached, uint8_t* commit_out,
+                                     int32_t* block_done_out, int batch, int block,
+                                     hipStream_t stream) {
+  using namespace bte;
+  if (!decoded || !cached || !commit_out) return BTE_ERR_NULL;
+  if (batch <= 0 || block < 1 || block > 1024) return BTE_ERR_DIM;
+  hipLaunchKernelGGL(commit_mask_kernel, dim3((batch + 255) / 256), dim3(256), 0, stream, decoded,
+                     cached, commit_out, block_done_out, batch, block);
   return hipGetLastError() == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
 }

@@ -182,6 +182,26 @@ int bte_focus_select(const float* delta, const int32_t* k, const uint8_t* decode
                      int32_t* cu_out, int batch, int block, hipStream_t stream);
 
 /*
+ * Neighbour-aware delayed commit of block KV states (FOCUS paper Section
+ * 4.3; App. E.3.1, App. E.3.3; FOCUS notes page, key design 4). With
+ * `decoded` the state entering this step and `cached` the positions already
+ * committed:
+ *   commit_out[b,i] = !cached[b,i] && decoded[b,i] && right(b,i)
+ *   right(b,i) = decoded[b,i+1] for i < block-1, and for the block's last
+ *                position: every position of the block decoded
+ *   cached[b,i] |= commit_out[b,i]
+ *   block_done_out[b] = 1 if every position is now cached (the caller then
+ *                       resets the block state), else 0
+ *
+ *   decoded, cached (in/out), commit_out [batch, block] uint8;
+ *   block_done_out [batch] int32 or NULL
+ * Errors: NULL (other than block_done_out) -> BTE_ERR_NULL; batch <= 0 or
+ * block out of [1, 1024] -> BTE_ERR_DIM.
+ */
+int bte_focus_commit_mask(const uint8_t* decoded, uint8_t* cached, uint8_t* commit_out,
+                          int32_t* block_done_out, int batch, int block, hipStream_t stream);
+
+/*
  * Gather-compaction of kept rows (FOCUS paper Section 4.2: H_reduced = H at
  * the kept index set; App. E.2.3: destinations from a prefix sum):
  *   dst[cu[b] + t, :] = src[b, idx[b,t], :]   for t < count[b]
@@ -196,6 +216,33 @@ int bte_focus_select(const float* delta, const int32_t* k, const uint8_t* decode
  */
 int bte_gather_rows(const void* src, const int32_t* idx, const int32_t* count, const int32_t* cu,
                     void* dst, int batch, int n, int k_max, size_t row_bytes, hipStream_t stream);
+
+/*
+ * Several row tensors compacted with one index set in one launch (FOCUS
+ * paper App. E.2.3: hidden states, residual connections, RoPE positions and
+ * cache indices are compacted together by the prefix sum). For each tensor k
+ * and t < count[b]:
+ *   tensors[k].dst[cu[b] + t, :] = tensors[k].src[b, idx[b,t], :]
+ * Rows are opaque byte strings of tensors[k].row_bytes bytes.
+ *
+ *   tensors: host array of n_tensors descriptors (device pointers inside);
+ *   src [batch, n, row_bytes]; dst [>= cu[batch], row_bytes];
+ *   idx [batch, k_max], count [batch], cu [batch + 1] int32
+ * Limits: 1 <= n_tensors <= 8; row_bytes a multiple of 4 and < 2^32;
+ *   src/dst 4-byte aligned (16-byte rows and pointers are copied 16 bytes at
+ *   a time).
+ * Errors: NULL -> BTE_ERR_NULL; counts out of range -> BTE_ERR_DIM;
+ * alignment -> BTE_ERR_ALIGN.
+ */
+typedef struct {
+  const void* src;
+  void* dst;
+  size_t row_bytes;
+} bte_rows_tensor;
+
+int bte_gather_rows_multi(const bte_rows_tensor* tensors, int n_tensors, const int32_t* idx,
+                          const int32_t* count, const int32_t* cu, int batch, int n, int k_max,
+                          hipStream_t stream);
 
 /*
  * In-place scatter of the kept rows' new K/V into the exact KV cache

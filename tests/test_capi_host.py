@@ -25,7 +25,7 @@ def declared():
 
 def test_every_declared_symbol_is_exported():
     names = declared()
-    assert len(names) == 14
+    assert len(names) == 16
     for name in names:
         assert hasattr(lib, name), name
 
@@ -168,3 +168,21 @@ def test_paged_errors():
     assert s(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, 0, 16, FAKE, FAKE, 2, 8, 2048, None) == DIM
     assert s(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, 4, 12, FAKE, FAKE, 2, 8, 2048, None) == UNSUP
     assert s(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, 4, 16, FAKE, FAKE, 2, 0, 2048, None) == OK
+
+
+def test_commit_and_multi_errors():
+    f = lib.bte_focus_commit_mask
+    assert f(None, FAKE, FAKE, None, 4, 32, None) == NULL
+    assert f(FAKE, FAKE, FAKE, None, 0, 32, None) == DIM
+    assert f(FAKE, FAKE, FAKE, None, 4, 2000, None) == DIM
+    g = lib.bte_gather_rows_multi
+    T = bte._RowsTensor
+    ok = (T * 2)(T(1 << 20, 1 << 21, 8192), T(1 << 22, 1 << 23, 4))
+    assert g(None, 2, FAKE, FAKE, FAKE, 4, 32, 8, None) == NULL
+    assert g(ctypes.cast(ok, ctypes.c_void_p), 0, FAKE, FAKE, FAKE, 4, 32, 8, None) == DIM
+    assert g(ctypes.cast(ok, ctypes.c_void_p), 9, FAKE, FAKE, FAKE, 4, 32, 8, None) == DIM
+    bad = (T * 1)(T(1 << 20, 1 << 21, 6))
+    assert g(ctypes.cast(bad, ctypes.c_void_p), 1, FAKE, FAKE, FAKE, 4, 32, 8, None) == ALIGN
+    nul = (T * 1)(T(None, 1 << 21, 8))
+    assert g(ctypes.cast(nul, ctypes.c_void_p), 1, FAKE, FAKE, FAKE, 4, 32, 8, None) == NULL
+    assert g(ctypes.cast(ok, ctypes.c_void_p), 2, FAKE, FAKE, FAKE, 4, 32, 0, None) == OK

@@ -145,3 +145,50 @@ def test_select_on_real_deltas_with_budget():
     kk = k.cpu().numpy()
     np.testing.assert_array_equal(kk, oracle.focus_budget(d, ts, st, 1.5))
     _check_select(d, fi["decoded"].cpu().numpy().astype(bool), kk, rp, "chain")
+
+
+@pytest.mark.parametrize("block", [1, 3, 32, 64, 1000])
+def test_commit_mask(block):
+    bte = _bte()
+    r = np.random.default_rng(300 + block)
+    batch = 500
+    dec = r.random((batch, block)) < r.random((batch, 1))
+    dec[:20] = True                                           # whole blocks decoded
+    cac = dec & (r.random((batch, block)) < 0.5)
+    g_cac = _cuda(cac, torch.uint8)
+    say(f"commit mask block={block}")
+    commit, done = bte.focus_commit_mask(_cuda(dec, torch.uint8), g_cac)
+    w_commit, w_cac, w_done = oracle.commit_mask(dec, cac)
+    np.testing.assert_array_equal(commit.cpu().numpy().astype(bool), w_commit)
+    np.testing.assert_array_equal(g_cac.cpu().numpy().astype(bool), w_cac)
+    np.testing.assert_array_equal(done.cpu().numpy(), w_done)
+
+
+def test_gather_multi():
+    """Hidden rows (bf16 8 KB), residual (fp32 16 KB), RoPE positions (int32)
+    and cache indices (int64) compacted in one launch, after a constrained
+    selection, against the oracle's gather of each."""
+    bte = _bte()
+    r = np.random.default_rng(13)
+    batch, block = 300, 32
+    d, dec = _rand_delta(r, batch, block)
+    k = r.integers(0, 12, batch).astype(np.int32)
+    rp = np.full(batch, -1, np.int32)
+    idx, cnt, cu = bte.focus_select(_cuda(d, torch.float32), _cuda(k, torch.int32),
+                                    _cuda(dec, torch.uint8), _cuda(rp, torch.int32))
+    srcs = [torch.randn(batch, block, 4096, device="cuda").to(torch.bfloat16),
+            torch.randn(batch, block, 4096, device="cuda"),
+            torch.randint(0, 1 << 20, (batch, block), dtype=torch.int32, device="cuda"),
+            torch.randint(0, 1 << 40, (batch, block), dtype=torch.int64, device="cuda")]
+    say("gather multi")
+    outs = bte.gather_rows_multi(srcs, idx, cnt, cu)
+    torch.cuda.synchronize()
+    i_h, c_h, u_h = idx.cpu().numpy(), cnt.cpu().numpy(), cu.cpu().numpy()
+    total = int(u_h[-1])
+    for s_, o in zip(srcs, outs):
+        host = s_.cpu()
+        host = host.view(torch.int16) if host.dtype == torch.bfloat16 else host
+        want = oracle.gather_rows(host.numpy(), i_h, c_h, u_h)
+        got = o[:total].cpu()
+        got = got.view(torch.int16) if got.dtype == torch.bfloat16 else got
+        np.testing.assert_array_equal(got.numpy(), want)
