@@ -7,7 +7,9 @@ operations of the path, written from the pages' definitions:
   (FOCUS paper, arXiv 2601.23278: Section 3.1 Eq. 2, Section 3.2 Eq. 3,
   Section 4.2; App. E.2.1; FOCUS notes page, key design 1).
 * ``esdllm_score`` — ES-dLLM importance score (ES-dLLM notes page, key
-  design 1).
+  design 1); ``esdllm_skip_layer`` — one skip layer of its early skipping
+  (score, partial hidden-cache update, top-(1-r)|S|, survivor compaction;
+  key designs 1 and 2).
 * ``topk_select`` — per-sequence top-K of masked tokens (FOCUS paper
   Section 4.2; ES-dLLM notes page, key design 1 "top-(1-r_l)|S|").
 * ``gather_rows`` — Gather of the kept block hidden rows into H_reduced
@@ -40,7 +42,7 @@ closed forms, hand-worked examples, library routines and invariants.
 """
 from .focus import (block_scores, maxpool_keys, softmax_keys, importance,
                     focus_importance_delta)
-from .esdllm import esdllm_score
+from .esdllm import esdllm_score, esdllm_skip_layer
 from .selection import topk_select, focus_select
 from .budget import focus_budget, history_update
 from .rows import gather_rows, gather_rows_multi, kv_scatter
@@ -53,4 +55,4 @@ __all__ = ["block_scores", "maxpool_keys", "softmax_keys", "importance",
            "focus_importance_delta", "esdllm_score", "topk_select", "gather_rows",
            "kv_scatter", "reduced_attention", "attention_order", "focus_budget",
            "history_update", "focus_select", "kv_scatter_paged", "reduced_attention_paged",
-           "physical_row", "commit_mask", "gather_rows_multi"]
+           "physical_row", "commit_mask", "gather_rows_multi", "esdllm_skip_layer"]

@@ -41,3 +41,43 @@ def esdllm_score(h_new, h_prev, surv_pos, conf, alpha: float) -> np.ndarray:
                 v = l1 / (np.sqrt(hidden) * l2)
             out[b, s] = alpha * conf[b, p] + (1.0 - alpha) * v
     return out
+
+
+def esdllm_skip_layer(h_surv, h_cache, surv_pos, conf, alpha: float, keep: int, row_base=None):
+    """One skip layer of ES-dLLM's early skipping (ES-dLLM notes page, key
+    designs 1 and 2), composed of the oracle's own steps:
+
+    1. score every survivor against the layer's cached previous-iteration
+       hidden state (``esdllm_score``);
+    2. update the layer's hidden-state cache in place at every survivor's
+       position (partial cache update: skipped positions keep their state);
+    3. keep the top ``keep`` survivors by score (``topk_select``; the pages'
+       top-(1 - r_l)|S| with keep = floor((1 - r_l)|S|) passed in);
+    4. the next layer's survivors and their hidden rows are the kept ones, in
+       ascending survivor order.
+
+    h_surv [batch, n_surv, h]; h_cache [batch, L, h] (viewed as rows); surv_pos
+    [batch, n_surv]; conf [batch, L]. Returns (score, idx, count, cu, h_next
+    [sum(count), h], surv_next [sum(count)], h_cache updated copy).
+    """
+    from .selection import topk_select
+    from .rows import gather_rows, kv_scatter
+
+    h_surv = np.asarray(h_surv)
+    h_cache = np.asarray(h_cache)
+    surv_pos = np.asarray(surv_pos)
+    batch, n_surv = surv_pos.shape
+    L = h_cache.shape[1]
+    score = esdllm_score(h_surv, h_cache, surv_pos, conf, alpha)
+    ident = np.tile(np.arange(n_surv, dtype=np.int32), (batch, 1))
+    all_cnt = np.full(batch, n_surv, np.int32)
+    all_cu = np.arange(batch + 1, dtype=np.int32) * n_surv
+    rb = np.arange(batch, dtype=np.int64) * L if row_base is None else row_base
+    rows = h_surv.reshape(batch * n_surv, -1)
+    cache_rows = h_cache.reshape(batch * L, -1)
+    new_cache, _ = kv_scatter(rows, rows, ident, all_cnt, all_cu, rb, cache_rows, cache_rows,
+                              pos_map=surv_pos)
+    idx, count, cu = topk_select(score, np.full(batch, keep, np.int32), keep)
+    h_next = gather_rows(h_surv, idx, count, cu)
+    surv_next = gather_rows(surv_pos[:, :, None], idx, count, cu)[:, 0]
+    return score, idx, count, cu, h_next, surv_next, new_cache.reshape(h_cache.shape)

@@ -58,3 +58,37 @@ def test_zero_norm_cases():
     out = oracle.esdllm_score(h_new, h_prev, np.array([[0, 1]]), np.array([[0.2, 0.4]]), 0.5)
     assert out[0, 0] == 0.1          # 0/0 -> 0
     assert out[0, 1] == math.inf     # x/0 -> inf
+
+
+def test_skip_layer_survivor_invariants():
+    """Two skip layers (r = 0.5 each, as the pages' defaults at 1/8 and 1/4
+    depth): S' is a subset of S of size floor(|S| / 2) holding the top
+    scores; kept rows are the survivors' rows; the hidden cache changes only
+    at survivor positions, to the survivors' new states."""
+    r = np.random.default_rng(21)
+    batch, prompt, gen, h = 3, 10, 24, 16
+    L = prompt + gen
+    surv = np.tile(np.arange(prompt, L, dtype=np.int32), (batch, 1))
+    conf = r.random((batch, L))
+    for layer in range(2):
+        cache = r.standard_normal((batch, L, h))
+        cur = cache + r.standard_normal((batch, L, h)) * (r.random((batch, L, 1)) < 0.3)
+        h_surv = np.stack([cur[b, surv[b]] for b in range(batch)])
+        keep = surv.shape[1] // 2
+        score, idx, cnt, cu, h_next, s_next, new_cache = oracle.esdllm_skip_layer(
+            h_surv, cache, surv, conf, 0.5, keep)
+        assert np.all(cnt == keep)
+        s_next = s_next.reshape(batch, keep)
+        for b in range(batch):
+            assert set(s_next[b]) <= set(surv[b]) and np.all(np.diff(s_next[b]) > 0)
+            kept_scores = score[b, idx[b]]
+            dropped = np.delete(score[b], idx[b])
+            assert kept_scores.min() >= dropped.max()
+            np.testing.assert_array_equal(h_next[b * keep:(b + 1) * keep], h_surv[b, idx[b]])
+            changed = np.flatnonzero(np.any(new_cache[b] != cache[b], axis=1))
+            assert set(changed) <= set(surv[b])
+            np.testing.assert_array_equal(new_cache[b, surv[b]], h_surv[b])
+            other = np.setdiff1d(np.arange(L), surv[b])
+            np.testing.assert_array_equal(new_cache[b, other], cache[b, other])
+        surv = s_next
+    assert surv.shape[1] == gen // 4
