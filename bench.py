@@ -12,7 +12,8 @@ average durations from HIP events recorded on the launch stream, the
 roofline of the dominant kernel (reduced attention, HBM-bound) from its
 algorithmic bytes, and the CPU oracle timed on a bounded sample of the same
 workload. The ES-dLLM mode (score -> top-K -> gather -> scatter, batch 8) is
-timed as well and reported under "es_mode".
+timed as well and reported under "es_mode", and two ES-dLLM skip layers
+(256 -> 128 -> 64 survivors) under "es_pipeline".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -54,7 +55,7 @@ def main():
     import torch
 
     import block_token_eviction_amd as bte
-    from block_token_eviction_amd.chain import EsStep, FocusStep
+    from block_token_eviction_amd.chain import EsSkipLayer, EsStep, FocusStep
     import workloads as W
 
     dev = torch.device("cuda:0")
@@ -145,6 +146,41 @@ def main():
                "ms_per_step": round(es_ms, 4),
                "survivor positions/s": round(ec.batch * ec.generated / (es_ms * 1e-3), 1)}
 
+    # ES-dLLM skip layers (auxiliary): r = 0.5 at two layers, 256 -> 128 -> 64 survivors.
+    # Each layer's survivor states stand for the model layers before it; they are
+    # prepared outside the timed region with the library's gather.
+    px = W.es_pipeline_inputs(ec, layers=2, device=dev)
+    L = ec.prompt + ec.generated
+    sizes = [ec.generated, ec.generated // 2, ec.generated // 4]
+    skip = [EsSkipLayer(ec.batch, sizes[i], sizes[i + 1], L, ec.hidden, ec.dtype, dev) for i in range(2)]
+    arange = torch.arange(ec.batch + 1, dtype=torch.int32, device=dev)
+
+    def survivor_states(layer, surv):
+        n = surv.shape[1]
+        cnt = torch.full((ec.batch,), n, dtype=torch.int32, device=dev)
+        return bte.gather_rows(px["h_cur"][layer], surv, cnt, arange * n).view(ec.batch, n, -1)
+
+    h0 = survivor_states(0, px["surv_pos"])
+    _, s1 = skip[0].run(h0, px["h_cache"][0], px["surv_pos"], px["conf"], px["alpha"])
+    s1 = s1.clone()
+    h1 = survivor_states(1, s1)
+    torch.cuda.synchronize()
+    lev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2)]
+    lay_ms = [0.0, 0.0]
+    for _ in range(args.steps):
+        for i, (h, sv) in enumerate(((h0, px["surv_pos"]), (h1, s1))):
+            lev[i][0].record()
+            skip[i].run(h, px["h_cache"][i], sv, px["conf"], px["alpha"])
+            lev[i][1].record()
+        torch.cuda.synchronize()
+        for i in range(2):
+            lay_ms[i] += lev[i][0].elapsed_time(lev[i][1]) / args.steps
+    es_pipeline = {"workload": "esdllm_b8 skip layers (r = 0.5 at two layers: 256 -> 128 -> 64 "
+                               "survivors, hidden 4096, bf16)",
+                   "layer_ms": [round(v, 4) for v in lay_ms],
+                   "ms_per_iteration": round(sum(lay_ms), 4),
+                   "survivor positions/s": round(ec.batch * ec.generated / (sum(lay_ms) * 1e-3), 1)}
+
     if args.copy_calibration:
         src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -167,6 +203,7 @@ def main():
                    "k_range": [fc.k_lo, fc.k_hi], "prefix_range": [ac.prefix_lo, ac.prefix_hi],
                    "kept_rows": sum_k, "kv_rows": int(kv_len.sum()), "parallelism": "none (1 GPU)"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "es_mode": es_mode,
+        "es_pipeline": es_pipeline,
     }
     print(json.dumps(line), flush=True)
 

@@ -11,6 +11,13 @@ keep the top ones, gather their rows, scatter their new K/V in place):
 
     esdllm_score -> topk_select -> gather_rows -> kv_scatter
 
+ES-dLLM skip layer (the same page: at a skip layer the survivors are scored,
+the layer's hidden-state cache is updated in place at every survivor, and
+only the top (1 - r)|S| survivors go on to the next layer):
+
+    esdllm_score -> kv_scatter (hidden cache, all survivors) -> topk_select
+        -> gather_rows_multi (kept hidden rows + their positions)
+
 Every call enqueues HIP kernels on the current stream; nothing here reads
 device data back or synchronises. Per-sequence counts stay on the device, so
 the output buffers are sized by the host-side bound batch * k_max rows.
@@ -21,8 +28,8 @@ import math
 
 import torch
 
-from . import (attention_order, esdllm_score, focus_importance_delta, gather_rows, kv_scatter,
-               reduced_attention, topk_select)
+from . import (attention_order, esdllm_score, focus_importance_delta, gather_rows,
+               gather_rows_multi, kv_scatter, reduced_attention, topk_select)
 
 
 class FocusStep:
@@ -89,3 +96,38 @@ class EsStep:
         kv_scatter(new_k, new_v, self.idx, self.count, self.cu, row_base, cache_k, cache_v,
                    pos_map=surv_pos)
         return self.gathered
+
+
+class EsSkipLayer:
+    """One ES-dLLM skip layer on preallocated buffers. h_cache is the layer's
+    hidden-state cache [batch, seq_len, hidden] from the previous iteration,
+    updated in place; the kept survivors (ascending) and their hidden rows are
+    returned for the next layer."""
+
+    def __init__(self, batch: int, n_surv: int, keep: int, seq_len: int, hidden: int,
+                 dtype: torch.dtype, device):
+        self.batch, self.n_surv, self.keep, self.seq_len = batch, n_surv, keep, seq_len
+        i32 = dict(dtype=torch.int32, device=device)
+        self.score = torch.empty((batch, n_surv), dtype=torch.float32, device=device)
+        self.k = torch.full((batch,), keep, **i32)
+        self.idx = torch.empty((batch, keep), **i32)
+        self.count = torch.empty((batch,), **i32)
+        self.cu = torch.empty((batch + 1,), **i32)
+        self.h_next = torch.empty((batch * keep, hidden), dtype=dtype, device=device)
+        self.surv_next = torch.empty((batch * keep,), **i32)
+        # every survivor, for the hidden-cache update
+        self.all_idx = torch.arange(n_surv, **i32).repeat(batch, 1).contiguous()
+        self.all_count = torch.full((batch,), n_surv, **i32)
+        self.all_cu = torch.arange(batch + 1, **i32) * n_surv
+        self.row_base = torch.arange(batch, dtype=torch.int64, device=device) * seq_len
+
+    def run(self, h_surv, h_cache, surv_pos, conf, alpha: float):
+        """h_surv [batch, n_surv, hidden] this iteration's states of the survivors."""
+        b, n = self.batch, self.n_surv
+        esdllm_score(h_surv, h_cache, surv_pos, conf, alpha, out=self.score)
+        kv_scatter(h_surv.view(b * n, -1), None, self.all_idx, self.all_count, self.all_cu,
+                   self.row_base, h_cache.view(b * self.seq_len, -1), None, pos_map=surv_pos)
+        topk_select(self.score, self.k, self.keep, self.idx, self.count, self.cu)
+        gather_rows_multi([h_surv, surv_pos], self.idx, self.count, self.cu,
+                          outs=[self.h_next, self.surv_next])
+        return self.h_next.view(b, self.keep, -1), self.surv_next.view(b, self.keep)

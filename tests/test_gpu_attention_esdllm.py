@@ -169,3 +169,50 @@ def test_esdllm_fp32_and_odd_sizes():
     cfg = W.EsCfg("f32", seed=42, batch=3, prompt=5, generated=37, hidden=200, dtype=W.F32, keep=10)
     got, ref, _ = _es(cfg)
     assert_close(got, ref, "esdllm f32")
+
+
+def test_esdllm_two_skip_layers():
+    """ES-dLLM skip layers at 1/8 and 1/4 depth (r = 0.5 each) on the batch-8
+    workload: 256 -> 128 -> 64 survivors. Per layer: scores within tolerance of
+    the oracle; the selection equal to the oracle's top-K of the same fp32
+    scores; kept rows, survivor positions and the updated hidden cache bit
+    for bit."""
+    from block_token_eviction_amd.chain import EsSkipLayer
+    bte = _bte()
+    cfg = W.ES_B8
+    x = W.es_pipeline_inputs(cfg, layers=2, device="cuda")
+    L = cfg.prompt + cfg.generated
+    bits = lambda t: t.detach().cpu().view(torch.int16).numpy()
+    surv = x["surv_pos"]
+    n = surv.shape[1]
+    # this layer's survivor states, standing in for the model's layers before it
+    one = torch.arange(cfg.batch + 1, dtype=torch.int32, device="cuda")
+    for layer in range(2):
+        keep = n // 2
+        h_surv = bte.gather_rows(x["h_cur"][layer], surv, torch.full((cfg.batch,), n, dtype=torch.int32,
+                                 device="cuda"), one * n).view(cfg.batch, n, -1)
+        cache0 = bits(x["h_cache"][layer])                 # before the in-place update
+        cache0_f64 = W.to_f64(x["h_cache"][layer])
+        say(f"es skip layer {layer}: {n} -> {keep}")
+        step = EsSkipLayer(cfg.batch, n, keep, L, cfg.hidden, cfg.dtype, "cuda")
+        h_next, s_next = step.run(h_surv, x["h_cache"][layer], surv, x["conf"], x["alpha"])
+        torch.cuda.synchronize()
+        ref_score = oracle.esdllm_score(W.to_f64(h_surv), cache0_f64, surv.cpu().numpy(),
+                                        x["conf"].cpu().numpy(), x["alpha"])
+        assert_close(step.score.cpu().numpy(), ref_score, f"es score layer {layer}")
+        g_score = step.score.cpu().numpy()
+        r_idx, r_cnt, r_cu = oracle.topk_select(g_score, np.full(cfg.batch, keep), keep)
+        np.testing.assert_array_equal(step.idx.cpu().numpy(), r_idx)
+        np.testing.assert_array_equal(bits(h_next).reshape(cfg.batch * keep, -1),
+                                      oracle.gather_rows(bits(h_surv), r_idx, r_cnt, r_cu))
+        want_s = np.take_along_axis(surv.cpu().numpy(), r_idx, axis=1)
+        np.testing.assert_array_equal(s_next.cpu().numpy(), want_s)
+        rows = bits(h_surv).reshape(cfg.batch * n, -1)
+        ident = np.tile(np.arange(n, dtype=np.int32), (cfg.batch, 1))
+        want_cache, _ = oracle.kv_scatter(rows, rows, ident, np.full(cfg.batch, n, np.int32),
+                                          np.arange(cfg.batch + 1, dtype=np.int32) * n,
+                                          np.arange(cfg.batch) * L, cache0.reshape(cfg.batch * L, -1),
+                                          cache0.reshape(cfg.batch * L, -1), pos_map=surv.cpu().numpy())
+        np.testing.assert_array_equal(bits(x["h_cache"][layer]).reshape(cfg.batch * L, -1), want_cache)
+        surv, n = s_next.contiguous(), keep
+    assert n == cfg.generated // 4

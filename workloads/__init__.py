@@ -252,6 +252,35 @@ def esdllm_inputs(cfg: EsCfg, device="cpu") -> dict:
                 row_base=t(np.arange(n, dtype=np.int64) * L), alpha=cfg.alpha)
 
 
+def es_pipeline_inputs(cfg: EsCfg, layers: int = 2, device="cpu") -> dict:
+    """Inputs of ES-dLLM's skip layers (one per layer in `layers`): per layer,
+    the previous iteration's hidden states h_cache [batch, L, h] ~ N(0,1) and
+    this iteration's h_cur = h_cache + N(0, perturb_std^2) on
+    round(perturb_frac * L) positions per sequence (exact copy elsewhere);
+    one confidence c ~ Beta(0.5, 2) [batch, L]; the first skip layer's
+    survivors are every generated position. h_cur stands for the layer's
+    output, which the pages' model would compute for the survivors."""
+    n, L, h = cfg.batch, cfg.prompt + cfg.generated, cfg.hidden
+    out = {"h_cache": [], "h_cur": []}
+    m = int(math.floor(cfg.perturb_frac * L + 0.5))
+    for layer in range(layers):
+        base = normal((n, L, h), cfg.seed, 50 + 10 * layer, F32, device)
+        cur = base.clone()
+        noise = normal((n, L, h), cfg.seed, 51 + 10 * layer, F32, device, std=cfg.perturb_std)
+        rng = _np(cfg.seed, 52 + 10 * layer)
+        mask = np.zeros((n, L), bool)
+        for b in range(n):
+            mask[b, rng.choice(L, size=m, replace=False)] = True
+        mt = torch.from_numpy(mask).to(device)
+        cur[mt] += noise[mt]
+        out["h_cache"].append(base.to(cfg.dtype))
+        out["h_cur"].append(cur.to(cfg.dtype))
+    out["conf"] = torch.from_numpy(_np(cfg.seed, 59).beta(0.5, 2.0, size=(n, L)).astype(np.float32)).to(device)
+    out["surv_pos"] = torch.from_numpy(np.tile(np.arange(cfg.prompt, L, dtype=np.int32), (n, 1))).to(device)
+    out["alpha"] = cfg.alpha
+    return out
+
+
 def chain_inputs(fcfg: FocusCfg, acfg: AttnCfg, device="cpu") -> dict:
     """Inputs of one full FOCUS step: scoring inputs of `fcfg` plus the KV cache,
     capacity-sized new K/V and kept-query buffers (batch * k_hi rows) of `acfg`."""
