@@ -125,6 +125,32 @@ def main():
                 "tflops": round(flops_attn / (stage_ms[dom] * 1e-3) / 1e12, 2)}
     value = fc.batch * fc.block / (ms_step * 1e-3)
 
+    # The same step captured once in a HIP graph and replayed (no per-call
+    # launch gaps); reported beside the eager step, not as `value`.
+    graph_ms = None
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step.run(**run_args)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step.run(**run_args)
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms = round(g0.elapsed_time(g1) / args.steps, 4)
+        del graph
+    except RuntimeError as err:            # capture unsupported: report, keep the eager numbers
+        log(f"graph capture failed: {err}")
+
     # ES-dLLM mode (auxiliary): batch 8, 256 survivors, keep 128
     ec = W.ES_B8
     ei = W.esdllm_inputs(ec, device=dev)
@@ -203,7 +229,7 @@ def main():
                    "k_range": [fc.k_lo, fc.k_hi], "prefix_range": [ac.prefix_lo, ac.prefix_hi],
                    "kept_rows": sum_k, "kv_rows": int(kv_len.sum()), "parallelism": "none (1 GPU)"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "es_mode": es_mode,
-        "es_pipeline": es_pipeline,
+        "es_pipeline": es_pipeline, "graph_ms_per_step": graph_ms,
     }
     print(json.dumps(line), flush=True)
 

@@ -94,3 +94,44 @@ def test_chain_b1024_full_size_sampled():
     """The benchmarked workload itself (batch 1024, prefixes 1024..4096)."""
     sample = sorted(np.random.default_rng(9).choice(1024, size=48, replace=False).tolist())
     _check_chain(W.CHAIN_FOCUS_B1024, W.CHAIN_ATTN_B1024, sample)
+
+
+def test_focus_step_graph_replays_match_eager():
+    """A FOCUS step captured in a HIP graph and replayed three times, with eager
+    work and synchronisations in between: every replay equals the eager step
+    bit for bit (the kernels allocate nothing and record no memset nodes)."""
+    from block_token_eviction_amd.chain import FocusStep
+    fc = W.FocusCfg("graph", seed=81, batch=64)
+    ac = W.AttnCfg("graph", seed=81, batch=64, kept=None, prefix_lo=100, prefix_hi=600)
+    say("focus step under graph capture")
+    x = W.chain_inputs(fc, ac, device="cuda")
+    step = FocusStep(fc.batch, fc.block, fc.hidden, fc.hq, fc.head_dim, fc.k_hi, fc.dtype, "cuda")
+    args = {k: x[k] for k in ("q0", "k0", "q1", "k1", "decoded", "k", "hidden_rows", "pool_kernel",
+                              "new_k", "new_v", "q_kept", "cache_k", "cache_v", "seq_start",
+                              "kv_len", "row_base")}
+    cache0 = (x["cache_k"].clone(), x["cache_v"].clone())
+    step.run(**args)
+    torch.cuda.synchronize()
+    n = int(step.cu[-1])                                   # rows the step writes
+    want = [t.clone() for t in (step.delta, step.idx, step.count, step.cu, step.gathered[:n],
+                                step.out[:n], x["cache_k"], x["cache_v"])]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                              # warm-up on the capture stream
+        step.run(**args)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step.run(**args)
+    for rep in range(3):
+        x["cache_k"].copy_(cache0[0])                      # eager work between replays
+        x["cache_v"].copy_(cache0[1])
+        step.out.zero_()
+        step.gathered.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (step.delta, step.idx, step.count, step.cu, step.gathered[:n], step.out[:n],
+               x["cache_k"], x["cache_v"])
+        for a, b in zip(got, want):
+            assert torch.equal(a, b), f"replay {rep}"
