@@ -49,7 +49,9 @@ struct Cfg {
   static constexpr int kTile = 32 * kRowBytes;        // LDS bytes of one K or V tile
   static constexpr int kOStride = D + 1;              // floats per row of the merge buffer
   static constexpr int kMerge = kWaves * 32 * kOStride * 4 + 2 * kWaves * 32 * 4;
-  // LDS stages per wave (K + V tile each): two when all waves' stages fit in 128 KB.
+  // LDS stages per wave (K + V tile each): two when all waves' stages fit in
+  // 128 KB. (Three or four stages at one wave per workgroup measured slower:
+  // the larger LDS share leaves fewer workgroups per CU.)
   static constexpr int kStages = kWaves * 2 * 2 * kTile <= 128 * 1024 ? 2 : 1;
   static constexpr int kStageBytes = 2 * kTile;
   static constexpr int kStage = kWaves * kStages * kStageBytes;
@@ -117,6 +119,22 @@ struct KvMap {
   int max_pages;
   int lg_page;
 };
+
+// Waits until at most `behind` tiles of kPerTile copies each are still in
+// flight (s_waitcnt needs an immediate; behind <= kMax).
+template <int kMax, int kPerTile>
+__device__ __forceinline__ void wait_copies_behind(int behind) {
+  static_assert(kMax * kPerTile <= 63, "vmcnt holds at most 63");
+  if (kMax >= 3 && behind >= 3) {
+    __builtin_amdgcn_s_waitcnt(kVmcntNoLgkm | vmcnt_bits(kMax >= 3 ? 3 * kPerTile : 0));
+  } else if (kMax >= 2 && behind >= 2) {
+    __builtin_amdgcn_s_waitcnt(kVmcntNoLgkm | vmcnt_bits(kMax >= 2 ? 2 * kPerTile : 0));
+  } else if (kMax >= 1 && behind >= 1) {
+    __builtin_amdgcn_s_waitcnt(kVmcntNoLgkm | vmcnt_bits(kPerTile));
+  } else {
+    __builtin_amdgcn_s_waitcnt(kVmcntNoLgkm | vmcnt_bits(0));
+  }
+}
 
 // KV layouts: contiguous; paged with the sequence's page-table row staged in
 // LDS at workgroup start (a page lookup is then an LDS read); paged with
@@ -239,17 +257,16 @@ __device__ __forceinline__ void attn_body(
     return row * C::kRowBytes + (vpos(row, byte >> 4) << 4) + (byte & 15);
   };
 
-  if (w < ntiles) issue_tile(w, 0);
-  if (C::kStages == 2 && w + kWaves < ntiles) issue_tile(w + kWaves, 1);
-  int it = 0;
-  for (int kt = w; kt < ntiles; kt += kWaves, ++it) {
-    const int stage = C::kStages == 2 ? (it & 1) : 0;
-    // Wait for this tile's loads; the next tile's (2 * kHalf loads) may stay in flight.
-    if (C::kStages == 2 && kt + kWaves < ntiles) {
-      __builtin_amdgcn_s_waitcnt(kVmcntNoLgkm | vmcnt_bits(2 * C::kHalf));
-    } else {
-      __builtin_amdgcn_s_waitcnt(kVmcntNoLgkm | vmcnt_bits(0));
-    }
+  // Prologue: this wave's first kStages tiles, one per stage.
+#pragma unroll
+  for (int st = 0; st < C::kStages; ++st)
+    if (w + st * kWaves < ntiles) issue_tile(w + st * kWaves, st);
+  int stage = 0;
+  for (int kt = w; kt < ntiles; kt += kWaves) {
+    // Wait for this tile's copies; those of the wave's later tiles already
+    // issued (up to kStages - 1 tiles of 2 * kHalf copies) may stay in flight.
+    const int later = min(C::kStages - 1, (ntiles - 1 - kt) / kWaves);
+    wait_copies_behind<C::kStages - 1, 2 * C::kHalf>(later);
     __builtin_amdgcn_wave_barrier();
     const char* kt_lds = wave_lds + stage * C::kStageBytes;
     const char* vt_lds = kt_lds + C::kTile;
@@ -371,6 +388,7 @@ __device__ __forceinline__ void attn_body(
     __builtin_amdgcn_wave_barrier();
     // The V half is consumed too: refill it.
     if (refill < ntiles) issue_half(refill, stage, 1);
+    stage = stage + 1 == C::kStages ? 0 : stage + 1;
   }
 
   // Merge the 4 wave states: out = sum_w e^(m_w - M) O_w / sum_w e^(m_w - M) l_w.
