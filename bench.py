@@ -12,8 +12,11 @@ average durations from HIP events recorded on the launch stream, the
 roofline of the dominant kernel (reduced attention, HBM-bound) from its
 algorithmic bytes, and the CPU oracle timed on a bounded sample of the same
 workload. The ES-dLLM mode (score -> top-K -> gather -> scatter, batch 8) is
-timed as well and reported under "es_mode", and two ES-dLLM skip layers
-(256 -> 128 -> 64 survivors) under "es_pipeline".
+timed as well and reported under "es_mode", two ES-dLLM skip layers
+(256 -> 128 -> 64 survivors) under "es_pipeline", and the extended FOCUS step
+(device budget, constrained selection, one compaction launch for four
+per-token tensors, paged KV pool, delayed commit mask, history update) on the
+same batch-1024 workload under "full_step".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -30,6 +33,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+ALPHA = 1.5                    # FOCUS budget multiplier of the pages' worked example
+PAGE = 64                      # KV pool page size (rows) of the extended step
 METRIC = "block tokens/s through score→top-K→gather→reduced attn; % of HBM/MFMA roofline"
 
 
@@ -93,6 +98,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
+    step_ms = sorted(ev[s][0][0].elapsed_time(ev[s][-1][1]) for s in range(args.steps))
     stage_ms = {name: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
                 for i, (name, _) in enumerate(stages)}
 
@@ -124,6 +130,9 @@ def main():
                 "algo_bytes_per_launch": int(bytes_[dom]),
                 "tflops": round(flops_attn / (stage_ms[dom] * 1e-3) / 1e12, 2)}
     value = fc.batch * fc.block / (ms_step * 1e-3)
+    copy_gbs = copy_bandwidth(dev)
+    roofline["copy_GBps"] = round(copy_gbs, 1)
+    roofline["frac_of_copy"] = round(achieved / copy_gbs, 4)
 
     # The same step captured once in a HIP graph and replayed (no per-call
     # launch gaps); reported beside the eager step, not as `value`.
@@ -207,6 +216,8 @@ def main():
                    "ms_per_iteration": round(sum(lay_ms), 4),
                    "survivor positions/s": round(ec.batch * ec.generated / (sum(lay_ms) * 1e-3), 1)}
 
+    full = full_step_leg(x, fc, ac, args.steps, args.warmup, dev)
+
     if args.copy_calibration:
         src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -230,11 +241,124 @@ def main():
                    "kept_rows": sum_k, "kv_rows": int(kv_len.sum()), "parallelism": "none (1 GPU)"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "es_mode": es_mode,
         "es_pipeline": es_pipeline, "graph_ms_per_step": graph_ms,
+        "step_ms_p10_p50_p90": [round(percentile(step_ms, q), 4) for q in (10, 50, 90)],
+        "full_step": full,
     }
     print(json.dumps(line), flush=True)
 
 
 COPY_CAL_BYTES = 256 << 20
+
+
+def percentile(sorted_vals, q):
+    """Nearest-rank percentile of an ascending list."""
+    i = max(0, min(len(sorted_vals) - 1, math.ceil(q / 100 * len(sorted_vals)) - 1))
+    return sorted_vals[i]
+
+
+def copy_bandwidth(dev, nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """Device-to-device copy rate (read + write bytes per second, GB/s): the
+    measured second reference for the roofline fraction."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    return gbs
+
+
+def full_step_leg(x, fc, ac, steps: int, warmup: int, dev):
+    """The extended FOCUS step on the batch-1024 workload: per-kernel average
+    durations from HIP events on the launch stream, and the step time from the
+    first kernel's start to the last one's end. The per-sequence state that the
+    step updates in place (history, rightmost processed position, cached
+    mask) is restored after each step, outside the events, so that every
+    timed step starts from the same state."""
+    import numpy as np
+    import torch
+
+    from block_token_eviction_amd.chain import FocusFullStep
+    import workloads as W
+
+    log("extended step: generating the paged pool and decode state")
+    y = W.focus_full_inputs(fc, ac, page_size=PAGE, device=dev, base=x)
+    per_token = [y["hidden_rows"], y["residual"], y["rope_pos"], y["cache_idx"]]
+    st = FocusFullStep(fc.batch, fc.block, fc.hq, fc.head_dim,
+                       [(t.shape[2:], t.dtype) for t in per_token], fc.dtype, dev)
+    state = [y[k] for k in ("token_sum", "total_steps", "rightmost_processed", "cached")]
+    saved = [t.clone() for t in state]
+    stages = [
+        ("focus_importance_delta", lambda: st.score(y["q0"], y["k0"], y["q1"], y["k1"], y["decoded"], fc.pool_kernel)),
+        ("focus_budget", lambda: st.budget(y["token_sum"], y["total_steps"], ALPHA)),
+        ("focus_select", lambda: st.select(y["decoded"], y["rightmost_processed"])),
+        ("gather_rows_multi", lambda: st.compact(per_token)),
+        ("kv_scatter_paged", lambda: st.scatter(y["new_k_full"], y["new_v_full"], y["pos_base"], y["block_table"], PAGE, y["pool_k"], y["pool_v"])),
+        ("attention_order", lambda: st.schedule(y["kv_len"])),
+        ("reduced_attention_paged", lambda: st.attend(y["q_full"], y["pool_k"], y["pool_v"], y["block_table"], PAGE, y["kv_len"])),
+        ("focus_commit_mask", lambda: st.commit_mask(y["decoded"], y["cached"])),
+        ("focus_history_update", lambda: st.history(y["decoded"], y["decoded_now"], y["token_sum"], y["total_steps"])),
+    ]
+
+    def restore():
+        for t, t0 in zip(state, saved):
+            t.copy_(t0)
+
+    for _ in range(warmup):
+        for _, fn in stages:
+            fn()
+        restore()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in stages] for _ in range(steps)]
+    log(f"extended step: timing {steps} steps")
+    for s in range(steps):
+        for i, (_, fn) in enumerate(stages):
+            ev[s][i][0].record()
+            fn()
+            ev[s][i][1].record()
+        restore()
+    torch.cuda.synchronize()
+    stage_ms = {name: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)]))
+                for i, (name, _) in enumerate(stages)}
+    step_ms = sorted(ev[s][0][0].elapsed_time(ev[s][-1][1]) for s in range(steps))
+
+    count = st.count.cpu().numpy().astype(np.int64)
+    n_sel = int(count.sum())
+    kv_len = y["kv_len"].cpu().numpy().astype(np.int64)
+    n, B, H = fc.batch, fc.block, fc.hidden
+    hq, hkv, D, es = fc.hq, fc.hkv, fc.head_dim, 2
+    pages = int(((kv_len + PAGE - 1) // PAGE).sum())
+    bytes_ = {
+        "focus_importance_delta": 2 * n * B * (hq + hkv) * D * es + n * B * (1 + 4),
+        "focus_budget": n * (B * 4 + 12),
+        "focus_select": n * (B * 4 + 4 + B + 8 + B * 4 + 4) + (n + 1) * 4,
+        "gather_rows_multi": 2 * n_sel * (H * 2 + H * 4 + 4 + 8),
+        "kv_scatter_paged": 2 * 2 * n_sel * hkv * D * es,
+        "attention_order": 2 * n * 4,
+        "reduced_attention_paged": int(kv_len.sum()) * hkv * D * es * 2 + 2 * n_sel * hq * D * es
+                                   + pages * 4,
+        "focus_commit_mask": n * (4 * B + 4),
+        "focus_history_update": n * (2 * B + 16),
+    }
+    kernels = {k: {"ms": round(stage_ms[k], 4), "algo_bytes": int(bytes_[k]),
+                   "GB/s": round(bytes_[k] / (stage_ms[k] * 1e-3) / 1e9, 1),
+                   "hbm_frac": round(bytes_[k] / (stage_ms[k] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+               for k in stage_ms}
+    med = percentile(step_ms, 50)
+    return {"workload": f"chain_b1024 extended (alpha {ALPHA}, pages of {PAGE} rows, shuffled pool; "
+                        "decode state drawn per sequence)",
+            "ms_per_step_p10_p50_p90": [round(percentile(step_ms, q), 4) for q in (10, 50, 90)],
+            "block tokens/s": round(n * B / (med * 1e-3), 1),
+            "selected_rows": n_sel, "mean_selected": round(n_sel / n, 2),
+            "kernels": kernels}
 KERNEL_SOURCES = {"reduced_attention": ["reduced_attention.hip", "bte_device.h"],
                   "focus_importance_delta": ["focus_delta.hip", "bte_device.h"]}
 

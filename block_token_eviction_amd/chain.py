@@ -6,6 +6,15 @@ layer, the KV scatter and the reduced-query attention):
 
     focus_importance_delta -> topk_select -> gather_rows -> kv_scatter -> reduced_attention
 
+Extended FOCUS step (FOCUS paper Section 4.1 budget, Section 4.2 selection
+with its structural constraints, Section 4.3 delayed commit; App. E.2.2 to
+E.3.1 for the fused selection, the one-launch compaction, the paged pool
+and the per-sequence history):
+
+    focus_importance_delta -> focus_budget -> focus_select -> gather_rows_multi
+        -> kv_scatter_paged -> attention_order -> reduced_attention_paged
+        -> focus_commit_mask -> focus_history_update
+
 ES-dLLM mode (ES-dLLM notes page, key designs 1 and 2: score the survivors,
 keep the top ones, gather their rows, scatter their new K/V in place):
 
@@ -28,8 +37,10 @@ import math
 
 import torch
 
-from . import (attention_order, esdllm_score, focus_importance_delta, gather_rows,
-               gather_rows_multi, kv_scatter, reduced_attention, topk_select)
+from . import (attention_order, esdllm_score, focus_budget, focus_commit_mask,
+               focus_history_update, focus_importance_delta, focus_select, gather_rows,
+               gather_rows_multi, kv_scatter, kv_scatter_paged, reduced_attention,
+               reduced_attention_paged, topk_select)
 
 
 class FocusStep:
@@ -75,6 +86,78 @@ class FocusStep:
         self.scatter(new_k, new_v, row_base, cache_k, cache_v)
         self.schedule(kv_len)
         self.attend(q_kept, cache_k, cache_v, seq_start, kv_len)
+        return self.out
+
+
+class FocusFullStep:
+    """The FOCUS step with the device-side budget and history, the constrained
+    selection (|S| up to B rows per sequence), one compaction launch for the
+    per-token tensors, a paged KV pool and the delayed commit mask. The
+    per-sequence state (token_sum, total_steps, rightmost_processed, cached)
+    is the caller's and is updated in place."""
+
+    def __init__(self, batch: int, block: int, hq: int, head_dim: int, row_shapes, dtype: torch.dtype,
+                 device):
+        """row_shapes: (shape of one row, dtype) of each per-token tensor to compact."""
+        self.batch, self.block = batch, block
+        self.scale = 1.0 / math.sqrt(head_dim)
+        i32 = dict(dtype=torch.int32, device=device)
+        cap = batch * block
+        self.delta = torch.empty((batch, block), dtype=torch.float32, device=device)
+        self.k = torch.empty((batch,), **i32)
+        self.idx = torch.empty((batch, block), **i32)
+        self.count = torch.empty((batch,), **i32)
+        self.cu = torch.empty((batch + 1,), **i32)
+        self.rows = [torch.empty((cap,) + tuple(shape), dtype=dt, device=device)
+                     for shape, dt in row_shapes]
+        self.order = torch.empty((batch,), **i32)
+        self.out = torch.empty((cap, hq, head_dim), dtype=dtype, device=device)
+        self.commit = torch.empty((batch, block), dtype=torch.uint8, device=device)
+        self.block_done = torch.empty((batch,), **i32)
+
+    def score(self, q0, k0, q1, k1, decoded, pool_kernel):
+        return focus_importance_delta(q0, k0, q1, k1, decoded, pool_kernel, out=self.delta)
+
+    def budget(self, token_sum, total_steps, alpha, threshold_mode=0):
+        return focus_budget(self.delta, token_sum, total_steps, alpha, threshold_mode, out=self.k)
+
+    def select(self, decoded, rightmost_processed):
+        return focus_select(self.delta, self.k, decoded, rightmost_processed, self.idx, self.count,
+                            self.cu)
+
+    def compact(self, per_token):
+        return gather_rows_multi(per_token, self.idx, self.count, self.cu, outs=self.rows)
+
+    def scatter(self, new_k, new_v, pos_base, block_table, page_size, pool_k, pool_v):
+        return kv_scatter_paged(new_k, new_v, self.idx, self.count, self.cu, pos_base, block_table,
+                                page_size, pool_k, pool_v)
+
+    def schedule(self, kv_len):
+        return attention_order(kv_len, out=self.order)
+
+    def attend(self, q_kept, pool_k, pool_v, block_table, page_size, kv_len):
+        return reduced_attention_paged(q_kept, self.count, self.cu, pool_k, pool_v, block_table,
+                                       page_size, kv_len, self.block, self.scale, out=self.out,
+                                       order=self.order)
+
+    def commit_mask(self, decoded, cached):
+        return focus_commit_mask(decoded, cached, self.commit, self.block_done)
+
+    def history(self, decoded, decoded_now, token_sum, total_steps):
+        return focus_history_update(decoded, decoded_now, token_sum, total_steps)
+
+    def run(self, *, q0, k0, q1, k1, decoded, decoded_now, pool_kernel, alpha, token_sum,
+            total_steps, rightmost_processed, cached, per_token, new_k, new_v, q_kept, pos_base,
+            block_table, page_size, pool_k, pool_v, kv_len, threshold_mode=0):
+        self.score(q0, k0, q1, k1, decoded, pool_kernel)
+        self.budget(token_sum, total_steps, alpha, threshold_mode)
+        self.select(decoded, rightmost_processed)
+        self.compact(per_token)
+        self.scatter(new_k, new_v, pos_base, block_table, page_size, pool_k, pool_v)
+        self.schedule(kv_len)
+        self.attend(q_kept, pool_k, pool_v, block_table, page_size, kv_len)
+        self.commit_mask(decoded, cached)
+        self.history(decoded, decoded_now, token_sum, total_steps)
         return self.out
 
 

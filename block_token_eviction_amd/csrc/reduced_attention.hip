@@ -215,17 +215,34 @@ __device__ __forceinline__ void attn_body(
   const int lrow = lane / C::kChunks;
   const int lslot = lane % C::kChunks;
   const uint32_t lane_row_off = (uint32_t)(lrow * kv_row);
-  // Copies the K (which = 0) or V (which = 1) half of key tile kt into `stage`.
-  // A full tile's copies each cover kRpi consecutive rows that share one page
-  // (pages hold a multiple of kRpi rows), so each copy has a wave-uniform base.
-  auto issue_half = [&](int kt, int stage, int which) {
+  // A full tile inside one page (contiguous cache, or pages of at least 32
+  // rows, since tiles start at multiples of 32) is 32 consecutive cache rows
+  // from the row of its first position: one page lookup serves all its copies,
+  // K and V. Smaller pages take one lookup per copy.
+  const bool tile_in_page = kPaged == kContig || map.lg_page >= 5;
+  auto tile_row = [&](int kt) -> size_t {
+    if constexpr (kPaged == kContig) {
+      return (size_t)kt * 32;
+    } else {
+      const int p = kt * 32;
+      const int lg = map.lg_page;
+      const int page = __builtin_amdgcn_readfirstlane(kPaged == kPagedLds ? pages[p >> lg] : bt[p >> lg]);
+      return ((size_t)page << lg) + (size_t)(p & ((1 << lg) - 1));
+    }
+  };
+  // Copies the K (which = 0) or V (which = 1) half of key tile kt into `stage`;
+  // trow = tile_row(kt) when tile_in_page. A full tile's copies each cover kRpi
+  // consecutive rows that share one page (pages hold a multiple of kRpi rows),
+  // so each copy has a wave-uniform base.
+  auto issue_half = [&](int kt, int stage, int which, size_t trow) {
     char* dst = wave_lds + stage * C::kStageBytes + which * C::kTile;
     const char* base = which ? vbase : kbase;
     if (kt * 32 + 32 <= L) {
 #pragma unroll
       for (int i = 0; i < C::kHalf; ++i) {
         const int row = C::kRpi * i + lrow;
-        const size_t row_base = kv_pos_row(kt * 32 + C::kRpi * i) * kv_row;   // wave-uniform
+        const size_t first = tile_in_page ? trow + C::kRpi * i : kv_pos_row(kt * 32 + C::kRpi * i);
+        const size_t row_base = first * kv_row;                            // wave-uniform
         const int chunk = which ? vpos(row, lslot) : kpos(row, lslot);
         copy16_to_lds(base + row_base + (lane_row_off + 16 * chunk), dst + 1024 * i);
       }
@@ -243,8 +260,9 @@ __device__ __forceinline__ void attn_body(
     }
   };
   auto issue_tile = [&](int kt, int stage) {
-    issue_half(kt, stage, 0);
-    issue_half(kt, stage, 1);
+    const size_t trow = tile_in_page ? tile_row(kt) : 0;
+    issue_half(kt, stage, 0, trow);
+    issue_half(kt, stage, 1, trow);
   };
 
   // Lane part of the V^T transposing reads: k-slot (h, t) of P.V MFMA cc is
@@ -294,9 +312,11 @@ __device__ __forceinline__ void attn_body(
     // The K half of the stage is consumed: refill it with tile kt + kStages*kWaves
     // now (the V half follows after P.V), once the operand reads have landed.
     const int refill = kt + C::kStages * kWaves;
+    size_t refill_row = 0;
     if (refill < ntiles) {
       __builtin_amdgcn_s_waitcnt(kLgkm0);
-      issue_half(refill, stage, 0);
+      refill_row = tile_in_page ? tile_row(refill) : 0;
+      issue_half(refill, stage, 0, refill_row);
     }
 
     // V^T operands, shared by the query tiles: k-slot (h, t) of MFMA cc is key
@@ -387,7 +407,7 @@ __device__ __forceinline__ void attn_body(
     }
     __builtin_amdgcn_wave_barrier();
     // The V half is consumed too: refill it.
-    if (refill < ntiles) issue_half(refill, stage, 1);
+    if (refill < ntiles) issue_half(refill, stage, 1, refill_row);
     stage = stage + 1 == C::kStages ? 0 : stage + 1;
   }
 
@@ -461,10 +481,15 @@ __device__ __forceinline__ void attn_body(
 }
 
 // Workgroup x runs on XCD x % 8 (MI355X dispatches workgroups round-robin over
-// its 8 XCDs). The mapping below puts all KV heads (and row groups) of one
-// sequence on one XCD, one after another, so the 256-byte head slices of each
-// cache row are fetched together; sequences go round-robin over the XCDs in
-// the given order.
+// its 8 XCDs). The mapping below puts all KV heads of one sequence on one XCD,
+// one after another, so the 256-byte head slices of each cache row are fetched
+// together; sequences go round-robin over the XCDs in the given order. The
+// query row group is the slowest grid dimension: every sequence's first row
+// group comes first, in that order, then the second ones, and so on. Row
+// groups past a sequence's kept rows exit at once; grouped at the end of the
+// grid they cost little, while interleaved with real work at a period of 2 or
+// 4 they line up with the dispatcher's round-robin inside an XCD and leave
+// part of its CUs without real work (measured: 43 % slower at two row groups).
 constexpr int kXcds = 8;
 
 template <int D, bool BF16, int T, int kWaves, int kPaged>
@@ -472,17 +497,17 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T =
     const char* __restrict__ q, const int32_t* __restrict__ count, const int32_t* __restrict__ cu,
     const char* __restrict__ cache_k, const char* __restrict__ cache_v, KvMap map,
     const int32_t* __restrict__ kv_len, const int32_t* __restrict__ order, char* __restrict__ out,
-    int batch, int hq, int hkv, int n_rg, float c) {
+    int batch, int hq, int hkv, float c) {
   __shared__ __attribute__((aligned(16))) char smem[Cfg<D, BF16, kWaves>::kLds];
   __shared__ int32_t pages[kPaged == kPagedLds ? kPageCache : 1];
-  const int per_seq = hkv * n_rg;                      // workgroups per sequence
-  const int slot = blockIdx.x / kXcds;
-  const int grp = slot / per_seq;
-  const int r = kXcds * grp + (int)(blockIdx.x % kXcds);  // position in the processing order
+  const int per_rg = (batch + kXcds - 1) / kXcds * kXcds * hkv;   // workgroups per row group
+  const int rg = blockIdx.x / per_rg;
+  const int x = blockIdx.x - rg * per_rg;
+  const int slot = x / kXcds;
+  const int grp = slot / hkv;
+  const int r = kXcds * grp + x % kXcds;               // position in the processing order
   if (r >= batch) return;
-  const int j = slot - grp * per_seq;
-  const int g = j / n_rg;
-  const int rg = j - g * n_rg;
+  const int g = slot - grp * hkv;
   // Workgroups start in index order, so taking the sequences in the caller's
   // order (longest first) keeps long items out of the tail. An entry outside
   // [0, batch) is clamped: a bad order gives wrong results, never a stray access.
@@ -528,7 +553,7 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((attn_kernel<D, BF16, T, kWaves, kPaged>), dim3((unsigned)grid),
                      dim3(64 * kWaves), 0, stream, (const char*)a.q, a.count, a.cu,
                      (const char*)a.ck, (const char*)a.cv, a.map, a.kl, a.order, (char*)a.out,
-                     a.batch, a.hq, a.hkv, (int)n_rg, a.c);
+                     a.batch, a.hq, a.hkv, a.c);
   return hipGetLastError();
 }
 

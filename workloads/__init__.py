@@ -292,3 +292,79 @@ def chain_inputs(fcfg: FocusCfg, acfg: AttnCfg, device="cpu") -> dict:
                 new_k=ai["new_k"], new_v=ai["new_v"], q_kept=ai["q"], cache_k=ai["cache_k"],
                 cache_v=ai["cache_v"], seq_start=ai["seq_start"], kv_len=ai["kv_len"],
                 row_base=ai["row_base"], prefix=ai["prefix"], rows=ai["rows"])
+
+
+def page_table(kv_len, page_size: int, seed: int, spare: int = 0):
+    """A shuffled page pool for sequences of kv_len rows: block_table int32
+    [batch, max_pages] (sequence b's logical page p lives in pool page
+    block_table[b, p]; -1 past its last page) and the pool's page count.
+    Pages are handed out in a random permutation of the pool, so the pages
+    of one sequence are scattered over it."""
+    kv_len = np.asarray(kv_len, np.int64)
+    need = (kv_len + page_size - 1) // page_size
+    n_pages = int(need.sum()) + spare
+    perm = _np(seed, 70).permutation(n_pages).astype(np.int32)
+    bt = np.full((kv_len.size, int(need.max())), -1, np.int32)
+    at = 0
+    for b in range(kv_len.size):
+        bt[b, :need[b]] = perm[at:at + need[b]]
+        at += int(need[b])
+    return bt, n_pages
+
+
+def focus_full_inputs(fcfg: FocusCfg, acfg: AttnCfg, page_size: int = 64, device="cpu",
+                      base: dict | None = None) -> dict:
+    """Inputs of the extended FOCUS step (device budget, constrained selection,
+    multi-tensor compaction, paged KV pool, delayed commit, history update), on
+    top of `chain_inputs` (passed as `base` or drawn here).
+
+    Per-sequence decode state, drawn once:
+      total_steps ~ U{0..30}; token_sum ~ U{2 total_steps .. 4 total_steps}
+        (2-4 tokens per past step);
+      rightmost_processed ~ U{-1..B-1};
+      cached = decoded AND Bernoulli(0.5);
+      decoded_now = decoded plus U{2..4} of the masked positions (all of them
+        if fewer are masked): the tokens this step decodes.
+    Per-token tensors compacted with the kept rows: the hidden rows of
+    `chain_inputs`, an fp32 residual [batch, B, hidden] ~ N(0,1), RoPE
+    positions P_b + j (int32) and cache row indices seq_start[b] + P_b + j
+    (int64). Capacity buffers hold batch * B rows (|S| can reach B). The KV
+    pool is `page_table`'s shuffled pages of `page_size` rows, K/V ~ N(0,1).
+    """
+    x = chain_inputs(fcfg, acfg, device) if base is None else base
+    n, B, H = fcfg.batch, fcfg.block, fcfg.hidden
+    hq, hkv, D = acfg.hq, acfg.hkv, acfg.head_dim
+    seed = fcfg.seed
+    rng = _np(seed, 60)
+    steps = rng.integers(0, 31, size=n).astype(np.int64)
+    token_sum = np.array([rng.integers(2 * s, 4 * s + 1) for s in steps], np.int64)
+    rp = rng.integers(-1, B, size=n).astype(np.int32)
+    dec = x["decoded"].cpu().numpy().astype(bool)
+    cached = dec & (rng.uniform(size=(n, B)) < 0.5)
+    now = dec.copy()
+    rng2 = _np(seed, 61)
+    for b in range(n):
+        masked = np.flatnonzero(~dec[b])
+        m = min(masked.size, int(rng2.integers(2, 5)))
+        if m:
+            now[b, rng2.choice(masked, size=m, replace=False)] = True
+    prefix = x["prefix"].cpu().numpy().astype(np.int64)
+    seq_start = x["seq_start"].cpu().numpy().astype(np.int64)
+    j = np.arange(B, dtype=np.int64)
+    rope_pos = (prefix[:, None] + j[None, :]).astype(np.int32)
+    cache_idx = (seq_start + prefix)[:, None] + j[None, :]
+    bt, n_pages = page_table(x["kv_len"].cpu().numpy(), page_size, seed, spare=3)
+    cap = n * B
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    return dict(
+        x, decoded_now=t(now.astype(np.uint8)), token_sum=t(token_sum.astype(np.int32)),
+        total_steps=t(steps.astype(np.int32)), rightmost_processed=t(rp),
+        cached=t(cached.astype(np.uint8)),
+        residual=normal((n, B, H), seed, 62, F32, device), rope_pos=t(rope_pos),
+        cache_idx=t(cache_idx), pos_base=t(prefix.astype(np.int32)),
+        new_k_full=normal((cap, hkv, D), seed, 63, acfg.dtype, device),
+        new_v_full=normal((cap, hkv, D), seed, 64, acfg.dtype, device),
+        q_full=normal((cap, hq, D), seed, 65, acfg.dtype, device),
+        block_table=t(bt), page_size=page_size,
+        pool_k=normal((n_pages * page_size, hkv, D), seed, 66, acfg.dtype, device),
+        pool_v=normal((n_pages * page_size, hkv, D), seed, 67, acfg.dtype, device))
