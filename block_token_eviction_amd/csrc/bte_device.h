@@ -14,6 +14,22 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
+// MI355X has 8 XCDs, each with its own L2; workgroup x of a grid is dispatched
+// to XCD x % 8.
+constexpr int kXcds = 8;
+
+// XCD-grouped work mapping: a grid of ceil(batch / 8) * 8 * per workgroups,
+// where workgroup i takes part s < per of sequence b. All parts of sequence b
+// run on XCD b % 8, one after another in part order, and every XCD gets every
+// eighth sequence. Returns false for the padding past the last sequence.
+__device__ __forceinline__ bool xcd_seq_part(int batch, int per, int& b, int& s) {
+  const int i = (int)blockIdx.x;
+  const int grp = i / (kXcds * per);
+  const int j = i - grp * kXcds * per;
+  s = j / kXcds;
+  b = kXcds * grp + (j - s * kXcds);
+  return b < batch;
+}
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {

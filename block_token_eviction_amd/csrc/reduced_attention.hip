@@ -490,7 +490,6 @@ __device__ __forceinline__ void attn_body(
 // grid they cost little, while interleaved with real work at a period of 2 or
 // 4 they line up with the dispatcher's round-robin inside an XCD and leave
 // part of its CUs without real work (measured: 43 % slower at two row groups).
-constexpr int kXcds = 8;
 
 template <int D, bool BF16, int T, int kWaves, int kPaged>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T == 1 ? 2 : 1))) void attn_kernel(

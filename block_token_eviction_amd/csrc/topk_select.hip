@@ -115,73 +115,101 @@ __global__ __launch_bounds__(1024) void exclusive_scan_kernel(const int32_t* __r
 // ---------------------------------------------------------------------------
 // FOCUS dynamic budget (FOCUS notes page, key design 2; FOCUS paper Section
 // 4.1 and App. E.3.2):  K = min(B, max(ceil(alpha * N_bar), N_sigma)).
-// One thread per sequence; the integer-deciding arithmetic is float64 with a
-// fixed ascending summation order and no contraction, so the result is the
-// same on every run and matches a plain float64 evaluation of the same steps.
-// N_sigma counts masked positions (finite delta) with delta >= sigma (mode 0:
-// tested exactly as delta >= 0 and delta^2 >= variance) or delta > mu + sigma
-// (mode 1, App. E.2.2: d = delta - mu > 0 and d^2 > variance); mu and the
-// variance are the population ones over the masked positions.
-__global__ __launch_bounds__(256) void focus_budget_kernel(
+// One wave per sequence; lanes load the block positions 64 at a time. The
+// integer-deciding arithmetic is float64 with no contraction and the sums run
+// over the positions in ascending order (each value taken from its lane in a
+// wave-uniform loop), so the result is the same on every run and matches a
+// plain float64 evaluation of the same steps. N_sigma counts masked positions
+// (finite delta) with delta >= sigma (mode 0: tested exactly as delta >= 0 and
+// delta^2 >= variance) or delta > mu + sigma (mode 1, App. E.2.2:
+// d = delta - mu > 0 and d^2 > variance); mu and the variance are the
+// population ones over the masked positions.
+constexpr int kSeqPerBlock = 4;                 // sequences (waves) per workgroup
+
+__device__ __forceinline__ float lane_value(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+__global__ __launch_bounds__(64 * kSeqPerBlock) void focus_budget_kernel(
     const float* __restrict__ delta, const int32_t* __restrict__ token_sum,
     const int32_t* __restrict__ total_steps, double alpha, int mode, int32_t* __restrict__ k_out,
     int batch, int B) {
 #pragma clang fp contract(off)
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= batch) return;
+  const int b = blockIdx.x * kSeqPerBlock + (int)(threadIdx.x / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
+  if (b >= batch) return;                                        // wave-uniform
   const float* row = delta + (size_t)b * B;
   int n = 0;
   double total = 0.0;
-  for (int j = 0; j < B; ++j) {
-    const float x = row[j];
-    if (isfinite(x)) {
-      total += (double)x;
-      ++n;
+  for (int c0 = 0; c0 < B; c0 += kWave) {
+    const float x = c0 + lane < B ? row[c0 + lane] : -INFINITY;
+    n += __popcll(__ballot(isfinite(x)));
+    const int cnt = min(kWave, B - c0);
+    for (int l = 0; l < cnt; ++l) {
+      const float v = lane_value(x, l);
+      if (isfinite(v)) total += (double)v;
     }
   }
   int nsig = 0;
   if (n > 0) {
     const double mu = total / (double)n;
     double ss = 0.0;
-    for (int j = 0; j < B; ++j) {
-      const float x = row[j];
-      if (isfinite(x)) {
-        const double d = (double)x - mu;
-        ss += d * d;
+    for (int c0 = 0; c0 < B; c0 += kWave) {
+      const float x = c0 + lane < B ? row[c0 + lane] : -INFINITY;
+      const int cnt = min(kWave, B - c0);
+      for (int l = 0; l < cnt; ++l) {
+        const float v = lane_value(x, l);
+        if (isfinite(v)) {
+          const double d = (double)v - mu;
+          ss += d * d;
+        }
       }
     }
     const double var = ss / (double)n;
-    for (int j = 0; j < B; ++j) {
-      const float x = row[j];
-      if (!isfinite(x)) continue;
-      if (mode == 0) {
-        const double xd = (double)x;
-        nsig += (xd >= 0.0 && xd * xd >= var) ? 1 : 0;
-      } else {
-        const double d = (double)x - mu;
-        nsig += (d > 0.0 && d * d > var) ? 1 : 0;
+    for (int c0 = 0; c0 < B; c0 += kWave) {
+      const float x = c0 + lane < B ? row[c0 + lane] : -INFINITY;
+      bool hit = false;
+      if (isfinite(x)) {
+        if (mode == 0) {
+          const double xd = (double)x;
+          hit = xd >= 0.0 && xd * xd >= var;
+        } else {
+          const double d = (double)x - mu;
+          hit = d > 0.0 && d * d > var;
+        }
       }
+      nsig += __popcll(__ballot(hit));
     }
   }
-  const int steps = total_steps[b];
-  const double nbar = steps > 0 ? (double)token_sum[b] / (double)steps : 1.0;
-  const double kh = ceil(alpha * nbar);
-  const int khist = kh >= (double)B ? B : (kh <= 0.0 ? 0 : (int)kh);
-  const int k = khist > nsig ? khist : nsig;
-  k_out[b] = k < B ? k : B;
+  if (lane == 0) {
+    const int steps = total_steps[b];
+    const double nbar = steps > 0 ? (double)token_sum[b] / (double)steps : 1.0;
+    const double kh = ceil(alpha * nbar);
+    const int khist = kh >= (double)B ? B : (kh <= 0.0 ? 0 : (int)kh);
+    const int k = khist > nsig ? khist : nsig;
+    k_out[b] = k < B ? k : B;
+  }
 }
 
 // Per-sequence decoding history (FOCUS paper App. E.3.1): positions decoded
 // now but not before are added to token_sum; total_steps advances by one.
-__global__ __launch_bounds__(256) void history_update_kernel(
+// One wave per sequence.
+__global__ __launch_bounds__(64 * kSeqPerBlock) void history_update_kernel(
     const uint8_t* __restrict__ prev, const uint8_t* __restrict__ now,
     int32_t* __restrict__ token_sum, int32_t* __restrict__ total_steps, int batch, int B) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  const int b = blockIdx.x * kSeqPerBlock + (int)(threadIdx.x / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
   if (b >= batch) return;
+  const size_t base = (size_t)b * B;
   int n = 0;
-  for (int j = 0; j < B; ++j) n += (now[(size_t)b * B + j] && !prev[(size_t)b * B + j]) ? 1 : 0;
-  token_sum[b] += n;
-  total_steps[b] += 1;
+  for (int c0 = 0; c0 < B; c0 += kWave) {
+    const int j = c0 + lane;
+    n += __popcll(__ballot(j < B && now[base + j] != 0 && prev[base + j] == 0));
+  }
+  if (lane == 0) {
+    token_sum[b] += n;
+    total_steps[b] += 1;
+  }
 }
 
 // FOCUS token eviction with its structural constraints in one pass (FOCUS
@@ -262,32 +290,39 @@ __global__ __launch_bounds__(256) void focus_select_kernel(
 
 
 // Neighbour-aware delayed commit of block KV states (FOCUS paper Section 4.3,
-// App. E.3.1, App. E.3.3). One thread per sequence: position i commits in
-// this step if it is not cached yet and both it and its right neighbour are
-// decoded (the block's last position: once the whole block is decoded).
-// `cached` is updated in place; block_done = every position cached.
-__global__ __launch_bounds__(256) void commit_mask_kernel(const uint8_t* __restrict__ decoded,
-                                                          uint8_t* __restrict__ cached,
-                                                          uint8_t* __restrict__ commit,
-                                                          int32_t* __restrict__ block_done,
-                                                          int batch, int B) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+// App. E.3.1, App. E.3.3). One wave per sequence, lanes over the positions:
+// position i commits in this step if it is not cached yet and both it and its
+// right neighbour are decoded (the block's last position: once the whole
+// block is decoded). `cached` is updated in place; block_done = every
+// position cached.
+__global__ __launch_bounds__(64 * kSeqPerBlock) void commit_mask_kernel(
+    const uint8_t* __restrict__ decoded, uint8_t* __restrict__ cached,
+    uint8_t* __restrict__ commit, int32_t* __restrict__ block_done, int batch, int B) {
+  const int b = blockIdx.x * kSeqPerBlock + (int)(threadIdx.x / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
   if (b >= batch) return;
-  const uint8_t* d = decoded + (size_t)b * B;
-  uint8_t* c = cached + (size_t)b * B;
-  uint8_t* o = commit + (size_t)b * B;
+  const size_t base = (size_t)b * B;
+  const uint8_t* d = decoded + base;
   bool whole = true;
-  for (int j = 0; j < B; ++j) whole = whole && d[j] != 0;
-  bool done = true;
-  for (int j = 0; j < B; ++j) {
-    const bool right = j + 1 < B ? d[j + 1] != 0 : whole;
-    const bool was = c[j] != 0;
-    const bool now = !was && d[j] != 0 && right;
-    o[j] = now ? 1 : 0;
-    if (now) c[j] = 1;
-    done = done && (was || now);
+  for (int c0 = 0; c0 < B; c0 += kWave) {
+    const int j = c0 + lane;
+    whole = whole && __ballot(j < B && d[j] == 0) == 0;
   }
-  if (block_done) block_done[b] = done ? 1 : 0;
+  bool done = true;
+  for (int c0 = 0; c0 < B; c0 += kWave) {
+    const int j = c0 + lane;
+    bool open = false;                                  // not cached after this step
+    if (j < B) {
+      const bool right = j + 1 < B ? d[j + 1] != 0 : whole;
+      const bool was = cached[base + j] != 0;
+      const bool now = !was && d[j] != 0 && right;
+      commit[base + j] = now ? 1 : 0;
+      if (now) cached[base + j] = 1;
+      open = !(was || now);
+    }
+    done = done && __ballot(open) == 0;
+  }
+  if (lane == 0 && block_done) block_done[b] = done ? 1 : 0;
 }
 
 }  // namespace
@@ -323,7 +358,8 @@ extern "C" int bte_focus_budget(const float* delta, const int32_t* token_sum,
   if (batch <= 0 || block < 1 || block > 1024) return BTE_ERR_DIM;
   if (!(alpha >= 0.f) || !isfinite(alpha) || (threshold_mode != 0 && threshold_mode != 1))
     return BTE_ERR_DIM;
-  hipLaunchKernelGGL(focus_budget_kernel, dim3((batch + 255) / 256), dim3(256), 0, stream, delta,
+  hipLaunchKernelGGL(focus_budget_kernel, dim3((batch + kSeqPerBlock - 1) / kSeqPerBlock),
+                     dim3(64 * kSeqPerBlock), 0, stream, delta,
                      token_sum, total_steps, (double)alpha, threshold_mode, k_out, batch, block);
   return hipGetLastError() == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
 }
@@ -334,7 +370,8 @@ extern "C" int bte_focus_history_update(const uint8_t* decoded_prev, const uint8
   using namespace bte;
   if (!decoded_prev || !decoded_now || !token_sum || !total_steps) return BTE_ERR_NULL;
   if (batch <= 0 || block < 1 || block > 1024) return BTE_ERR_DIM;
-  hipLaunchKernelGGL(history_update_kernel, dim3((batch + 255) / 256), dim3(256), 0, stream,
+  hipLaunchKernelGGL(history_update_kernel, dim3((batch + kSeqPerBlock - 1) / kSeqPerBlock),
+                     dim3(64 * kSeqPerBlock), 0, stream,
                      decoded_prev, decoded_now, token_sum, total_steps, batch, block);
   return hipGetLastError() == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
 }
@@ -360,7 +397,8 @@ extern "C" int bte_focus_commit_mask(const uint8_t* decoded, uint8_t* cached, ui
   using namespace bte;
   if (!decoded || !cached || !commit_out) return BTE_ERR_NULL;
   if (batch <= 0 || block < 1 || block > 1024) return BTE_ERR_DIM;
-  hipLaunchKernelGGL(commit_mask_kernel, dim3((batch + 255) / 256), dim3(256), 0, stream, decoded,
+  hipLaunchKernelGGL(commit_mask_kernel, dim3((batch + kSeqPerBlock - 1) / kSeqPerBlock),
+                     dim3(64 * kSeqPerBlock), 0, stream, decoded,
                      cached, commit_out, block_done_out, batch, block);
   return hipGetLastError() == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
 }
