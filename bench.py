@@ -360,7 +360,8 @@ def full_step_leg(x, fc, ac, steps: int, warmup: int, dev):
             "selected_rows": n_sel, "mean_selected": round(n_sel / n, 2),
             "kernels": kernels}
 KERNEL_SOURCES = {"reduced_attention": ["reduced_attention.hip", "bte_device.h"],
-                  "focus_importance_delta": ["focus_delta.hip", "bte_device.h"]}
+                  "focus_importance_delta": ["focus_delta.hip", "bte_device.h"],
+                  "rows": ["rows.hip", "bte_device.h"]}
 
 
 def kernel_source_hash(kernel: str) -> str:

@@ -3,7 +3,9 @@
 Usage:
   python profile_summary.py trace  <kernel_stats.csv> <out.md> "<command>"
   python profile_summary.py counters <fetch_counter_collection.csv> <write_counter_collection.csv>
-        <kernel-substring> <out.json> "<fetch command>" "<write command>"
+        <kernel-substring> <source-key> <out.json> "<fetch command>" "<write command>"
+
+<source-key> names the kernel's source files in bench.KERNEL_SOURCES.
 
 `counters` scales FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the named
 kernel by the ratio of the known byte count of bench.py's calibration copy
@@ -61,7 +63,7 @@ def _per_kernel(path, counter, sub):
     return vals, cal
 
 
-def counters(fetch_csv, write_csv, sub, out_json, fetch_cmd, write_cmd):
+def counters(fetch_csv, write_csv, sub, source_key, out_json, fetch_cmd, write_cmd):
     f, fcal = _per_kernel(fetch_csv, "FETCH_SIZE", sub)
     w, wcal = _per_kernel(write_csv, "WRITE_SIZE", sub)
     kib = 1024.0
@@ -69,14 +71,13 @@ def counters(fetch_csv, write_csv, sub, out_json, fetch_cmd, write_cmd):
     wscale = bench.COPY_CAL_BYTES / (max(wcal) * kib)
     fetch = statistics.mean(f) * kib * fscale
     write = statistics.mean(w) * kib * wscale
-    kernel = "reduced_attention" if "attn" in sub else "focus_importance_delta"
     rec = {"kernel": sub, "launches": len(f), "fetch_kib_raw": statistics.mean(f),
            "write_kib_raw": statistics.mean(w), "copy_fetch_kib_raw": max(fcal),
            "copy_write_kib_raw": max(wcal), "copy_bytes": bench.COPY_CAL_BYTES,
            "fetch_scale": fscale, "write_scale": wscale,
            "fetch_bytes_per_launch": int(fetch), "write_bytes_per_launch": int(write),
            "traffic_bytes_per_launch": int(fetch + write),
-           "kernel_sources_sha1": bench.kernel_source_hash(kernel),
+           "kernel_sources_sha1": bench.kernel_source_hash(source_key),
            "commands": [fetch_cmd, write_cmd]}
     json.dump(rec, open(out_json, "w"), indent=1)
     print(json.dumps(rec))
@@ -86,4 +87,4 @@ if __name__ == "__main__":
     if sys.argv[1] == "trace":
         trace(*sys.argv[2:5])
     else:
-        counters(*sys.argv[2:8])
+        counters(*sys.argv[2:9])
