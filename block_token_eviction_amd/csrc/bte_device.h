@@ -58,6 +58,11 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// Streaming store: the line is written once and not read again by the kernel.
+__device__ __forceinline__ void st16_stream(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
 // 32x32 output tile of one MFMA: lane l, register r holds row
 // m = 8*(r/4) + 4*(l/32) + r%4 and column n = l%32.
 __device__ __forceinline__ f32x16 mfma_bf16(u32x4 a, u32x4 b, f32x16 c) {
