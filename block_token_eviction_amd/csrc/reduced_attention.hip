@@ -148,7 +148,12 @@ constexpr int kPageCache = 2048;
 
 // One workgroup's work: sequence b, KV head g, the T 32-row query tiles from
 // row0 on (each holding at least one real row).
-template <int D, bool BF16, int T, int kWaves, int kPaged>
+// kQSplit = false: the waves share the query rows and take every kWaves-th key
+// tile, their states merged at the end. kQSplit = true: wave w takes the 32*T
+// query rows from row0 + 32*T*w and every key tile (each wave streams the same
+// K/V through its own LDS stages, side by side on one CU, so the second read of
+// a tile is mostly an L2 hit instead of a second pass over HBM).
+template <int D, bool BF16, int T, int kWaves, int kPaged, bool kQSplit>
 __device__ __forceinline__ void attn_body(
     char* __restrict__ smem, const int32_t* __restrict__ pages, const char* __restrict__ q,
     const int32_t* __restrict__ cu, const char* __restrict__ cache_k,
@@ -161,6 +166,9 @@ __device__ __forceinline__ void attn_body(
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31;
   const int h = lane >> 5;
+  const int qrow0 = kQSplit ? row0 + 32 * T * w : row0;   // this wave's first query row
+  const int kt0 = kQSplit ? 0 : w;                       // this wave's first key tile
+  constexpr int kStep = kQSplit ? 1 : kWaves;            // and its key-tile stride
   const int L = kv_len[b];
   const int cub = cu[b];
   const size_t kv_row = (size_t)hkv * C::kRowBytes;    // bytes per cache position
@@ -184,7 +192,7 @@ __device__ __forceinline__ void attn_body(
   u32x4 qop[T][C::kHalf];
 #pragma unroll
   for (int tq = 0; tq < T; ++tq) {
-    const int rho = row0 + 32 * tq + n;
+    const int rho = qrow0 + 32 * tq + n;
     const bool ok = rho < rows;
     const int tok = ok ? rho / G : 0;
     const int head = g * G + (ok ? rho - tok * G : 0);
@@ -278,12 +286,12 @@ __device__ __forceinline__ void attn_body(
   // Prologue: this wave's first kStages tiles, one per stage.
 #pragma unroll
   for (int st = 0; st < C::kStages; ++st)
-    if (w + st * kWaves < ntiles) issue_tile(w + st * kWaves, st);
+    if (kt0 + st * kStep < ntiles) issue_tile(kt0 + st * kStep, st);
   int stage = 0;
-  for (int kt = w; kt < ntiles; kt += kWaves) {
+  for (int kt = kt0; kt < ntiles; kt += kStep) {
     // Wait for this tile's copies; those of the wave's later tiles already
     // issued (up to kStages - 1 tiles of 2 * kHalf copies) may stay in flight.
-    const int later = min(C::kStages - 1, (ntiles - 1 - kt) / kWaves);
+    const int later = min(C::kStages - 1, (ntiles - 1 - kt) / kStep);
     wait_copies_behind<C::kStages - 1, 2 * C::kHalf>(later);
     __builtin_amdgcn_wave_barrier();
     const char* kt_lds = wave_lds + stage * C::kStageBytes;
@@ -309,9 +317,9 @@ __device__ __forceinline__ void attn_body(
       }
     }
 
-    // The K half of the stage is consumed: refill it with tile kt + kStages*kWaves
+    // The K half of the stage is consumed: refill it with tile kt + kStages*kStep
     // now (the V half follows after P.V), once the operand reads have landed.
-    const int refill = kt + C::kStages * kWaves;
+    const int refill = kt + C::kStages * kStep;
     size_t refill_row = 0;
     if (refill < ntiles) {
       __builtin_amdgcn_s_waitcnt(kLgkm0);
@@ -440,23 +448,30 @@ __device__ __forceinline__ void attn_body(
     // kept in L2), with streaming stores 6 %.
     constexpr int kChunks = C::kRowBytes / 16;          // 16-byte chunks per output row
     constexpr int kElems = 16 / C::ES;                  // elements per chunk
+    // Rows written for this tq: 32 merged ones (key split) or the 32 of each wave.
+    constexpr int kOutRows = kQSplit ? 32 * kWaves : 32;
     constexpr int kRowsPerPass = 64 * kWaves / kChunks;
-    static_assert(kRowsPerPass >= 1 && 32 % kRowsPerPass == 0, "passes tile the 32 rows");
+    static_assert(kRowsPerPass >= 1 && kOutRows % kRowsPerPass == 0, "passes tile the rows");
     const int chunk = threadIdx.x % kChunks;
 #pragma unroll
-    for (int r0 = 0; r0 < 32; r0 += kRowsPerPass) {
-      const int rr = r0 + threadIdx.x / kChunks;         // query row of the tile
-      const int rho = row0 + 32 * tq + rr;
+    for (int r0 = 0; r0 < kOutRows; r0 += kRowsPerPass) {
+      const int ro = r0 + threadIdx.x / kChunks;         // output row of this tq
+      const int vq = kQSplit ? ro / 32 : 0;              // query split: the wave that owns it
+      const int rr = ro % 32;                            // its row within the 32-row tile
+      const int rho = row0 + (kQSplit ? 32 * T * vq : 0) + 32 * tq + rr;
       if (rho < rows) {
+        // Merge weights: one state per wave (key split), or the owner's own state.
+        constexpr int kStates = kQSplit ? 1 : kWaves;
+        const int v0 = kQSplit ? vq : 0;
         float M = -INFINITY;
 #pragma unroll
-        for (int v = 0; v < kWaves; ++v) M = fmaxf(M, mbuf[v * 32 + rr]);
-        float wgt[kWaves];
+        for (int v = 0; v < kStates; ++v) M = fmaxf(M, mbuf[(v0 + v) * 32 + rr]);
+        float wgt[kStates];
         float Ls = 0.f;
 #pragma unroll
-        for (int v = 0; v < kWaves; ++v) {
-          wgt[v] = fast_exp2((mbuf[v * 32 + rr] - M) * c);
-          Ls = fmaf(lbuf[v * 32 + rr], wgt[v], Ls);
+        for (int v = 0; v < kStates; ++v) {
+          wgt[v] = fast_exp2((mbuf[(v0 + v) * 32 + rr] - M) * c);
+          Ls = fmaf(lbuf[(v0 + v) * 32 + rr], wgt[v], Ls);
         }
         const float inv = 1.0f / Ls;
         const int tok = rho / G;
@@ -468,7 +483,8 @@ __device__ __forceinline__ void attn_body(
           const int d = chunk * kElems + i;
           float acc = 0.f;
 #pragma unroll
-          for (int v = 0; v < kWaves; ++v) acc = fmaf(obuf[(v * 32 + rr) * C::kOStride + d], wgt[v], acc);
+          for (int v = 0; v < kStates; ++v)
+            acc = fmaf(obuf[((v0 + v) * 32 + rr) * C::kOStride + d], wgt[v], acc);
           res[i] = acc * inv;
         }
         u32x4 val;
@@ -500,7 +516,10 @@ __device__ __forceinline__ void attn_body(
 // heads the row group is the slowest grid dimension instead: every
 // sequence's first row group, then the second ones, and so on.
 
-template <int D, bool BF16, int T, int kWaves, int kPaged>
+// kQSplitOk: a row group spans 32*T*kWaves query rows; a workgroup with more
+// than 32*T real rows in it splits them over its waves (attn_body kQSplit),
+// one with fewer splits the keys as usual.
+template <int D, bool BF16, int T, int kWaves, int kPaged, bool kQSplitOk>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T == 1 ? 2 : 1))) void attn_kernel(
     const char* __restrict__ q, const int32_t* __restrict__ count, const int32_t* __restrict__ cu,
     const char* __restrict__ cache_k, const char* __restrict__ cache_v, KvMap map,
@@ -532,7 +551,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T =
   // [0, batch) is clamped: a bad order gives wrong results, never a stray access.
   const int b = order ? min(max(order[r], 0), batch - 1) : r;
   const int rows = count[b] * (hq / hkv);
-  const int row0 = rg * 32 * T;
+  constexpr int kSpan = kQSplitOk ? 32 * T * kWaves : 32 * T;   // query rows per row group
+  const int row0 = rg * kSpan;
   if (row0 >= rows) return;
   if constexpr (kPaged == kPagedLds) {
     const int n_pages = min((kv_len[b] + (1 << map.lg_page) - 1) >> map.lg_page, map.max_pages);
@@ -540,13 +560,22 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T =
     for (int i = threadIdx.x; i < n_pages; i += 64 * kWaves) pages[i] = bt[i];
     __syncthreads();
   }
-  // Workgroup-uniform: skip query tiles that hold no real row.
+  // Workgroup-uniform choices (every wave of the workgroup takes the same body,
+  // so their barriers match): split the query rows when one wave's tiles do not
+  // hold them all; otherwise skip query tiles that hold no real row.
+  if constexpr (kQSplitOk) {
+    if (rows - row0 > 32 * T) {
+      attn_body<D, BF16, T, kWaves, kPaged, true>(smem, pages, q, cu, cache_k, cache_v, map, kv_len,
+                                                  out, hq, hkv, c, b, g, rows, row0);
+      return;
+    }
+  }
   if (T == 2 && rows - row0 > 32)
-    attn_body<D, BF16, T, kWaves, kPaged>(smem, pages, q, cu, cache_k, cache_v, map, kv_len, out,
-                                          hq, hkv, c, b, g, rows, row0);
+    attn_body<D, BF16, T, kWaves, kPaged, false>(smem, pages, q, cu, cache_k, cache_v, map, kv_len,
+                                                 out, hq, hkv, c, b, g, rows, row0);
   else
-    attn_body<D, BF16, 1, kWaves, kPaged>(smem, pages, q, cu, cache_k, cache_v, map, kv_len, out,
-                                          hq, hkv, c, b, g, rows, row0);
+    attn_body<D, BF16, 1, kWaves, kPaged, false>(smem, pages, q, cu, cache_k, cache_v, map, kv_len,
+                                                 out, hq, hkv, c, b, g, rows, row0);
 }
 
 struct AttnArgs {
@@ -563,13 +592,14 @@ struct AttnArgs {
   float c;
 };
 
-template <int D, bool BF16, int T, int kWaves, int kPaged>
+template <int D, bool BF16, int T, int kWaves, int kPaged, bool kQSplitOk = false>
 hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   const long rows = (long)a.k_max * (a.hq / a.hkv);
-  const long n_rg = (rows + 32 * T - 1) / (32 * T);
+  const long span = kQSplitOk ? 32L * T * kWaves : 32L * T;
+  const long n_rg = (rows + span - 1) / span;
   const long grid = (long)((a.batch + kXcds - 1) / kXcds) * kXcds * a.hkv * n_rg;
   if (grid > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_kernel<D, BF16, T, kWaves, kPaged>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((attn_kernel<D, BF16, T, kWaves, kPaged, kQSplitOk>), dim3((unsigned)grid),
                      dim3(64 * kWaves), 0, stream, (const char*)a.q, a.count, a.cu,
                      (const char*)a.ck, (const char*)a.cv, a.map, a.kl, a.order, (char*)a.out,
                      a.batch, a.hq, a.hkv, (int)n_rg, a.hkv >= 4 ? 1 : 0, a.c);
@@ -590,6 +620,11 @@ template <int D, int kPaged>
 hipError_t launch_bf16(const AttnArgs& a, hipStream_t stream) {
   const long rows = (long)a.k_max * (a.hq / a.hkv);
   const int T = rows > 32 ? 2 : 1;
+  // More than 64 query rows per KV head possible: two-wave workgroups over
+  // 128-row groups, whose waves split the rows when there are more than 64
+  // (each streams the K/V once; the second stream is served mostly by L2) and
+  // the keys otherwise.
+  if (rows > 64) return launch<D, true, 2, 2, kPaged, true>(a, stream);
   const long items = (long)a.batch * a.hkv * ((rows + 32 * T - 1) / (32 * T));
   const int nw = waves_for(items, a.order != nullptr);
   if (T == 2) {

@@ -86,6 +86,27 @@ def test_attention_many_items(cfg, ordered):
     _attn(cfg, ordered=ordered)
 
 
+# More than 64 query rows per KV head (k_max * G > 64): two-wave workgroups over
+# 128-row groups; those with more than 64 real rows split them over the waves
+# (each wave streams all keys), the others split the keys. Budgets 0..32 mix
+# both kinds in one launch; with G = 8 a sequence has up to 256 rows, so its
+# second 128-row group is split or not as well.
+QSPLIT = [
+    W.AttnCfg("qsplit_mixed", seed=64, batch=300, kept=None, k_lo=0, k_hi=32, hq=32, hkv=8,
+              head_dim=128, prefix_lo=1, prefix_hi=300),
+    W.AttnCfg("qsplit_g8", seed=65, batch=120, kept=None, k_lo=1, k_hi=32, hq=32, hkv=4,
+              head_dim=128, prefix_lo=20, prefix_hi=260),
+    W.AttnCfg("qsplit_d64", seed=66, batch=200, kept=None, k_lo=10, k_hi=32, hq=32, hkv=8,
+              head_dim=64, prefix_lo=1, prefix_hi=150),
+]
+
+
+@pytest.mark.parametrize("cfg", QSPLIT, ids=[c.name for c in QSPLIT])
+@pytest.mark.parametrize("ordered", [False, True], ids=["index_order", "longest_first"])
+def test_attention_query_split(cfg, ordered):
+    _attn(cfg, ordered=ordered)
+
+
 @pytest.mark.parametrize("batch", [1, 7, 64, 65, 1000, 1024, 2000, 3000, 5000, 16384])
 def test_attention_order_matches_oracle(batch):
     bte = _bte()

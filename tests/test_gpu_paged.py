@@ -57,6 +57,9 @@ CFGS = [
                head_dim=64, prefix_lo=30, prefix_hi=200), 256),
     (W.AttnCfg("paged_f32", seed=73, batch=5, kept=4, hq=8, hkv=2, head_dim=128, dtype=W.F32,
                prefix_lo=40, prefix_hi=150), 32),
+    # up to 128 query rows per KV head: query-split workgroups through the table
+    (W.AttnCfg("paged_qsplit", seed=75, batch=150, kept=None, k_lo=4, k_hi=32, hq=32, hkv=8,
+               head_dim=128, prefix_lo=10, prefix_hi=400), 16),
     # more than 2048 pages per sequence: page entries are read from memory
     (W.AttnCfg("paged_long_table", seed=74, batch=3, kept=5, hq=8, hkv=2, head_dim=128,
                prefix_lo=16600, prefix_hi=17000), 8),
