@@ -68,8 +68,8 @@ def test_attention_edge_cases(cfg, ordered):
     _attn(cfg, ordered=ordered)
 
 
-# Enough (sequence, KV head) items that the launch takes one wave per item
-# (with a longest-first order) or two (without); budgets 4..12 kept rows give
+# Enough (sequence, KV head) items that the launch takes two waves per item
+# (the smaller cases above take four); budgets up to 12 or 16 kept rows give
 # workgroups of one and of two 32-row query tiles. Short prefixes keep the
 # float64 oracle fast.
 MANY = [
