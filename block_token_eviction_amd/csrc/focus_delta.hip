@@ -321,11 +321,14 @@ hipError_t launch_w(const void* q0, const void* k0, const void* q1, const void* 
 }
 
 // One wave per KV group, at most 8 (a wave loops over groups beyond that).
+// fp32 rows of head dim 128 need more than the 256 VGPRs a wave may hold at two
+// waves per SIMD (eight per workgroup): those take at most four waves.
 template <int D, bool BF16, int R>
 hipError_t launch_r(const void* q0, const void* k0, const void* q1, const void* k1,
                     const uint8_t* decoded, float* out, int batch, int B, int hq, int hkv, int rt_r,
                     float c, hipStream_t stream) {
-  if (hkv >= 8) return launch_w<D, BF16, R, 8>(q0, k0, q1, k1, decoded, out, batch, B, hq, hkv, rt_r, c, stream);
+  constexpr bool kWide = BF16 || D < 128;
+  if (kWide && hkv >= 8) return launch_w<D, BF16, R, kWide ? 8 : 4>(q0, k0, q1, k1, decoded, out, batch, B, hq, hkv, rt_r, c, stream);
   if (hkv >= 4) return launch_w<D, BF16, R, 4>(q0, k0, q1, k1, decoded, out, batch, B, hq, hkv, rt_r, c, stream);
   if (hkv >= 2) return launch_w<D, BF16, R, 2>(q0, k0, q1, k1, decoded, out, batch, B, hq, hkv, rt_r, c, stream);
   return launch_w<D, BF16, R, 1>(q0, k0, q1, k1, decoded, out, batch, B, hq, hkv, rt_r, c, stream);
