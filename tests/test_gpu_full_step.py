@@ -141,3 +141,63 @@ def test_full_step_b1024_sampled():
     """The benchmarked extended step itself (batch 1024, prefixes 1024..4096, pages of 64)."""
     sample = sorted(np.random.default_rng(11).choice(1024, size=24, replace=False).tolist())
     _check_full_step(W.CHAIN_FOCUS_B1024, W.CHAIN_ATTN_B1024, 64, sample)
+
+
+def test_full_step_graph_replays_match_eager():
+    """The extended step captured in a HIP graph and replayed three times, with the
+    per-sequence state restored and the outputs cleared eagerly in between: every
+    replay equals the eager step bit for bit (outputs, state, KV pool)."""
+    from block_token_eviction_amd.chain import FocusFullStep
+    fc = W.FocusCfg("full_graph", seed=53, batch=48)
+    ac = W.AttnCfg("full_graph", seed=53, batch=48, kept=None, prefix_lo=30, prefix_hi=500)
+    say("extended step under graph capture")
+    page = 16
+    x = W.focus_full_inputs(fc, ac, page_size=page, device="cuda")
+    per_token = [x["hidden_rows"], x["residual"], x["rope_pos"], x["cache_idx"]]
+    step = FocusFullStep(fc.batch, fc.block, fc.hq, fc.head_dim,
+                         [(t.shape[2:], t.dtype) for t in per_token], fc.dtype, "cuda")
+    state = [x[k] for k in ("token_sum", "total_steps", "rightmost_processed", "cached")]
+    state0 = [t.clone() for t in state]
+    pool0 = (x["pool_k"].clone(), x["pool_v"].clone())
+    args = dict(q0=x["q0"], k0=x["k0"], q1=x["q1"], k1=x["k1"], decoded=x["decoded"],
+                decoded_now=x["decoded_now"], pool_kernel=fc.pool_kernel, alpha=ALPHA,
+                token_sum=x["token_sum"], total_steps=x["total_steps"],
+                rightmost_processed=x["rightmost_processed"], cached=x["cached"],
+                per_token=per_token, new_k=x["new_k_full"], new_v=x["new_v_full"],
+                q_kept=x["q_full"], pos_base=x["pos_base"], block_table=x["block_table"],
+                page_size=page, pool_k=x["pool_k"], pool_v=x["pool_v"], kv_len=x["kv_len"])
+
+    def reset():
+        for t, t0 in zip(state, state0):
+            t.copy_(t0)
+        x["pool_k"].copy_(pool0[0])
+        x["pool_v"].copy_(pool0[1])
+        step.out.zero_()
+        for r in step.rows:
+            r.zero_()
+
+    reset()
+    step.run(**args)
+    torch.cuda.synchronize()
+    n = int(step.cu[-1])
+    outs = lambda: [step.delta, step.k, step.idx, step.count, step.cu, step.commit,
+                    step.block_done, step.out[:n]] + [r[:n] for r in step.rows] + state + \
+                   [x["pool_k"], x["pool_v"]]
+    want = [t.clone() for t in outs()]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                  # warm-up on the capture stream
+        reset()
+        step.run(**args)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    reset()
+    with torch.cuda.graph(g):
+        step.run(**args)
+    for rep in range(3):
+        reset()                                  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs(), want)):
+            assert torch.equal(a, b), f"replay {rep}, tensor {i}"
