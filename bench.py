@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 ALPHA = 1.5                    # FOCUS budget multiplier of the pages' worked example
 PAGE = 64                      # KV pool page size (rows) of the extended step
 METRIC = "block tokens/s through score→top-K→gather→reduced attn; % of HBM/MFMA roofline"
@@ -123,6 +124,12 @@ def main():
                    "GB/s": round(bytes_[n] / (stage_ms[n] * 1e-3) / 1e9, 1),
                    "hbm_frac": round(bytes_[n] / (stage_ms[n] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
                for n in stage_ms}
+    # matrix-core work of the score tiles: S = Q K^T for 2 layers, every (sequence, query head)
+    flops_score = score_flops(fc.batch, B, hq, D)
+    kernels["focus_importance_delta"]["tflops"] = round(
+        flops_score / (stage_ms["focus_importance_delta"] * 1e-3) / 1e12, 2)
+    kernels["reduced_attention"]["tflops"] = round(
+        flops_attn / (stage_ms["reduced_attention"] * 1e-3) / 1e12, 2)
     dom = "reduced_attention"
     achieved = bytes_[dom] / (stage_ms[dom] * 1e-3) / 1e9
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -217,6 +224,7 @@ def main():
                    "survivor positions/s": round(ec.batch * ec.generated / (sum(lay_ms) * 1e-3), 1)}
 
     full = full_step_leg(x, fc, ac, args.steps, args.warmup, dev)
+    score_resident = score_resident_leg(dev)
 
     if args.copy_calibration:
         src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device=dev)
@@ -242,12 +250,50 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "es_mode": es_mode,
         "es_pipeline": es_pipeline, "graph_ms_per_step": graph_ms,
         "step_ms_p10_p50_p90": [round(percentile(step_ms, q), 4) for q in (10, 50, 90)],
-        "full_step": full,
+        "full_step": full, "score_resident": score_resident,
     }
     print(json.dumps(line), flush=True)
 
 
 COPY_CAL_BYTES = 256 << 20
+
+
+def score_flops(batch: int, block: int, hq: int, head_dim: int) -> int:
+    """MFMA flops of the importance delta: two layers of B x B score tiles per
+    (sequence, query head), 2 * D flops per score."""
+    return 2 * batch * hq * block * block * head_dim * 2
+
+
+def score_resident_leg(dev, batch: int = 256, reps: int = 100):
+    """Auxiliary, labelled as such: the importance-delta kernel repeated on a
+    small batch whose inputs (batch 256: 168 MB) stay in the 256 MB Infinity
+    Cache between launches, so HBM does not bound it. Shows the contraction
+    phase's own matrix-core rate against the bf16 dense peak; not a bench
+    figure of the workload."""
+    import torch
+
+    import block_token_eviction_amd as bte
+    import workloads as W
+
+    cfg = W.FocusCfg("score_resident", seed=5, batch=batch)
+    fi = W.focus_inputs(cfg, device=dev)
+    out = torch.empty((batch, cfg.block), dtype=torch.float32, device=dev)
+    run = lambda: bte.focus_importance_delta(fi["q0"], fi["k0"], fi["q1"], fi["k1"], fi["decoded"],
+                                             cfg.pool_kernel, out=out)
+    for _ in range(10):
+        run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    tf = score_flops(batch, cfg.block, cfg.hq, cfg.head_dim) / (ms * 1e-3) / 1e12
+    return {"workload": f"focus delta, batch {batch}, inputs cache-resident (auxiliary)",
+            "ms": round(ms, 4), "tflops": round(tf, 1),
+            "frac_of_bf16_dense_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
 
 
 def percentile(sorted_vals, q):
