@@ -266,10 +266,11 @@ def score_flops(batch: int, block: int, hq: int, head_dim: int) -> int:
 
 def score_resident_leg(dev, batch: int = 256, reps: int = 100):
     """Auxiliary, labelled as such: the importance-delta kernel repeated on a
-    small batch whose inputs (batch 256: 168 MB) stay in the 256 MB Infinity
-    Cache between launches, so HBM does not bound it. Shows the contraction
-    phase's own matrix-core rate against the bf16 dense peak; not a bench
-    figure of the workload."""
+    batch whose inputs (batch 256: 168 MB) fit in the 256 MB Infinity Cache,
+    with no flush between launches, and its algorithmic matrix-core rate
+    against the bf16 dense peak. The kernel's streaming loads need not keep
+    the inputs cached, so this does not guarantee cache-fed reads; not a
+    bench figure of the workload."""
     import torch
 
     import block_token_eviction_amd as bte
@@ -291,7 +292,7 @@ def score_resident_leg(dev, batch: int = 256, reps: int = 100):
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / reps
     tf = score_flops(batch, cfg.block, cfg.hq, cfg.head_dim) / (ms * 1e-3) / 1e12
-    return {"workload": f"focus delta, batch {batch}, inputs cache-resident (auxiliary)",
+    return {"workload": f"focus delta, batch {batch}, repeated without flush (auxiliary)",
             "ms": round(ms, 4), "tflops": round(tf, 1),
             "frac_of_bf16_dense_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
 
