@@ -31,6 +31,25 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return eligible ? key : 0u;
 }
 
+// Rank of `key`, held by position j, in row[0 .. n): the keys above it plus the
+// equal keys at lower positions. Eight keys per iteration come from two
+// 16-byte LDS reads that are in flight together (one read per key waited for
+// each in turn: 9 us for rows of 256). row is 16-byte aligned and holds 0,
+// below every eligible key, from n up to n rounded to 8.
+__device__ __forceinline__ int rank_in_row(const uint32_t* row, int n, uint32_t key, int j) {
+  int rank = 0;
+  for (int i0 = 0; i0 < n; i0 += 8) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(row + i0);
+    const u32x4 c = *reinterpret_cast<const u32x4*>(row + i0 + 4);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      rank += (a[u] > key) | ((a[u] == key) & (i0 + u < j));
+      rank += (c[u] > key) | ((c[u] == key) & (i0 + 4 + u < j));
+    }
+  }
+  return rank;
+}
+
 // NT threads per row (NT = 64 packs 256/64 rows per workgroup).
 template <int NT>
 __global__ __launch_bounds__(NT < 256 ? 256 : NT) void topk_kernel(
@@ -39,7 +58,7 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void topk_kernel(
   constexpr int WG = NT < 256 ? 256 : NT;
   constexpr int RPW = WG / NT;                 // rows per workgroup
   constexpr int WPR = NT / kWave;              // waves per row
-  __shared__ uint32_t keys[RPW][NT];
+  __shared__ __attribute__((aligned(16))) uint32_t keys[RPW][NT];   // 0 past n
   __shared__ int wcnt[RPW][WPR];
   __shared__ int wsel[RPW][WPR];
 
@@ -63,11 +82,7 @@ __global__ __launch_bounds__(NT < 256 ? 256 : NT) void topk_kernel(
   keff = keff < n_elig ? keff : n_elig;
   keff = keff < k_max ? keff : k_max;
 
-  int rank = 0;
-  for (int i = 0; i < n; ++i) {
-    const uint32_t o = keys[slot][i];
-    rank += (o > key) | ((o == key) & (i < j));
-  }
+  const int rank = rank_in_row(keys[slot], n, key, j);
   const bool sel = key != 0u && rank < keff;
   const uint64_t sm = __ballot(sel);
   if ((threadIdx.x & (kWave - 1)) == 0) wsel[slot][wv] = __popcll(sm);
@@ -228,7 +243,7 @@ __global__ __launch_bounds__(256) void focus_select_kernel(
     const float* __restrict__ delta, const int32_t* __restrict__ kbud,
     const uint8_t* __restrict__ decoded, int32_t* __restrict__ rightmost,
     int32_t* __restrict__ idx_out, int32_t* __restrict__ count_out, int batch, int B) {
-  __shared__ uint32_t keys[4][kWave];
+  __shared__ __attribute__((aligned(16))) uint32_t keys[4][kWave];   // 0 past B
   const int slot = threadIdx.x / kWave;
   const int j = threadIdx.x % kWave;
   const int b = blockIdx.x * 4 + slot;
@@ -244,11 +259,7 @@ __global__ __launch_bounds__(256) void focus_select_kernel(
   const int n_elig = __popcll(__ballot(key != 0u));
   int keff = kbud[b];
   keff = keff < 0 ? 0 : (keff < n_elig ? keff : n_elig);
-  int rank = 0;
-  for (int i = 0; i < B; ++i) {
-    const uint32_t o = keys[slot][i];
-    rank += (o > key) | ((o == key) & (i < j));
-  }
+  const int rank = rank_in_row(keys[slot], B, key, j);
   const bool cand = key != 0u && rank < keff;
   const uint64_t cm = __ballot(cand);
   const int maxc = cm ? 63 - __clzll(cm) : -1;
