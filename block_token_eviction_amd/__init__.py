@@ -17,11 +17,13 @@ import os
 
 import torch
 
+from . import contract
+
 __all__ = ["lib", "LIB_PATH", "BteError", "status_string", "focus_importance_delta",
            "esdllm_score", "topk_select", "gather_rows", "kv_scatter", "reduced_attention",
            "attention_order", "reduced_attention_paged", "kv_scatter_paged", "focus_budget",
            "focus_history_update", "focus_select", "focus_commit_mask", "gather_rows_multi",
-           "BTE_F32", "BTE_BF16"]
+           "BTE_F32", "BTE_BF16", "contract"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbte.so")
 BTE_F32, BTE_BF16 = 0, 1
@@ -134,6 +136,8 @@ def esdllm_score(h_new, h_prev, surv_pos, conf, alpha: float, out=None):
     assert surv_pos.shape == (batch, n_surv) and conf.shape == (batch, seq_len)
     if out is None:
         out = torch.empty((batch, n_surv), dtype=torch.float32, device=h_new.device)
+    if contract.enabled():
+        contract.check_positions(surv_pos, h_prev.shape[1], "surv_pos")
     _check("bte_esdllm_score", lib.bte_esdllm_score(
         _ptr(h_new), _ptr(h_prev), _ptr(surv_pos), _ptr(conf), float(alpha), _ptr(out), batch,
         n_surv, seq_len, hidden, _dtype(h_new), _stream()))
@@ -171,6 +175,8 @@ def gather_rows(src, idx, count, cu, out=None):
     if out is None:
         out = torch.empty((batch * k_max,) + tuple(src.shape[2:]), dtype=src.dtype, device=src.device)
     assert out.dtype == src.dtype and out[0].numel() * out.element_size() == row_bytes
+    if contract.enabled():
+        contract.check_rows(idx, count, cu, k_max, n=n, out_rows=out.shape[0])
     _check("bte_gather_rows", lib.bte_gather_rows(
         _ptr(src), _ptr(idx), _ptr(count), _ptr(cu), _ptr(out), batch, n, k_max, row_bytes,
         _stream()))
@@ -185,6 +191,9 @@ def kv_scatter(new_k, new_v, idx, count, cu, row_base, cache_k, cache_v, pos_map
     row_bytes = cache_k[0].numel() * cache_k.element_size()
     assert new_k[0].numel() * new_k.element_size() == row_bytes
     n = 0 if pos_map is None else pos_map.shape[1]
+    if contract.enabled():
+        contract.check_scatter(idx, count, cu, k_max, row_base, cache_k.shape[0], new_k.shape[0],
+                               pos_map)
     _check("bte_kv_scatter", lib.bte_kv_scatter(
         _ptr(new_k), _ptr(new_v), _ptr(idx), _ptr(count), _ptr(cu), _ptr(pos_map), n,
         _ptr(row_base), _ptr(cache_k), _ptr(cache_v), batch, k_max, row_bytes, _stream()))
@@ -210,6 +219,9 @@ def reduced_attention(q, count, cu, cache_k, cache_v, seq_start, kv_len, k_max: 
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    if contract.enabled():
+        contract.check_attention(count, cu, kv_len, k_max, min(q.shape[0], out.shape[0]),
+                                 seq_start=seq_start, cache_rows=cache_k.shape[0], order=order)
     _check("bte_reduced_attention", lib.bte_reduced_attention(
         _ptr(q), _ptr(count), _ptr(cu), _ptr(cache_k), _ptr(cache_v), _ptr(seq_start),
         _ptr(kv_len), _ptr(order), _ptr(out), batch, k_max, hq, hkv, d, float(scale), _dtype(q),
@@ -301,6 +313,10 @@ def reduced_attention_paged(q, count, cu, cache_k, cache_v, block_table, page_si
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    if contract.enabled():
+        contract.check_attention(count, cu, kv_len, k_max, min(q.shape[0], out.shape[0]),
+                                 cache_rows=cache_k.shape[0], block_table=block_table,
+                                 page_size=page_size, order=order)
     _check("bte_reduced_attention_paged", lib.bte_reduced_attention_paged(
         _ptr(q), _ptr(count), _ptr(cu), _ptr(cache_k), _ptr(cache_v), _ptr(block_table),
         block_table.shape[1], page_size, _ptr(kv_len), _ptr(order), _ptr(out), batch, k_max, hq,
@@ -318,6 +334,9 @@ def kv_scatter_paged(new_k, new_v, idx, count, cu, pos_base, block_table, page_s
     row_bytes = cache_k[0].numel() * cache_k.element_size()
     assert new_k[0].numel() * new_k.element_size() == row_bytes
     n = 0 if pos_map is None else pos_map.shape[1]
+    if contract.enabled():
+        contract.check_scatter_paged(idx, count, cu, k_max, pos_base, block_table, page_size,
+                                     cache_k.shape[0], new_k.shape[0], pos_map)
     _check("bte_kv_scatter_paged", lib.bte_kv_scatter_paged(
         _ptr(new_k), _ptr(new_v), _ptr(idx), _ptr(count), _ptr(cu), _ptr(pos_map), n,
         _ptr(pos_base), _ptr(block_table), block_table.shape[1], page_size, _ptr(cache_k),
@@ -362,6 +381,8 @@ def gather_rows_multi(srcs, idx, count, cu, outs=None):
         rb = s_[0, 0].numel() * s_.element_size()
         assert o[0].numel() * o.element_size() == rb
         descs.append(_RowsTensor(s_.data_ptr(), o.data_ptr(), rb))
+    if contract.enabled():
+        contract.check_rows(idx, count, cu, k_max, n=n, out_rows=min(o.shape[0] for o in outs))
     arr = (_RowsTensor * len(descs))(*descs)
     _check("bte_gather_rows_multi", lib.bte_gather_rows_multi(
         ctypes.cast(arr, ctypes.c_void_p), len(descs), _ptr(idx), _ptr(count), _ptr(cu), batch, n,

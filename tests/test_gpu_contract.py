@@ -1,0 +1,55 @@
+"""With BTE_CHECK=1 the binding validates the device-data contract on the host:
+valid calls give the same results as without it, and a violating call raises
+ContractError before anything is launched (the bad input never reaches a
+kernel)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from helpers import dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _bte():
+    import block_token_eviction_amd as bte
+    return bte
+
+
+def test_checked_calls_match_and_violations_raise(monkeypatch):
+    bte = _bte()
+    cfg = W.AttnCfg("contract", seed=91, batch=12, kept=None, k_lo=0, k_hi=12, prefix_lo=5,
+                    prefix_hi=200)
+    ai = W.attention_inputs(cfg)
+    g = dev(ai)
+    say("contract checks through the binding")
+    src = torch.randn(cfg.batch, cfg.block, 256, device="cuda").to(torch.bfloat16)
+    plain = bte.gather_rows(src, g["idx"], g["count"], g["cu"])
+    att = bte.reduced_attention(g["q"], g["count"], g["cu"], g["cache_k"], g["cache_v"],
+                                g["seq_start"], g["kv_len"], ai["k_max"])
+    monkeypatch.setenv("BTE_CHECK", "1")
+    n = int(ai["cu"][-1])
+    assert torch.equal(bte.gather_rows(src, g["idx"], g["count"], g["cu"])[:n], plain[:n])
+    att2 = bte.reduced_attention(g["q"], g["count"], g["cu"], g["cache_k"], g["cache_v"],
+                                 g["seq_start"], g["kv_len"], ai["k_max"])
+    assert torch.equal(att2[:n], att[:n])
+
+    # an index past the block: caught on the host
+    bad = ai["idx"].clone()
+    b = int(np.flatnonzero(ai["count"].numpy() > 0)[0])
+    bad[b, int(ai["count"][b]) - 1] = cfg.block
+    with pytest.raises(bte.contract.ContractError):
+        bte.gather_rows(src, bad.cuda(), g["count"], g["cu"])
+    # a sequence whose KV rows run past the cache
+    ss = ai["seq_start"].clone()
+    ss[b] = ai["rows"]
+    with pytest.raises(bte.contract.ContractError):
+        bte.reduced_attention(g["q"], g["count"], g["cu"], g["cache_k"], g["cache_v"], ss.cuda(),
+                              g["kv_len"], ai["k_max"])
+    # kept rows scattered past the end of the cache
+    rb = ai["row_base"].clone()
+    rb[b] = ai["rows"]
+    with pytest.raises(bte.contract.ContractError):
+        bte.kv_scatter(g["new_k"], g["new_v"], g["idx"], g["count"], g["cu"], rb.cuda(),
+                       g["cache_k"].clone(), g["cache_v"].clone())
