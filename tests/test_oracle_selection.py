@@ -85,3 +85,24 @@ def test_negative_zero_ties_go_to_lower_index():
     s = np.array([[-0.0, 0.0]], np.float32)
     idx, _, _ = oracle.topk_select(s, np.array([1]), 1)
     assert idx[0, 0] == 0
+
+
+def test_exhaustive_n6_against_stable_sort():
+    """Every row of {-inf, -1, -0.0, +0.0, 1}^6 and every K in [0, 7]: the kept
+    set is the first K_eff eligible positions of a stable sort by descending
+    score (numpy's stable argsort, ties in index order, -0.0 == +0.0),
+    output ascending."""
+    vals = [-math.inf, -1.0, -0.0, 0.0, 1.0]
+    rows = np.array(list(itertools.product(vals, repeat=6)), dtype=np.float32)
+    order = np.argsort(-rows, axis=1, kind="stable")
+    elig = rows > -np.inf
+    for k in range(0, 8):
+        for k_max in (6, 4):
+            idx, count, cu = oracle.topk_select(rows, np.full(len(rows), k, np.int32), k_max)
+            for r in range(len(rows)):
+                ranked = [j for j in order[r] if elig[r, j]]
+                want = sorted(ranked[:min(k, len(ranked), k_max)])
+                assert count[r] == len(want)
+                assert idx[r, :count[r]].tolist() == want
+                assert (idx[r, count[r]:] == -1).all()
+            assert cu[0] == 0 and np.array_equal(np.diff(cu), count)
