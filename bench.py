@@ -440,6 +440,18 @@ def measured_traffic(kernel: str):
     return rec.get("traffic_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(x, fc, ac, budget_s: float = 12.0):
     """The float64 oracle on the first sequences of the same workload, chunk by
     chunk until about `budget_s` seconds of CPU work; block tokens/s of that sample."""
@@ -477,7 +489,7 @@ def cpu_baseline(x, fc, ac, budget_s: float = 12.0):
         done = hi
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {"value": round(done * fc.block / elapsed, 1), "unit": "block tokens/s",
-            "cores": threads, "kind": "oracle",
+            "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"first {done} of {fc.batch} sequences of chain_b1024, whole step, "
                       f"{elapsed:.1f} s (numpy float64; BLAS threads = {threads})"}
 
