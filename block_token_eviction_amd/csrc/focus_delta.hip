@@ -261,12 +261,22 @@ __global__ __launch_bounds__(64 * kWaves) void focus_delta_kernel(
     __builtin_amdgcn_wave_barrier();
     const char* src = wring + stage * Tl::kBytes;
     const int t = tile % per_group;
+    // Each tile is read from LDS into registers first; as soon as those reads
+    // have landed the stage is refilled kStages tiles ahead, so the copy is in
+    // flight during this tile's MFMA and softmax work.
+    auto refill = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      __builtin_amdgcn_wave_barrier();
+      if (tile + kStages < ntiles) issue(tile + kStages, stage);
+    };
     if (t < 2) {
       if (t == 0) read_half<D, BF16>(K0, src, kj, h);
       else read_half<D, BF16>(K1, src, kj, h);
+      refill();
     } else {
       Row Q;
       read_half<D, BF16>(Q, src, n, h);
+      refill();
       f32x16 s;
       if (t & 1) s = score_tile<D, BF16>(K1, Q);
       else s = score_tile<D, BF16>(K0, Q);
@@ -277,9 +287,6 @@ __global__ __launch_bounds__(64 * kWaves) void focus_delta_kernel(
       if (t & 1) pool_softmax_accumulate<R>(s, h, rt_r, B, c, qvalid, acc1);
       else pool_softmax_accumulate<R>(s, h, rt_r, B, c, qvalid, acc0);
     }
-    __builtin_amdgcn_wave_barrier();
-    // The stage has been read into registers: refill it kStages tiles ahead.
-    if (tile + kStages < ntiles) issue(tile + kStages, stage);
   }
 
   // Sum over the 32 query rows held by each lane half (fixed butterfly order).
