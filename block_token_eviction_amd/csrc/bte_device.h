@@ -78,6 +78,19 @@ __device__ __forceinline__ float swap_halves(float v) { return __shfl_xor(v, 32,
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// LDS reads for kernels that keep HBM->LDS copies (global_load_lds) in flight.
+// The compiler cannot tell which LDS bytes those copies write, so before a plain
+// LDS load it waits for every copy in flight (s_waitcnt vmcnt(0)) and the copy
+// pipeline drains. These reads are inline asm, which the compiler does not
+// track: the kernel's own vmcnt waits must make the data land first, and a
+// result may only be used after an asm s_waitcnt lgkmcnt that takes it as an
+// in/out operand.
+__device__ __forceinline__ u32x4 lds_read16(const void* p) {
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(a) : "memory");
+  return v;
+}
 // s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14; expcnt and
 // lgkmcnt left at their maxima, i.e. not waited on. Used to wait for all but
 // the newest N HBM->LDS copies of a wave.

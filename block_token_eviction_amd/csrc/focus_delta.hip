@@ -55,6 +55,11 @@ struct HalfRow {
   u32x4 v[Tile<D, BF16>::kHalf];
 };
 
+// Plain LDS loads: the compiler then also waits for the other stage's copy in
+// flight before them, so about one tile per wave is in flight. Reading through
+// inline asm instead (which keeps both stages in flight) measured slower,
+// 123 us against 115 us at batch 1,024: these tiles are 32 scattered 256-byte
+// rows each, and fewer outstanding requests stream them better.
 template <int D, bool BF16>
 __device__ __forceinline__ void read_half(HalfRow<D, BF16>& r, const char* tile, int row, int h) {
   using Tl = Tile<D, BF16>;

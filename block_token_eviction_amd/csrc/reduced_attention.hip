@@ -78,6 +78,28 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
   asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(a) : "memory");
   return v;
 }
+// K operands are read with lds_read16 (inline asm, so that the compiler does not
+// wait for the copies in flight before them), one chunk ahead of their MFMAs.
+// lds_wait16 waits until v has arrived, with at most N (0 or 1) LDS reads
+// issued after it still outstanding (LDS reads return in order).
+template <int N>
+__device__ __forceinline__ void lds_wait16(u32x4& v) {
+  static_assert(N == 0 || N == 1, "one read in flight at most");
+  if constexpr (N == 0)
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v) : : "memory");
+  else
+    asm volatile("s_waitcnt lgkmcnt(1)" : "+v"(v) : : "memory");
+}
+
+// Page-table entry from its LDS copy, read as inline asm for the same reason
+// (the value is waited for inside the asm).
+__device__ __forceinline__ int lds_read_page(const int32_t* p) {
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int32_t*)p;
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+  return v;
+}
+
 // Waits for all outstanding LDS reads; the results are in/out operands, so no
 // use of them can be scheduled before the wait.
 template <int N>
@@ -182,7 +204,7 @@ __device__ __forceinline__ void attn_body(
       return (size_t)p;
     } else {
       const int lg = map.lg_page;
-      const int page = kPaged == kPagedLds ? pages[p >> lg] : bt[p >> lg];
+      const int page = kPaged == kPagedLds ? lds_read_page(pages + (p >> lg)) : bt[p >> lg];
       return ((size_t)page << lg) + (size_t)(p & ((1 << lg) - 1));
     }
   };
@@ -198,7 +220,13 @@ __device__ __forceinline__ void attn_body(
     const int head = g * G + (ok ? rho - tok * G : 0);
     const char* p = q + (((size_t)(cub + tok)) * hq + head) * C::kRowBytes + h * (C::kRowBytes / 2);
 #pragma unroll
-    for (int cc = 0; cc < C::kHalf; ++cc) qop[tq][cc] = ok ? ld16(p + 16 * cc) : u32x4{0u, 0u, 0u, 0u};
+    // Unconditional loads (rows past the end read a valid row and are zeroed):
+    // a branch around them would hide from the compiler that the prologue's
+    // wait completes them, and it would then wait for every copy in the loop.
+    for (int cc = 0; cc < C::kHalf; ++cc) {
+      const u32x4 v = ld16(p + 16 * cc);
+      qop[tq][cc] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+    }
   }
 
   float m[T], lsum[T];
@@ -234,7 +262,8 @@ __device__ __forceinline__ void attn_body(
     } else {
       const int p = kt * 32;
       const int lg = map.lg_page;
-      const int page = __builtin_amdgcn_readfirstlane(kPaged == kPagedLds ? pages[p >> lg] : bt[p >> lg]);
+      const int page = __builtin_amdgcn_readfirstlane(
+          kPaged == kPagedLds ? lds_read_page(pages + (p >> lg)) : bt[p >> lg]);
       return ((size_t)page << lg) + (size_t)(p & ((1 << lg) - 1));
     }
   };
@@ -283,10 +312,22 @@ __device__ __forceinline__ void attn_body(
     return row * C::kRowBytes + (vpos(row, byte >> 4) << 4) + (byte & 15);
   };
 
-  // Prologue: this wave's first kStages tiles, one per stage.
+  // Prologue: this wave's first kStages tiles, one per stage. A wave with key
+  // tiles always issues kStages of them (past its last tile it repeats that
+  // tile into a stage the loop does not read), so that a fixed number of copies
+  // follows the query loads. Waiting until only those copies are outstanding
+  // completes the query loads while the copies stream; the compiler then knows
+  // them complete and puts no wait for them into the tile loop, where it would
+  // have to wait for every copy in flight.
+  static_assert(C::kStages * 2 * C::kHalf <= 63, "vmcnt holds at most 63");
+  if (kt0 < ntiles) {
+    const int last = kt0 + (ntiles - 1 - kt0) / kStep * kStep;    // this wave's last tile
 #pragma unroll
-  for (int st = 0; st < C::kStages; ++st)
-    if (kt0 + st * kStep < ntiles) issue_tile(kt0 + st * kStep, st);
+    for (int st = 0; st < C::kStages; ++st) issue_tile(min(kt0 + st * kStep, last), st);
+    __builtin_amdgcn_s_waitcnt(kVmcntNoLgkm | vmcnt_bits(C::kStages * 2 * C::kHalf));
+  } else {
+    __builtin_amdgcn_s_waitcnt(kVmcntNoLgkm | vmcnt_bits(0));
+  }
   int stage = 0;
   for (int kt = kt0; kt < ntiles; kt += kStep) {
     // Wait for this tile's copies; those of the wave's later tiles already
@@ -301,10 +342,19 @@ __device__ __forceinline__ void attn_body(
     f32x16 s[T];
 #pragma unroll
     for (int tq = 0; tq < T; ++tq) s[tq] = f32x16{};
+    // K operands, read one chunk ahead of the MFMAs that use them.
+    const char* krow = kt_lds + kj * C::kRowBytes;
+    u32x4 kop[C::kHalf];
+    kop[0] = lds_read16(krow + (kpos(kj, h * C::kHalf) << 4));
 #pragma unroll
     for (int cc = 0; cc < C::kHalf; ++cc) {
-      const int chunk = h * C::kHalf + cc;
-      const u32x4 ka = ld16(kt_lds + kj * C::kRowBytes + (kpos(kj, chunk) << 4));
+      if (cc + 1 < C::kHalf) {
+        kop[cc + 1] = lds_read16(krow + (kpos(kj, h * C::kHalf + cc + 1) << 4));
+        lds_wait16<1>(kop[cc]);
+      } else {
+        lds_wait16<0>(kop[cc]);
+      }
+      const u32x4 ka = kop[cc];
 #pragma unroll
       for (int tq = 0; tq < T; ++tq) {
         if constexpr (BF16) {
@@ -418,6 +468,9 @@ __device__ __forceinline__ void attn_body(
     if (refill < ntiles) issue_half(refill, stage, 1, refill_row);
     stage = stage + 1 == C::kStages ? 0 : stage + 1;
   }
+  // Every copy has landed (the last tile's wait took all of them); the merge
+  // below reuses the stage memory.
+  __builtin_amdgcn_s_waitcnt(kVmcntNoLgkm | vmcnt_bits(0));
 
   // Merge the 4 wave states: out = sum_w e^(m_w - M) O_w / sum_w e^(m_w - M) l_w.
   float* obuf = reinterpret_cast<float*>(smem);
