@@ -3,7 +3,11 @@
 Usage:
   python profile_summary.py trace  <kernel_stats.csv> <out.md> "<command>"
   python profile_summary.py counters <fetch_counter_collection.csv> <write_counter_collection.csv>
-        <kernel-substring> <source-key> <out.json> "<fetch command>" "<write command>"
+        <kernel-substring> <source-key> <out.json> "<fetch command>" "<write command>" [<grid size>]
+
+The optional grid size (work-items, as rocprofv3 reports it) keeps only the
+dispatches of that size, for a kernel that bench.py also launches at other
+batch sizes.
 
 <source-key> names the kernel's source files in bench.KERNEL_SOURCES.
 
@@ -46,16 +50,18 @@ def trace(stats_csv: str, out_md: str, command: str):
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
-def _per_kernel(path, counter, sub):
-    """Counter values of the named kernel's dispatches, and of the calibration copy
-    (the last copy dispatch with the largest grid: bench.py issues it last)."""
+def _per_kernel(path, counter, sub, grid=None):
+    """Counter values of the named kernel's dispatches (of grid size `grid`, if
+    given), and of the calibration copy (the last copy dispatch with the
+    largest grid: bench.py issues it last)."""
     vals, copies = [], []
     for r in _rows(path):
         if r["Counter_Name"] != counter:
             continue
         v = float(r["Counter_Value"])
         if sub in r["Kernel_Name"]:
-            vals.append(v)
+            if grid is None or int(r["Grid_Size"]) == grid:
+                vals.append(v)
         elif COPY_KERNEL in r["Kernel_Name"]:
             copies.append((int(r["Grid_Size"]), int(r["Dispatch_Id"]), v))
     big = max(g for g, _, _ in copies)
@@ -63,15 +69,16 @@ def _per_kernel(path, counter, sub):
     return vals, cal
 
 
-def counters(fetch_csv, write_csv, sub, source_key, out_json, fetch_cmd, write_cmd):
-    f, fcal = _per_kernel(fetch_csv, "FETCH_SIZE", sub)
-    w, wcal = _per_kernel(write_csv, "WRITE_SIZE", sub)
+def counters(fetch_csv, write_csv, sub, source_key, out_json, fetch_cmd, write_cmd, grid=None):
+    grid = None if grid is None else int(grid)
+    f, fcal = _per_kernel(fetch_csv, "FETCH_SIZE", sub, grid)
+    w, wcal = _per_kernel(write_csv, "WRITE_SIZE", sub, grid)
     kib = 1024.0
     fscale = bench.COPY_CAL_BYTES / (max(fcal) * kib)
     wscale = bench.COPY_CAL_BYTES / (max(wcal) * kib)
     fetch = statistics.mean(f) * kib * fscale
     write = statistics.mean(w) * kib * wscale
-    rec = {"kernel": sub, "launches": len(f), "fetch_kib_raw": statistics.mean(f),
+    rec = {"kernel": sub, "grid_size": grid, "launches": len(f), "fetch_kib_raw": statistics.mean(f),
            "write_kib_raw": statistics.mean(w), "copy_fetch_kib_raw": max(fcal),
            "copy_write_kib_raw": max(wcal), "copy_bytes": bench.COPY_CAL_BYTES,
            "fetch_scale": fscale, "write_scale": wscale,
@@ -87,4 +94,4 @@ if __name__ == "__main__":
     if sys.argv[1] == "trace":
         trace(*sys.argv[2:5])
     else:
-        counters(*sys.argv[2:9])
+        counters(*sys.argv[2:10])
