@@ -3,11 +3,13 @@
 Usage:
   python profile_summary.py trace  <kernel_stats.csv> <out.md> "<command>"
   python profile_summary.py counters <fetch_counter_collection.csv> <write_counter_collection.csv>
-        <kernel-substring> <source-key> <out.json> "<fetch command>" "<write command>" [<grid size>]
+        <kernel-substring> <source-key> <out.json> "<fetch command>" "<write command>"
+        [grid=<work-items>] [first=<n>]
 
-The optional grid size (work-items, as rocprofv3 reports it) keeps only the
-dispatches of that size, for a kernel that bench.py also launches at other
-batch sizes.
+For a kernel that bench.py also launches in other legs, grid= keeps only the
+dispatches of that grid size (work-items, as rocprofv3 reports it) and first=
+only the first n of those in dispatch order (bench.py runs the main step
+before the extended step and the ES-dLLM legs).
 
 <source-key> names the kernel's source files in bench.KERNEL_SOURCES.
 
@@ -50,10 +52,10 @@ def trace(stats_csv: str, out_md: str, command: str):
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
-def _per_kernel(path, counter, sub, grid=None):
-    """Counter values of the named kernel's dispatches (of grid size `grid`, if
-    given), and of the calibration copy (the last copy dispatch with the
-    largest grid: bench.py issues it last)."""
+def _per_kernel(path, counter, sub, grid=None, first=None):
+    """Counter values of the named kernel's dispatches (of grid size `grid` and
+    the first `first` of them, if given), and of the calibration copy (the last
+    copy dispatch with the largest grid: bench.py issues it last)."""
     vals, copies = [], []
     for r in _rows(path):
         if r["Counter_Name"] != counter:
@@ -61,24 +63,27 @@ def _per_kernel(path, counter, sub, grid=None):
         v = float(r["Counter_Value"])
         if sub in r["Kernel_Name"]:
             if grid is None or int(r["Grid_Size"]) == grid:
-                vals.append(v)
+                vals.append((int(r["Dispatch_Id"]), v))
         elif COPY_KERNEL in r["Kernel_Name"]:
             copies.append((int(r["Grid_Size"]), int(r["Dispatch_Id"]), v))
     big = max(g for g, _, _ in copies)
     cal = [v for g, d, v in sorted(copies, key=lambda x: x[1]) if g == big][-1:]
-    return vals, cal
+    vals = [v for _, v in sorted(vals)]
+    return (vals if first is None else vals[:first]), cal
 
 
-def counters(fetch_csv, write_csv, sub, source_key, out_json, fetch_cmd, write_cmd, grid=None):
-    grid = None if grid is None else int(grid)
-    f, fcal = _per_kernel(fetch_csv, "FETCH_SIZE", sub, grid)
-    w, wcal = _per_kernel(write_csv, "WRITE_SIZE", sub, grid)
+def counters(fetch_csv, write_csv, sub, source_key, out_json, fetch_cmd, write_cmd, *select):
+    opts = dict(a.split("=", 1) for a in select)
+    grid = int(opts["grid"]) if "grid" in opts else None
+    first = int(opts["first"]) if "first" in opts else None
+    f, fcal = _per_kernel(fetch_csv, "FETCH_SIZE", sub, grid, first)
+    w, wcal = _per_kernel(write_csv, "WRITE_SIZE", sub, grid, first)
     kib = 1024.0
     fscale = bench.COPY_CAL_BYTES / (max(fcal) * kib)
     wscale = bench.COPY_CAL_BYTES / (max(wcal) * kib)
     fetch = statistics.mean(f) * kib * fscale
     write = statistics.mean(w) * kib * wscale
-    rec = {"kernel": sub, "grid_size": grid, "launches": len(f), "fetch_kib_raw": statistics.mean(f),
+    rec = {"kernel": sub, "grid_size": grid, "first": first, "launches": len(f), "fetch_kib_raw": statistics.mean(f),
            "write_kib_raw": statistics.mean(w), "copy_fetch_kib_raw": max(fcal),
            "copy_write_kib_raw": max(wcal), "copy_bytes": bench.COPY_CAL_BYTES,
            "fetch_scale": fscale, "write_scale": wscale,
@@ -94,4 +99,4 @@ if __name__ == "__main__":
     if sys.argv[1] == "trace":
         trace(*sys.argv[2:5])
     else:
-        counters(*sys.argv[2:10])
+        counters(*sys.argv[2:9], *sys.argv[9:])
