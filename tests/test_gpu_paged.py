@@ -57,6 +57,12 @@ CFGS = [
                head_dim=64, prefix_lo=30, prefix_hi=200), 256),
     (W.AttnCfg("paged_f32", seed=73, batch=5, kept=4, hq=8, hkv=2, head_dim=128, dtype=W.F32,
                prefix_lo=40, prefix_hi=150), 32),
+    # fp32 head dim 64 through pages smaller than a key tile (one lookup per copy)
+    (W.AttnCfg("paged_f32_d64", seed=76, batch=7, kept=None, k_lo=1, k_hi=8, hq=16, hkv=4,
+               head_dim=64, dtype=W.F32, prefix_lo=1, prefix_hi=120), 8),
+    # head dim 64 with up to 96 query rows per KV head (query split) through the table
+    (W.AttnCfg("paged_d64_qsplit", seed=77, batch=40, kept=None, k_lo=8, k_hi=24, hq=32, hkv=8,
+               head_dim=64, prefix_lo=5, prefix_hi=300), 16),
     # up to 128 query rows per KV head: query-split workgroups through the table
     (W.AttnCfg("paged_qsplit", seed=75, batch=150, kept=None, k_lo=4, k_hi=32, hq=32, hkv=8,
                head_dim=128, prefix_lo=10, prefix_hi=400), 16),
