@@ -15,7 +15,9 @@ roofline of the dominant kernel (reduced attention, HBM-bound) from its
 algorithmic bytes, and the CPU oracle timed on a bounded sample of the same
 workload. The ES-dLLM mode (score -> top-K -> gather -> scatter, batch 8) is
 timed as well and reported under "es_mode", two ES-dLLM skip layers
-(256 -> 128 -> 64 survivors) under "es_pipeline", and the extended FOCUS step
+(256 -> 128 -> 64 survivors) under "es_pipeline", the KV scatter fused into
+the attention (one launch) against the two launches of the main step under
+"fused_scatter_attention", and the extended FOCUS step
 (device budget, constrained selection, one compaction launch for four
 per-token tensors, paged KV pool, delayed commit mask, history update) on the
 same batch-1024 workload under "full_step".
@@ -227,6 +229,7 @@ def main():
                    "ms_per_iteration": round(sum(lay_ms), 4),
                    "survivor positions/s": round(ec.batch * ec.generated / (sum(lay_ms) * 1e-3), 1)}
 
+    fused = fused_scatter_attention_leg(step, x, args.steps, bytes_)
     full = full_step_leg(x, fc, ac, args.steps, args.warmup, dev)
     score_resident = score_resident_leg(dev)
 
@@ -256,12 +259,47 @@ def main():
         "eager_ms_per_step": round(ms_step, 4),
         "graph_ms_per_step": round(graph_ms, 4) if graph_ms is not None else None,
         "eager_step_ms_p10_p50_p90": [round(percentile(step_ms, q), 4) for q in (10, 50, 90)],
-        "full_step": full, "score_resident": score_resident,
+        "full_step": full, "fused_scatter_attention": fused, "score_resident": score_resident,
     }
     print(json.dumps(line), flush=True)
 
 
 COPY_CAL_BYTES = 256 << 20
+
+
+def fused_scatter_attention_leg(step, x, steps: int, bytes_: dict):
+    """The KV scatter fused into the attention (one launch, bitwise the same
+    caches and outputs) against the two launches of the main step, alternated
+    step by step in one process on the batch-1024 workload; HIP events on the
+    launch stream. The fused launch reads the kept rows' K/V once (from the new
+    rows) and writes them into the cache while the K/V stream runs."""
+    import numpy as np
+    import torch
+
+    pos_base = x["prefix"].to(torch.int32)
+    step.schedule(x["kv_len"])
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    sep, fus = [], []
+    for _ in range(steps + 2):
+        e = [ev() for _ in range(4)]
+        e[0].record()
+        step.scatter(x["new_k"], x["new_v"], x["row_base"], x["cache_k"], x["cache_v"])
+        step.attend(x["q_kept"], x["cache_k"], x["cache_v"], x["seq_start"], x["kv_len"])
+        e[1].record()
+        e[2].record()
+        step.scatter_attend(x["q_kept"], x["new_k"], x["new_v"], pos_base, x["cache_k"],
+                            x["cache_v"], x["seq_start"], x["kv_len"])
+        e[3].record()
+        torch.cuda.synchronize()
+        sep.append(e[0].elapsed_time(e[1]))
+        fus.append(e[2].elapsed_time(e[3]))
+    sep, fus = float(np.median(sep[2:])), float(np.median(fus[2:]))
+    fused_bytes = bytes_["reduced_attention"] + bytes_["kv_scatter"] // 2   # + the cache writes
+    return {"workload": "chain_b1024 (scatter + attention of the main step)",
+            "separate_ms": round(sep, 4), "fused_ms": round(fus, 4),
+            "fused_algo_bytes": int(fused_bytes),
+            "fused_GB/s": round(fused_bytes / (fus * 1e-3) / 1e9, 1),
+            "fused_hbm_frac": round(fused_bytes / (fus * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def score_flops(batch: int, block: int, hq: int, head_dim: int) -> int:

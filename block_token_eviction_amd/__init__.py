@@ -23,7 +23,7 @@ __all__ = ["lib", "LIB_PATH", "BteError", "status_string", "focus_importance_del
            "esdllm_score", "topk_select", "gather_rows", "kv_scatter", "reduced_attention",
            "attention_order", "reduced_attention_paged", "kv_scatter_paged", "focus_budget",
            "focus_history_update", "focus_select", "focus_commit_mask", "gather_rows_multi",
-           "BTE_F32", "BTE_BF16", "contract"]
+           "kv_scatter_attention", "kv_scatter_attention_paged", "BTE_F32", "BTE_BF16", "contract"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbte.so")
 BTE_F32, BTE_BF16 = 0, 1
@@ -53,6 +53,10 @@ _SIG = {
     "bte_focus_select": ([_p, _p, _p, _p, _p, _p, _p, _i, _i, _p], _i),
     "bte_focus_commit_mask": ([_p, _p, _p, _p, _i, _i, _p], _i),
     "bte_gather_rows_multi": ([_p, _i, _p, _p, _p, _i, _i, _i, _p], _i),
+    "bte_kv_scatter_attention": ([_p, _p, _p, _p, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i,
+                                  _i, _i, _i, _f, _i, _p], _i),
+    "bte_kv_scatter_attention_paged": ([_p, _p, _p, _p, _i, _p, _p, _p, _p, _p, _p, _i, _i, _p, _p,
+                                        _p, _i, _i, _i, _i, _i, _f, _i, _p], _i),
 }
 for _name, (_args, _res) in _SIG.items():
     _fn = getattr(lib, _name)
@@ -229,6 +233,44 @@ def reduced_attention(q, count, cu, cache_k, cache_v, seq_start, kv_len, k_max: 
     return out
 
 
+def kv_scatter_attention(q, count, cu, idx, n: int, pos_base, new_k, new_v, cache_k, cache_v,
+                         seq_start, kv_len, k_max: int, scale: float | None = None, out=None,
+                         order=None):
+    """kv_scatter into rows seq_start[b] + pos_base[b] + idx, then reduced_attention, in one launch.
+
+    idx int32 [batch, k_max] block indices in [0, n); pos_base int32 [batch]. The cache is
+    updated in place and out [capacity, hq, D] (rows cu[b]+t) is the attention over it."""
+    _dev(q, count, cu, idx, pos_base, new_k, new_v, cache_k, cache_v, seq_start, kv_len, out, order)
+    _want(seq_start, torch.int64, "seq_start")
+    _want(kv_len, torch.int32, "kv_len")
+    _want(pos_base, torch.int32, "pos_base")
+    _want(idx, torch.int32, "idx")
+    hq, d = q.shape[1], q.shape[2]
+    hkv = cache_k.shape[1]
+    batch = count.shape[0]
+    assert idx.shape == (batch, k_max) and pos_base.shape == (batch,)
+    assert cache_v.shape == cache_k.shape and cache_k.dtype == q.dtype
+    assert new_k.shape[1:] == cache_k.shape[1:] and new_v.shape == new_k.shape
+    assert new_k.dtype == q.dtype and new_v.dtype == q.dtype
+    if order is not None:
+        _want(order, torch.int32, "order")
+        assert order.shape == (batch,)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if contract.enabled():
+        contract.check_attention(count, cu, kv_len, k_max, min(q.shape[0], out.shape[0]),
+                                 seq_start=seq_start, cache_rows=cache_k.shape[0], order=order)
+        contract.check_fused_scatter(idx, count, cu, k_max, n, pos_base, kv_len, new_k.shape[0],
+                                     seq_start=seq_start, cache_rows=cache_k.shape[0])
+    _check("bte_kv_scatter_attention", lib.bte_kv_scatter_attention(
+        _ptr(q), _ptr(count), _ptr(cu), _ptr(idx), n, _ptr(pos_base), _ptr(new_k), _ptr(new_v),
+        _ptr(cache_k), _ptr(cache_v), _ptr(seq_start), _ptr(kv_len), _ptr(order), _ptr(out), batch,
+        k_max, hq, hkv, d, float(scale), _dtype(q), _stream()))
+    return out
+
+
 def attention_order(kv_len, out=None):
     """kv_len int32 [batch] -> order int32 [batch]: sequences by length descending, index ascending."""
     _dev(kv_len, out)
@@ -321,6 +363,47 @@ def reduced_attention_paged(q, count, cu, cache_k, cache_v, block_table, page_si
         _ptr(q), _ptr(count), _ptr(cu), _ptr(cache_k), _ptr(cache_v), _ptr(block_table),
         block_table.shape[1], page_size, _ptr(kv_len), _ptr(order), _ptr(out), batch, k_max, hq,
         hkv, d, float(scale), _dtype(q), _stream()))
+    return out
+
+
+def kv_scatter_attention_paged(q, count, cu, idx, n: int, pos_base, new_k, new_v, cache_k, cache_v,
+                               block_table, page_size: int, kv_len, k_max: int,
+                               scale: float | None = None, out=None, order=None):
+    """kv_scatter_paged (logical positions pos_base[b] + idx) then reduced_attention_paged,
+    in one launch over the same page pool and table."""
+    _dev(q, count, cu, idx, pos_base, new_k, new_v, cache_k, cache_v, block_table, kv_len, out,
+         order)
+    _want(block_table, torch.int32, "block_table")
+    _want(kv_len, torch.int32, "kv_len")
+    _want(pos_base, torch.int32, "pos_base")
+    _want(idx, torch.int32, "idx")
+    hq, d = q.shape[1], q.shape[2]
+    hkv = cache_k.shape[1]
+    batch = count.shape[0]
+    assert idx.shape == (batch, k_max) and pos_base.shape == (batch,)
+    assert cache_v.shape == cache_k.shape and cache_k.dtype == q.dtype
+    assert new_k.shape[1:] == cache_k.shape[1:] and new_v.shape == new_k.shape
+    assert new_k.dtype == q.dtype and new_v.dtype == q.dtype
+    assert block_table.shape[0] == batch
+    if order is not None:
+        _want(order, torch.int32, "order")
+        assert order.shape == (batch,)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if contract.enabled():
+        contract.check_attention(count, cu, kv_len, k_max, min(q.shape[0], out.shape[0]),
+                                 cache_rows=cache_k.shape[0], block_table=block_table,
+                                 page_size=page_size, order=order)
+        contract.check_fused_scatter(idx, count, cu, k_max, n, pos_base, kv_len, new_k.shape[0],
+                                     cache_rows=cache_k.shape[0], block_table=block_table,
+                                     page_size=page_size)
+    _check("bte_kv_scatter_attention_paged", lib.bte_kv_scatter_attention_paged(
+        _ptr(q), _ptr(count), _ptr(cu), _ptr(idx), n, _ptr(pos_base), _ptr(new_k), _ptr(new_v),
+        _ptr(cache_k), _ptr(cache_v), _ptr(block_table), block_table.shape[1], page_size,
+        _ptr(kv_len), _ptr(order), _ptr(out), batch, k_max, hq, hkv, d, float(scale), _dtype(q),
+        _stream()))
     return out
 
 

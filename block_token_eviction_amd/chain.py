@@ -20,6 +20,12 @@ keep the top ones, gather their rows, scatter their new K/V in place):
 
     esdllm_score -> topk_select -> gather_rows -> kv_scatter
 
+In both FOCUS steps the KV scatter and the attention can run as one launch
+(kv_scatter_attention / kv_scatter_attention_paged, bitwise the same caches
+and outputs): the attention takes the kept positions' K/V from the new rows
+and writes them into the cache, so the scattered bytes ride in the
+attention's stream instead of a separate short launch.
+
 ES-dLLM skip layer (the same page: at a skip layer the survivors are scored,
 the layer's hidden-state cache is updated in place at every survivor, and
 only the top (1 - r)|S| survivors go on to the next layer):
@@ -39,8 +45,8 @@ import torch
 
 from . import (attention_order, esdllm_score, focus_budget, focus_commit_mask,
                focus_history_update, focus_importance_delta, focus_select, gather_rows,
-               gather_rows_multi, kv_scatter, kv_scatter_paged, reduced_attention,
-               reduced_attention_paged, topk_select)
+               gather_rows_multi, kv_scatter, kv_scatter_attention, kv_scatter_attention_paged,
+               kv_scatter_paged, reduced_attention, reduced_attention_paged, topk_select)
 
 
 class FocusStep:
@@ -78,14 +84,26 @@ class FocusStep:
         return reduced_attention(q_kept, self.count, self.cu, cache_k, cache_v, seq_start, kv_len,
                                  self.k_max, self.scale, out=self.out, order=self.order)
 
+    def scatter_attend(self, q_kept, new_k, new_v, pos_base, cache_k, cache_v, seq_start, kv_len):
+        """scatter (into rows seq_start + pos_base + idx) and attend in one launch."""
+        return kv_scatter_attention(q_kept, self.count, self.cu, self.idx, self.block, pos_base,
+                                    new_k, new_v, cache_k, cache_v, seq_start, kv_len, self.k_max,
+                                    self.scale, out=self.out, order=self.order)
+
     def run(self, *, q0, k0, q1, k1, decoded, k, hidden_rows, pool_kernel, new_k, new_v, q_kept,
-            cache_k, cache_v, seq_start, kv_len, row_base):
+            cache_k, cache_v, seq_start, kv_len, row_base=None, pos_base=None, fused=False):
+        """fused: one scatter + attention launch (needs pos_base, int32 [batch], the block's
+        first KV position); otherwise kv_scatter into row_base, then reduced_attention."""
         self.score(q0, k0, q1, k1, decoded, pool_kernel)
         self.select(k)
         self.gather(hidden_rows)
-        self.scatter(new_k, new_v, row_base, cache_k, cache_v)
-        self.schedule(kv_len)
-        self.attend(q_kept, cache_k, cache_v, seq_start, kv_len)
+        if fused:
+            self.schedule(kv_len)
+            self.scatter_attend(q_kept, new_k, new_v, pos_base, cache_k, cache_v, seq_start, kv_len)
+        else:
+            self.scatter(new_k, new_v, row_base, cache_k, cache_v)
+            self.schedule(kv_len)
+            self.attend(q_kept, cache_k, cache_v, seq_start, kv_len)
         return self.out
 
 
@@ -140,6 +158,14 @@ class FocusFullStep:
                                        page_size, kv_len, self.block, self.scale, out=self.out,
                                        order=self.order)
 
+    def scatter_attend(self, q_kept, new_k, new_v, pos_base, block_table, page_size, pool_k,
+                       pool_v, kv_len):
+        """scatter (logical positions pos_base + idx) and attend in one launch."""
+        return kv_scatter_attention_paged(q_kept, self.count, self.cu, self.idx, self.block,
+                                          pos_base, new_k, new_v, pool_k, pool_v, block_table,
+                                          page_size, kv_len, self.block, self.scale, out=self.out,
+                                          order=self.order)
+
     def commit_mask(self, decoded, cached):
         return focus_commit_mask(decoded, cached, self.commit, self.block_done)
 
@@ -148,14 +174,19 @@ class FocusFullStep:
 
     def run(self, *, q0, k0, q1, k1, decoded, decoded_now, pool_kernel, alpha, token_sum,
             total_steps, rightmost_processed, cached, per_token, new_k, new_v, q_kept, pos_base,
-            block_table, page_size, pool_k, pool_v, kv_len, threshold_mode=0):
+            block_table, page_size, pool_k, pool_v, kv_len, threshold_mode=0, fused=False):
         self.score(q0, k0, q1, k1, decoded, pool_kernel)
         self.budget(token_sum, total_steps, alpha, threshold_mode)
         self.select(decoded, rightmost_processed)
         self.compact(per_token)
-        self.scatter(new_k, new_v, pos_base, block_table, page_size, pool_k, pool_v)
-        self.schedule(kv_len)
-        self.attend(q_kept, pool_k, pool_v, block_table, page_size, kv_len)
+        if fused:
+            self.schedule(kv_len)
+            self.scatter_attend(q_kept, new_k, new_v, pos_base, block_table, page_size, pool_k,
+                                pool_v, kv_len)
+        else:
+            self.scatter(new_k, new_v, pos_base, block_table, page_size, pool_k, pool_v)
+            self.schedule(kv_len)
+            self.attend(q_kept, pool_k, pool_v, block_table, page_size, kv_len)
         self.commit_mask(decoded, cached)
         self.history(decoded, decoded_now, token_sum, total_steps)
         return self.out

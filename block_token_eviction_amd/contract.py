@@ -155,3 +155,52 @@ def check_positions(pos, limit: int, name: str):
     p = _np(pos)
     if p.size and (p.min() < 0 or p.max() >= limit):
         _fail(f"{name} has an entry outside [0, {limit})")
+
+
+def check_fused_scatter(idx, count, cu, k_max: int, n: int, pos_base, kv_len, new_rows: int,
+                        seq_start=None, cache_rows: int | None = None, block_table=None,
+                        page_size: int = 0):
+    """Scatter fused into the attention: the kept rows' block indices in
+    [0, n), each target position pos_base[b] + idx inside [0, kv_len[b]), and
+    no written cache row inside another attending sequence's KV rows (that
+    sequence would read it during the same launch). Cache rows are
+    seq_start[b] + position (contiguous) or pool rows through block_table."""
+    check_rows(idx, count, cu, k_max, n=n, in_rows=new_rows)
+    pb, kv = _np(pos_base).astype(np.int64), _np(kv_len).astype(np.int64)
+    cnt = _np(count).astype(np.int64)
+    pos = _positions(idx, count, None)
+    for b, p in enumerate(pos):
+        q = pb[b] + p
+        if q.size and (q.min() < 0 or q.max() >= kv[b]):
+            _fail(f"sequence {b}: a scatter target position is outside [0, kv_len = {kv[b]})")
+    if seq_start is not None:
+        ss = _np(seq_start).astype(np.int64)
+        rows = [ss[b] + pb[b] + p for b, p in enumerate(pos)]
+        readers = [(ss[b], ss[b] + kv[b]) for b in range(cnt.shape[0])]
+    elif block_table is not None:
+        bt = _np(block_table)
+        rows = [_page_rows(bt, page_size, b, pb[b] + p, cache_rows) for b, p in enumerate(pos)]
+        readers = None
+    else:
+        return
+    t = np.concatenate(rows) if rows else np.zeros(0, np.int64)
+    owner = np.concatenate([np.full(r.size, b, np.int64) for b, r in enumerate(rows)]) \
+        if rows else np.zeros(0, np.int64)
+    if np.unique(t).size != t.size:
+        _fail("two scattered rows target the same cache row")
+    if not t.size:
+        return
+    order = np.argsort(t)
+    t, owner = t[order], owner[order]
+    for b in np.flatnonzero(cnt > 0):
+        if readers is not None:
+            lo, hi = readers[b]
+            sel = slice(np.searchsorted(t, lo), np.searchsorted(t, hi))
+            hit = owner[sel]
+        else:
+            read = _page_rows(bt, page_size, int(b), np.arange(int(kv[b]), dtype=np.int64),
+                              cache_rows)
+            hit = owner[np.isin(t, read)]
+        if (hit != b).any():
+            _fail(f"sequence {int(b)} reads a cache row that sequence "
+                  f"{int(hit[hit != b][0])} writes in the same launch")

@@ -91,9 +91,9 @@ __device__ __forceinline__ void lds_wait16(u32x4& v) {
     asm volatile("s_waitcnt lgkmcnt(1)" : "+v"(v) : : "memory");
 }
 
-// Page-table entry from its LDS copy, read as inline asm for the same reason
-// (the value is waited for inside the asm).
-__device__ __forceinline__ int lds_read_page(const int32_t* p) {
+// Page-table entry from its LDS copy, read as inline asm
+// for the same reason (the value is waited for inside the asm).
+__device__ __forceinline__ int lds_read_word(const int32_t* p) {
   const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int32_t*)p;
   int v;
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
@@ -142,6 +142,27 @@ struct KvMap {
   int lg_page;
 };
 
+// The fused KV scatter (kScatter): kept row t < count[b] of sequence b brings
+// new K/V rows cu[b] + t of new_k/new_v, which belong at KV position
+// pos_base[b] + idx[b, t] (idx ascending in [0, n)). The attention copies
+// those positions' tile rows from new_k/new_v instead of the cache, and the
+// workgroup of query row group 0 writes them from its LDS tiles into the
+// cache once it has used them (so the scattered bytes are read from HBM once,
+// by the attention). The cache rows written are never read by the launch, so
+// the writes need no ordering against the reads.
+struct KvScatter {
+  const char* new_k;
+  const char* new_v;
+  const int32_t* idx;         // [batch, k_max]
+  const int32_t* pos_base;    // [batch]
+  char* cache_k;              // the caches again, writable
+  char* cache_v;
+  int n, k_max;
+};
+// Largest n: the kept set of a block is a 64-bit mask (bit j = block index j
+// kept), and kept row t at index j is the number of kept indices below j.
+constexpr int kScatterSpan = 64;
+
 // Waits until at most `behind` tiles of kPerTile copies each are still in
 // flight (s_waitcnt needs an immediate; behind <= kMax).
 template <int kMax, int kPerTile>
@@ -175,12 +196,15 @@ constexpr int kPageCache = 2048;
 // query rows from row0 + 32*T*w and every key tile (each wave streams the same
 // K/V through its own LDS stages, side by side on one CU, so the second read of
 // a tile is mostly an L2 hit instead of a second pass over HBM).
-template <int D, bool BF16, int T, int kWaves, int kPaged, bool kQSplit>
+// kScatter: the KV positions [pb, pb + sc.n) may hold kept rows; bit j of
+// `kept` marks block index j (position pb + j) as kept.
+template <int D, bool BF16, int T, int kWaves, int kPaged, bool kQSplit, bool kScatter>
 __device__ __forceinline__ void attn_body(
     char* __restrict__ smem, const int32_t* __restrict__ pages, const char* __restrict__ q,
     const int32_t* __restrict__ cu, const char* __restrict__ cache_k,
     const char* __restrict__ cache_v, const KvMap& map, const int32_t* __restrict__ kv_len,
-    char* __restrict__ out, int hq, int hkv, float c, int b, int g, int rows, int row0) {
+    char* __restrict__ out, int hq, int hkv, float c, int b, int g, int rows, int row0,
+    const KvScatter& sc, uint64_t kept, int pb) {
   using C = Cfg<D, BF16, kWaves>;
   constexpr int DT = D / 32;                           // 32-wide output column tiles
   const int G = hq / hkv;
@@ -204,7 +228,7 @@ __device__ __forceinline__ void attn_body(
       return (size_t)p;
     } else {
       const int lg = map.lg_page;
-      const int page = kPaged == kPagedLds ? lds_read_page(pages + (p >> lg)) : bt[p >> lg];
+      const int page = kPaged == kPagedLds ? lds_read_word(pages + (p >> lg)) : bt[p >> lg];
       return ((size_t)page << lg) + (size_t)(p & ((1 << lg) - 1));
     }
   };
@@ -256,6 +280,38 @@ __device__ __forceinline__ void attn_body(
   // from the row of its first position: one page lookup serves all its copies,
   // K and V. Smaller pages take one lookup per copy.
   const bool tile_in_page = kPaged == kContig || map.lg_page >= 5;
+  // Fused scatter: whether key tile kt holds positions of the block, and the
+  // kept row at block index j (-1 if j is not kept or outside the block).
+  auto in_block = [&](int kt) { return kt * 32 < pb + sc.n && kt * 32 + 32 > pb; };
+  auto kept_slot = [&](int j) -> int {
+    const bool hit = (unsigned)j < (unsigned)sc.n && ((kept >> (j & 63)) & 1ull);
+    return hit ? (int)__popcll(kept & ((1ull << (j & 63)) - 1ull)) : -1;
+  };
+  // The writes of the kept rows: query row group 0 writes them, from the wave
+  // that holds the tile (every wave holds every tile under the query split:
+  // wave 0 there). write_kept copies the kept rows of the K (which = 0) or V
+  // tile kt from LDS into the cache, 16 bytes per lane, once the tile has
+  // been used and before its stage is refilled. Stores are counted by vmcnt
+  // too, but loads complete in order among themselves, so the tile waits below
+  // stay exact: an outstanding store can only make them wait longer.
+  const bool writer = kScatter && row0 == 0 && (!kQSplit || w == 0);
+  auto write_kept = [&](int kt, const char* tile, int which) {
+    const int last = L - 1 - kt * 32;
+    char* cbase = (which ? sc.cache_v : sc.cache_k) + seq_off + (size_t)g * C::kRowBytes;
+#pragma unroll
+    for (int r0 = 0; r0 < 32; r0 += C::kRpi) {
+      const int row = r0 + lrow;
+      const int p = kt * 32 + row;
+      const bool hit = row <= last && kept_slot(p - pb) >= 0;
+      if (__ballot(hit) == 0) continue;                  // wave-uniform
+      if (hit) {
+        const int s = which ? vpos(row, lslot) : kpos(row, lslot);
+        u32x4 v = lds_read16(tile + row * C::kRowBytes + 16 * s);
+        lds_wait16<0>(v);
+        st16(cbase + kv_pos_row(p) * kv_row + 16 * lslot, v);
+      }
+    }
+  };
   auto tile_row = [&](int kt) -> size_t {
     if constexpr (kPaged == kContig) {
       return (size_t)kt * 32;
@@ -263,7 +319,7 @@ __device__ __forceinline__ void attn_body(
       const int p = kt * 32;
       const int lg = map.lg_page;
       const int page = __builtin_amdgcn_readfirstlane(
-          kPaged == kPagedLds ? lds_read_page(pages + (p >> lg)) : bt[p >> lg]);
+          kPaged == kPagedLds ? lds_read_word(pages + (p >> lg)) : bt[p >> lg]);
       return ((size_t)page << lg) + (size_t)(p & ((1 << lg) - 1));
     }
   };
@@ -274,7 +330,24 @@ __device__ __forceinline__ void attn_body(
   auto issue_half = [&](int kt, int stage, int which, size_t trow) {
     char* dst = wave_lds + stage * C::kStageBytes + which * C::kTile;
     const char* base = which ? vbase : kbase;
-    if (kt * 32 + 32 <= L) {
+    if (kScatter && in_block(kt)) {
+      // A tile holding positions that may be kept rows: each row comes from
+      // its new K/V row when it is one, else from the cache (rows past the
+      // sequence end repeat its last row, as below).
+      const char* nbase = (which ? sc.new_v : sc.new_k) + (size_t)g * C::kRowBytes;
+      const int last = L - 1 - kt * 32;
+#pragma unroll
+      for (int i = 0; i < C::kHalf; ++i) {
+        const int row = C::kRpi * i + lrow;
+        const int p = kt * 32 + (row < last ? row : last);
+        const int j = p - pb;
+        const int t = kept_slot(j);
+        const int chunk = which ? vpos(row, lslot) : kpos(row, lslot);
+        const char* src = t >= 0 ? nbase + (size_t)(cub + t) * kv_row + 16 * chunk
+                                 : base + kv_pos_row(p) * kv_row + 16 * chunk;
+        copy16_to_lds(src, dst + 1024 * i);
+      }
+    } else if (kt * 32 + 32 <= L) {
 #pragma unroll
       for (int i = 0; i < C::kHalf; ++i) {
         const int row = C::kRpi * i + lrow;
@@ -366,6 +439,8 @@ __device__ __forceinline__ void attn_body(
         }
       }
     }
+
+    if (writer && in_block(kt)) write_kept(kt, kt_lds, 0);
 
     // The K half of the stage is consumed: refill it with tile kt + kStages*kStep
     // now (the V half follows after P.V), once the operand reads have landed.
@@ -464,6 +539,7 @@ __device__ __forceinline__ void attn_body(
       }
     }
     __builtin_amdgcn_wave_barrier();
+    if (writer && in_block(kt)) write_kept(kt, vt_lds, 1);
     // The V half is consumed too: refill it.
     if (refill < ntiles) issue_half(refill, stage, 1, refill_row);
     stage = stage + 1 == C::kStages ? 0 : stage + 1;
@@ -572,38 +648,39 @@ __device__ __forceinline__ void attn_body(
 // kQSplitOk: a row group spans 32*T*kWaves query rows; a workgroup with more
 // than 32*T real rows in it splits them over its waves (attn_body kQSplit),
 // one with fewer splits the keys as usual.
-template <int D, bool BF16, int T, int kWaves, int kPaged, bool kQSplitOk>
+template <int D, bool BF16, int T, int kWaves, int kPaged, bool kQSplitOk, bool kScatter>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T == 1 ? 2 : 1))) void attn_kernel(
     const char* __restrict__ q, const int32_t* __restrict__ count, const int32_t* __restrict__ cu,
     const char* __restrict__ cache_k, const char* __restrict__ cache_v, KvMap map,
     const int32_t* __restrict__ kv_len, const int32_t* __restrict__ order, char* __restrict__ out,
-    int batch, int hq, int hkv, int n_rg, int rg_inner, float c) {
+    int batch, int hq, int hkv, int n_rg, int rg_inner, float c, KvScatter sc) {
   __shared__ __attribute__((aligned(16))) char smem[Cfg<D, BF16, kWaves>::kLds];
   __shared__ int32_t pages[kPaged == kPagedLds ? kPageCache : 1];
   int r, g, rg;                                        // r: position in the processing order
   if (rg_inner) {
     const int per_seq = hkv * n_rg;                    // workgroups per sequence
-    const int slot = blockIdx.x / kXcds;
-    const int grp = slot / per_seq;
+    const int s = blockIdx.x / kXcds;
+    const int grp = s / per_seq;
     r = kXcds * grp + (int)(blockIdx.x % kXcds);
-    const int j = slot - grp * per_seq;
+    const int j = s - grp * per_seq;
     rg = j / hkv;
     g = j - rg * hkv;
   } else {
     const int per_rg = (batch + kXcds - 1) / kXcds * kXcds * hkv;   // workgroups per row group
     rg = blockIdx.x / per_rg;
     const int x = blockIdx.x - rg * per_rg;
-    const int slot = x / kXcds;
-    const int grp = slot / hkv;
+    const int s = x / kXcds;
+    const int grp = s / hkv;
     r = kXcds * grp + x % kXcds;
-    g = slot - grp * hkv;
+    g = s - grp * hkv;
   }
   if (r >= batch) return;
   // Workgroups start in index order, so taking the sequences in the caller's
   // order (longest first) keeps long items out of the tail. An entry outside
   // [0, batch) is clamped: a bad order gives wrong results, never a stray access.
   const int b = order ? min(max(order[r], 0), batch - 1) : r;
-  const int rows = count[b] * (hq / hkv);
+  const int cnt = count[b];
+  const int rows = cnt * (hq / hkv);
   constexpr int kSpan = kQSplitOk ? 32 * T * kWaves : 32 * T;   // query rows per row group
   const int row0 = rg * kSpan;
   if (row0 >= rows) return;
@@ -613,22 +690,44 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T =
     for (int i = threadIdx.x; i < n_pages; i += 64 * kWaves) pages[i] = bt[i];
     __syncthreads();
   }
+  int pb = 0;
+  uint64_t kept = 0;
+  if constexpr (kScatter) {
+    // The kept set as a mask, OR-ed over the wave from one index per lane (the
+    // load is unconditional, index clamped into the row, so that it is issued
+    // beside the other per-sequence loads). An index outside [0, n) marks
+    // nothing (it breaks the device contract).
+    const int lane = threadIdx.x & 63;
+    const int j = sc.idx[(size_t)b * sc.k_max + min(lane, sc.k_max - 1)];
+    unsigned long long bit = lane < cnt && j >= 0 && j < sc.n ? 1ull << j : 0ull;
+#pragma unroll
+    for (int x = 32; x > 0; x >>= 1) bit |= __shfl_xor(bit, x, kWave);
+    kept = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(bit >> 32)) << 32) |
+           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bit);
+    pb = __builtin_amdgcn_readfirstlane(sc.pos_base[b]);
+  }
   // Workgroup-uniform choices (every wave of the workgroup takes the same body,
   // so their barriers match): split the query rows when one wave's tiles do not
   // hold them all; otherwise skip query tiles that hold no real row.
+  bool done = false;
   if constexpr (kQSplitOk) {
     if (rows - row0 > 32 * T) {
-      attn_body<D, BF16, T, kWaves, kPaged, true>(smem, pages, q, cu, cache_k, cache_v, map, kv_len,
-                                                  out, hq, hkv, c, b, g, rows, row0);
-      return;
+      attn_body<D, BF16, T, kWaves, kPaged, true, kScatter>(smem, pages, q, cu, cache_k, cache_v,
+                                                            map, kv_len, out, hq, hkv, c, b, g,
+                                                            rows, row0, sc, kept, pb);
+      done = true;
     }
   }
-  if (T == 2 && rows - row0 > 32)
-    attn_body<D, BF16, T, kWaves, kPaged, false>(smem, pages, q, cu, cache_k, cache_v, map, kv_len,
-                                                 out, hq, hkv, c, b, g, rows, row0);
-  else
-    attn_body<D, BF16, 1, kWaves, kPaged, false>(smem, pages, q, cu, cache_k, cache_v, map, kv_len,
-                                                 out, hq, hkv, c, b, g, rows, row0);
+  if (!done) {
+    if (T == 2 && rows - row0 > 32)
+      attn_body<D, BF16, T, kWaves, kPaged, false, kScatter>(smem, pages, q, cu, cache_k, cache_v,
+                                                             map, kv_len, out, hq, hkv, c, b, g,
+                                                             rows, row0, sc, kept, pb);
+    else
+      attn_body<D, BF16, 1, kWaves, kPaged, false, kScatter>(smem, pages, q, cu, cache_k, cache_v,
+                                                             map, kv_len, out, hq, hkv, c, b, g,
+                                                             rows, row0, sc, kept, pb);
+  }
 }
 
 struct AttnArgs {
@@ -643,19 +742,20 @@ struct AttnArgs {
   void* out;
   int batch, k_max, hq, hkv;
   float c;
+  KvScatter sc;               // used by the fused-scatter kernels only
 };
 
-template <int D, bool BF16, int T, int kWaves, int kPaged, bool kQSplitOk = false>
+template <int D, bool BF16, int T, int kWaves, int kPaged, bool kScatter, bool kQSplitOk = false>
 hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   const long rows = (long)a.k_max * (a.hq / a.hkv);
   const long span = kQSplitOk ? 32L * T * kWaves : 32L * T;
   const long n_rg = (rows + span - 1) / span;
   const long grid = (long)((a.batch + kXcds - 1) / kXcds) * kXcds * a.hkv * n_rg;
   if (grid > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_kernel<D, BF16, T, kWaves, kPaged, kQSplitOk>), dim3((unsigned)grid),
-                     dim3(64 * kWaves), 0, stream, (const char*)a.q, a.count, a.cu,
-                     (const char*)a.ck, (const char*)a.cv, a.map, a.kl, a.order, (char*)a.out,
-                     a.batch, a.hq, a.hkv, (int)n_rg, a.hkv >= 4 ? 1 : 0, a.c);
+  hipLaunchKernelGGL((attn_kernel<D, BF16, T, kWaves, kPaged, kQSplitOk, kScatter>),
+                     dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, (const char*)a.q, a.count,
+                     a.cu, (const char*)a.ck, (const char*)a.cv, a.map, a.kl, a.order,
+                     (char*)a.out, a.batch, a.hq, a.hkv, (int)n_rg, a.hkv >= 4 ? 1 : 0, a.c, a.sc);
   return hipGetLastError();
 }
 
@@ -669,7 +769,7 @@ inline int waves_for(long items, bool ordered) {
   return items >= (ordered ? 1024 : 2048) ? 2 : 4;
 }
 
-template <int D, int kPaged>
+template <int D, int kPaged, bool kScatter>
 hipError_t launch_bf16(const AttnArgs& a, hipStream_t stream) {
   const long rows = (long)a.k_max * (a.hq / a.hkv);
   const int T = rows > 32 ? 2 : 1;
@@ -677,23 +777,26 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t stream) {
   // 128-row groups, whose waves split the rows when there are more than 64
   // (each streams the K/V once; the second stream is served mostly by L2) and
   // the keys otherwise.
-  if (rows > 64) return launch<D, true, 2, 2, kPaged, true>(a, stream);
+  if (rows > 64) return launch<D, true, 2, 2, kPaged, kScatter, true>(a, stream);
   const long items = (long)a.batch * a.hkv * ((rows + 32 * T - 1) / (32 * T));
   const int nw = waves_for(items, a.order != nullptr);
   if (T == 2)
-    return nw == 2 ? launch<D, true, 2, 2, kPaged>(a, stream) : launch<D, true, 2, 4, kPaged>(a, stream);
-  return nw == 2 ? launch<D, true, 1, 2, kPaged>(a, stream) : launch<D, true, 1, 4, kPaged>(a, stream);
+    return nw == 2 ? launch<D, true, 2, 2, kPaged, kScatter>(a, stream)
+                   : launch<D, true, 2, 4, kPaged, kScatter>(a, stream);
+  return nw == 2 ? launch<D, true, 1, 2, kPaged, kScatter>(a, stream)
+                 : launch<D, true, 1, 4, kPaged, kScatter>(a, stream);
 }
 
-// Shared by the contiguous and paged entry points.
-template <int kPaged>
+// Shared by the contiguous and paged entry points, with and without the fused scatter.
+template <int kPaged, bool kScatter = false>
 int attention(const AttnArgs& a, int head_dim, bte_dtype dtype, hipStream_t stream) {
   hipError_t e;
   if (dtype == BTE_BF16)
-    e = head_dim == 128 ? launch_bf16<128, kPaged>(a, stream) : launch_bf16<64, kPaged>(a, stream);
+    e = head_dim == 128 ? launch_bf16<128, kPaged, kScatter>(a, stream)
+                        : launch_bf16<64, kPaged, kScatter>(a, stream);
   else  // fp32 operands take twice the registers: 32 query rows per workgroup only
-    e = head_dim == 128 ? launch<128, false, 1, 4, kPaged>(a, stream)
-                        : launch<64, false, 1, 4, kPaged>(a, stream);
+    e = head_dim == 128 ? launch<128, false, 1, 4, kPaged, kScatter>(a, stream)
+                        : launch<64, false, 1, 4, kPaged, kScatter>(a, stream);
   if (e == hipErrorInvalidValue) return BTE_ERR_DIM;
   return e == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
 }
@@ -790,7 +893,7 @@ extern "C" int bte_reduced_attention(const void* q, const int32_t* count, const 
                                    hkv, head_dim, scale, dtype);
   if (st != BTE_OK || k_max == 0) return st;
   const AttnArgs a{q, count, cu, cache_k, cache_v, KvMap{seq_start, nullptr, 0, 0}, kv_len, order,
-                   out, batch, k_max, hq, hkv, scale * kLog2e};
+                   out, batch, k_max, hq, hkv, scale * kLog2e, {}};
   return attention<kContig>(a, head_dim, dtype, stream);
 }
 
@@ -813,7 +916,64 @@ extern "C" int bte_reduced_attention_paged(const void* q, const int32_t* count, 
   int lg = 0;
   while ((1 << lg) < page_size) ++lg;
   const AttnArgs a{q, count, cu, cache_k, cache_v, KvMap{nullptr, block_table, max_pages, lg},
-                   kv_len, order, out, batch, k_max, hq, hkv, scale * kLog2e};
+                   kv_len, order, out, batch, k_max, hq, hkv, scale * kLog2e, {}};
   return max_pages <= kPageCache ? attention<kPagedLds>(a, head_dim, dtype, stream)
                                   : attention<kPagedMem>(a, head_dim, dtype, stream);
+}
+
+// Host-side checks of the fused scatter's own arguments.
+static int scatter_args_ok(const int32_t* idx, int n, const int32_t* pos_base, const void* new_k,
+                           const void* new_v) {
+  using namespace bte;
+  if (!idx || !pos_base || !new_k || !new_v) return BTE_ERR_NULL;
+  if (n <= 0) return BTE_ERR_DIM;
+  if (n > kScatterSpan) return BTE_ERR_UNSUPPORTED;
+  if (!aligned16(new_k) || !aligned16(new_v)) return BTE_ERR_ALIGN;
+  return BTE_OK;
+}
+
+extern "C" int bte_kv_scatter_attention(const void* q, const int32_t* count, const int32_t* cu,
+                                        const int32_t* idx, int n, const int32_t* pos_base,
+                                        const void* new_k, const void* new_v, void* cache_k,
+                                        void* cache_v, const int64_t* seq_start,
+                                        const int32_t* kv_len, const int32_t* order, void* out,
+                                        int batch, int k_max, int hq, int hkv, int head_dim,
+                                        float scale, bte_dtype dtype, hipStream_t stream) {
+  using namespace bte;
+  if (!seq_start) return BTE_ERR_NULL;
+  int st = attention_args_ok(q, count, cu, cache_k, cache_v, kv_len, out, batch, k_max, hq, hkv,
+                             head_dim, scale, dtype);
+  if (st == BTE_OK) st = scatter_args_ok(idx, n, pos_base, new_k, new_v);
+  if (st != BTE_OK || k_max == 0) return st;
+  AttnArgs a{q, count, cu, cache_k, cache_v, KvMap{seq_start, nullptr, 0, 0}, kv_len, order,
+             out, batch, k_max, hq, hkv, scale * kLog2e, {}};
+  a.sc = KvScatter{(const char*)new_k, (const char*)new_v, idx, pos_base, (char*)cache_k,
+                   (char*)cache_v, n, k_max};
+  return attention<kContig, true>(a, head_dim, dtype, stream);
+}
+
+extern "C" int bte_kv_scatter_attention_paged(
+    const void* q, const int32_t* count, const int32_t* cu, const int32_t* idx, int n,
+    const int32_t* pos_base, const void* new_k, const void* new_v, void* cache_k, void* cache_v,
+    const int32_t* block_table, int max_pages, int page_size, const int32_t* kv_len,
+    const int32_t* order, void* out, int batch, int k_max, int hq, int hkv, int head_dim,
+    float scale, bte_dtype dtype, hipStream_t stream) {
+  using namespace bte;
+  if (!block_table) return BTE_ERR_NULL;
+  int st = attention_args_ok(q, count, cu, cache_k, cache_v, kv_len, out, batch, k_max, hq, hkv,
+                             head_dim, scale, dtype);
+  if (st == BTE_OK) st = scatter_args_ok(idx, n, pos_base, new_k, new_v);
+  if (st != BTE_OK) return st;
+  if (max_pages <= 0) return BTE_ERR_DIM;
+  if (page_size < 8 || page_size > (1 << 20) || (page_size & (page_size - 1)) != 0)
+    return BTE_ERR_UNSUPPORTED;
+  if (k_max == 0) return BTE_OK;
+  int lg = 0;
+  while ((1 << lg) < page_size) ++lg;
+  AttnArgs a{q, count, cu, cache_k, cache_v, KvMap{nullptr, block_table, max_pages, lg}, kv_len,
+             order, out, batch, k_max, hq, hkv, scale * kLog2e, {}};
+  a.sc = KvScatter{(const char*)new_k, (const char*)new_v, idx, pos_base, (char*)cache_k,
+                   (char*)cache_v, n, k_max};
+  return max_pages <= kPageCache ? attention<kPagedLds, true>(a, head_dim, dtype, stream)
+                                  : attention<kPagedMem, true>(a, head_dim, dtype, stream);
 }

@@ -349,7 +349,62 @@ int bte_reduced_attention_paged(const void* q, const int32_t* count, const int32
                                 bte_dtype dtype, hipStream_t stream);
 
 /*
- * Work order for bte_reduced_attention: order_out[0..batch-1] = the sequence
+ * KV scatter and reduced attention in one launch (FOCUS paper App. E.2.4:
+ * the processed positions' fresh K/V are written into the exact cache, then
+ * the ragged attention of the kept queries reads prefix + block; Section 4.2:
+ * later layers run on the kept rows only). The result is bitwise that of
+ *   bte_kv_scatter(new_k, new_v, idx, count, cu, NULL, 0, row_base, ...)
+ *     with row_base[b] = seq_start[b] + pos_base[b], followed by
+ *   bte_reduced_attention(q, count, cu, cache_k, cache_v, seq_start, ...)
+ * on the same stream: cache rows seq_start[b] + pos_base[b] + idx[b, t]
+ * (t < count[b]) receive new_k/new_v rows cu[b] + t, all other cache rows are
+ * untouched, and out is the attention over the updated cache. The attention
+ * takes the kept positions' K/V straight from new_k/new_v, so the scattered
+ * bytes are written once and never read back; the writes share the launch's
+ * HBM stream instead of costing a separate launch.
+ *
+ *   q, out [>= cu[batch], hq, head_dim] dtype
+ *   idx [batch, k_max] int32: block indices in [0, n), strictly ascending in
+ *     idx[b, 0..count[b]-1] (as bte_topk_select and bte_focus_select emit them)
+ *   pos_base [batch] int32: the KV position of block index 0
+ *   new_k, new_v [>= cu[batch], hkv, head_dim] dtype (16-byte aligned)
+ *   cache_k, cache_v [rows, hkv, head_dim] dtype, updated in place
+ *   count, cu, seq_start, kv_len, order, scale: as bte_reduced_attention
+ * Device contract (as both calls, plus): 0 <= pos_base[b] + idx[b, t] <
+ * kv_len[b] for t < count[b], so that every written row lies in the
+ * sequence's own KV range.
+ * Limits: 1 <= n <= 64 (the block sizes of the FOCUS paper are 16, 32 and
+ * 64); otherwise as bte_reduced_attention.
+ * Errors: as bte_reduced_attention; NULL idx, pos_base, new_k or new_v ->
+ * BTE_ERR_NULL; n <= 0 -> BTE_ERR_DIM; n > 64 -> BTE_ERR_UNSUPPORTED;
+ * new_k/new_v not 16-byte aligned -> BTE_ERR_ALIGN.
+ */
+int bte_kv_scatter_attention(const void* q, const int32_t* count, const int32_t* cu,
+                             const int32_t* idx, int n, const int32_t* pos_base,
+                             const void* new_k, const void* new_v, void* cache_k, void* cache_v,
+                             const int64_t* seq_start, const int32_t* kv_len,
+                             const int32_t* order, void* out, int batch, int k_max, int hq,
+                             int hkv, int head_dim, float scale, bte_dtype dtype,
+                             hipStream_t stream);
+
+/*
+ * The fused scatter + attention over a paged cache: bitwise
+ *   bte_kv_scatter_paged(new_k, new_v, idx, count, cu, NULL, 0, pos_base,
+ *                        block_table, max_pages, page_size, ...)
+ * followed by bte_reduced_attention_paged(...) with the same table. Arguments,
+ * contract and limits as bte_kv_scatter_attention and
+ * bte_reduced_attention_paged.
+ */
+int bte_kv_scatter_attention_paged(const void* q, const int32_t* count, const int32_t* cu,
+                                   const int32_t* idx, int n, const int32_t* pos_base,
+                                   const void* new_k, const void* new_v, void* cache_k,
+                                   void* cache_v, const int32_t* block_table, int max_pages,
+                                   int page_size, const int32_t* kv_len, const int32_t* order,
+                                   void* out, int batch, int k_max, int hq, int hkv, int head_dim,
+                                   float scale, bte_dtype dtype, hipStream_t stream);
+
+/*
+ * Work order for bte_reduced_attention:order_out[0..batch-1] = the sequence
  * indices sorted by kv_len descending, ties by index ascending. Starting the
  * longest sequences first keeps them out of the kernel's tail (greedy
  * longest-processing-time scheduling); the lengths are the same for every

@@ -62,3 +62,32 @@ def selection_valid(g_idx, g_cnt, ref_delta, k, k_max, tol_abs=ABS_TOL, tol_rel=
         if not np.array_equal(np.sort(order[:keff]), sel):
             differ.append(b)
     return differ
+
+
+def page_table(kv_len, page_size, seed, spare=5):
+    """Shuffled pages: block_table [batch, max_pages] (-1 past a sequence's
+    pages) and, for every pool row, the contiguous cache row it holds (-1 if
+    none)."""
+    r = np.random.default_rng(seed)
+    kv_len = np.asarray(kv_len, np.int64)
+    need = (kv_len + page_size - 1) // page_size
+    n_pages = int(need.sum()) + spare
+    perm = r.permutation(n_pages).astype(np.int32)
+    bt = np.full((len(kv_len), int(need.max())), -1, np.int32)
+    src = np.full(n_pages * page_size, -1, np.int64)
+    seq_start = np.concatenate([[0], np.cumsum(kv_len)[:-1]])
+    at = 0
+    for b in range(len(kv_len)):
+        pages = perm[at:at + need[b]]
+        at += need[b]
+        bt[b, :need[b]] = pages
+        p = np.arange(kv_len[b])
+        src[pages[p // page_size].astype(np.int64) * page_size + p % page_size] = seq_start[b] + p
+    return bt, src, n_pages
+
+
+def pool(cache, src, n_pages, page_size):
+    pool = torch.randn((n_pages * page_size,) + tuple(cache.shape[1:]), device=cache.device).to(cache.dtype)
+    have = torch.from_numpy(np.flatnonzero(src >= 0)).to(cache.device)
+    pool[have] = cache[torch.from_numpy(src[src >= 0]).to(cache.device)]
+    return pool

@@ -25,7 +25,7 @@ def declared():
 
 def test_every_declared_symbol_is_exported():
     names = declared()
-    assert len(names) == 16
+    assert len(names) == 18
     for name in names:
         assert hasattr(lib, name), name
 
@@ -118,6 +118,49 @@ def test_attention_errors():
     assert call(a3=MIS) == ALIGN
     assert call(a10=0) == OK                  # nothing kept: no launch
     assert call(a7=None, a10=0) == OK         # the order is optional
+
+
+def test_scatter_attention_errors():
+    f = lib.bte_kv_scatter_attention
+    # q, count, cu, idx, n, pos_base, new_k, new_v, cache_k, cache_v, seq_start, kv_len, order,
+    # out, batch, k_max, hq, hkv, head_dim, scale, dtype, stream
+    args = [FAKE] * 4 + [32] + [FAKE] * 9 + [4, 8, 32, 8, 128, 0.088, 1, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a3=None) == NULL             # idx
+    assert call(a5=None) == NULL             # pos_base
+    assert call(a6=None) == NULL             # new_k
+    assert call(a10=None) == NULL            # seq_start
+    assert call(a4=0) == DIM
+    assert call(a4=65) == UNSUP
+    assert call(a11=None) == NULL            # kv_len
+    assert call(a17=3) == DIM                # hq % hkv
+    assert call(a18=96) == UNSUP
+    assert call(a7=MIS) == ALIGN             # new_v
+    assert call(a8=MIS) == ALIGN             # cache_k
+    assert call(a15=0) == OK                 # nothing kept: no launch
+    g = lib.bte_kv_scatter_attention_paged
+    # q, count, cu, idx, n, pos_base, new_k, new_v, ck, cv, block_table, max_pages, page_size,
+    # kv_len, order, out, batch, k_max, hq, hkv, head_dim, scale, dtype, stream
+    pargs = [FAKE] * 4 + [32] + [FAKE] * 6 + [4, 64] + [FAKE] * 3 + [4, 8, 32, 8, 128, 0.088, 1,
+                                                                       None]
+
+    def pcall(**kw):
+        a = list(pargs)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return g(*a)
+    assert pcall(a10=None) == NULL           # block_table
+    assert pcall(a3=None) == NULL
+    assert pcall(a4=65) == UNSUP
+    assert pcall(a11=0) == DIM
+    assert pcall(a12=48) == UNSUP
+    assert pcall(a6=MIS) == ALIGN
+    assert pcall(a17=0) == OK
 
 
 def test_attention_order_errors():

@@ -90,6 +90,32 @@ def test_scatter_paged_targets():
         C.check_scatter_paged(idx, cnt, cu, 12, pos_base, bt, 8, pool_rows=24, new_rows=5)
 
 
+def test_fused_scatter_targets():
+    idx, cnt, cu = _explicit([[1, 30], [0, 5, 31]])
+    kv = np.array([40, 50], np.int32)
+    ss = np.array([0, 40], np.int64)
+    pb = np.array([8, 18], np.int32)                           # blocks end at 40 and 50
+    C.check_fused_scatter(idx, cnt, cu, 12, 32, pb, kv, 5, seq_start=ss, cache_rows=90)
+    with pytest.raises(C.ContractError, match="kv_len"):          # 10 + 30 >= 40
+        C.check_fused_scatter(idx, cnt, cu, 12, 32, np.array([10, 18], np.int32), kv, 5,
+                              seq_start=ss, cache_rows=90)
+    with pytest.raises(C.ContractError, match=r"outside \[0, 31\)"):   # block index 31, n = 31
+        C.check_fused_scatter(idx, cnt, cu, 12, 31, pb, kv, 5, seq_start=ss, cache_rows=90)
+    # sequence 0's KV rows overlap sequence 1's: sequence 1 writes rows sequence 0 reads
+    with pytest.raises(C.ContractError, match="reads a cache row"):
+        C.check_fused_scatter(idx, cnt, cu, 12, 32, pb, kv, 5, seq_start=np.array([0, 5]),
+                              cache_rows=90)
+    # paged: sequence 1's block lands on a page that sequence 0 also maps
+    bt = np.array([[0, 1, 2, 3, 4], [5, 6, 7, 8, 9], ], np.int32)
+    C.check_fused_scatter(idx, cnt, cu, 12, 32, pb, kv, 5, cache_rows=100, block_table=bt,
+                          page_size=10)
+    shared = bt.copy()
+    shared[1, 2] = 1                                           # positions 20..29 of seq 1 -> page 1
+    with pytest.raises(C.ContractError, match="reads a cache row"):
+        C.check_fused_scatter(idx, cnt, cu, 12, 32, pb, kv, 5, cache_rows=100,
+                              block_table=shared, page_size=10)
+
+
 def test_attention_contract():
     cnt = np.array([2, 0, 3], np.int32)
     cu = np.array([0, 2, 2, 5], np.int32)

@@ -23,9 +23,9 @@ def _f64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def _check_chain(fc, ac, sample, device="cuda"):
+def _check_chain(fc, ac, sample, device="cuda", fused=False):
     from block_token_eviction_amd.chain import FocusStep
-    say(f"chain {fc.name} batch={fc.batch} sample={len(sample)}")
+    say(f"chain {fc.name} batch={fc.batch} sample={len(sample)} fused={fused}")
     x = W.chain_inputs(fc, ac, device=device)
     cache_k0 = {int(b): None for b in sample}
     seq_start = x["seq_start"].cpu().numpy()
@@ -37,7 +37,8 @@ def _check_chain(fc, ac, sample, device="cuda"):
     step.run(q0=x["q0"], k0=x["k0"], q1=x["q1"], k1=x["k1"], decoded=x["decoded"], k=x["k"],
              hidden_rows=x["hidden_rows"], pool_kernel=fc.pool_kernel, new_k=x["new_k"],
              new_v=x["new_v"], q_kept=x["q_kept"], cache_k=x["cache_k"], cache_v=x["cache_v"],
-             seq_start=x["seq_start"], kv_len=x["kv_len"], row_base=x["row_base"])
+             seq_start=x["seq_start"], kv_len=x["kv_len"], row_base=x["row_base"],
+             pos_base=x["prefix"].to(torch.int32), fused=fused)
     torch.cuda.synchronize()
     g_delta = step.delta.cpu().numpy()
     g_idx, g_cnt, g_cu = step.idx.cpu().numpy(), step.count.cpu().numpy(), step.cu.cpu().numpy()
@@ -84,31 +85,39 @@ def _check_chain(fc, ac, sample, device="cuda"):
     return differ
 
 
-def test_chain_small_every_sequence():
+FUSED = pytest.mark.parametrize("fused", [False, True], ids=["scatter_then_attention",
+                                                              "fused_scatter_attention"])
+
+
+@FUSED
+def test_chain_small_every_sequence(fused):
     fc = W.FocusCfg("chain_small", seed=51, batch=48)
     ac = W.AttnCfg("chain_small", seed=51, batch=48, kept=None, prefix_lo=40, prefix_hi=700)
-    _check_chain(fc, ac, list(range(48)))
+    _check_chain(fc, ac, list(range(48)), fused=fused)
 
 
-def test_chain_b1024_full_size_sampled():
+@FUSED
+def test_chain_b1024_full_size_sampled(fused):
     """The benchmarked workload itself (batch 1024, prefixes 1024..4096)."""
     sample = sorted(np.random.default_rng(9).choice(1024, size=48, replace=False).tolist())
-    _check_chain(W.CHAIN_FOCUS_B1024, W.CHAIN_ATTN_B1024, sample)
+    _check_chain(W.CHAIN_FOCUS_B1024, W.CHAIN_ATTN_B1024, sample, fused=fused)
 
 
-def test_focus_step_graph_replays_match_eager():
+@FUSED
+def test_focus_step_graph_replays_match_eager(fused):
     """A FOCUS step captured in a HIP graph and replayed three times, with eager
     work and synchronisations in between: every replay equals the eager step
     bit for bit (the kernels allocate nothing and record no memset nodes)."""
     from block_token_eviction_amd.chain import FocusStep
     fc = W.FocusCfg("graph", seed=81, batch=64)
     ac = W.AttnCfg("graph", seed=81, batch=64, kept=None, prefix_lo=100, prefix_hi=600)
-    say("focus step under graph capture")
+    say(f"focus step under graph capture fused={fused}")
     x = W.chain_inputs(fc, ac, device="cuda")
     step = FocusStep(fc.batch, fc.block, fc.hidden, fc.hq, fc.head_dim, fc.k_hi, fc.dtype, "cuda")
     args = {k: x[k] for k in ("q0", "k0", "q1", "k1", "decoded", "k", "hidden_rows", "pool_kernel",
                               "new_k", "new_v", "q_kept", "cache_k", "cache_v", "seq_start",
                               "kv_len", "row_base")}
+    args.update(pos_base=x["prefix"].to(torch.int32), fused=fused)
     cache0 = (x["cache_k"].clone(), x["cache_v"].clone())
     step.run(**args)
     torch.cuda.synchronize()

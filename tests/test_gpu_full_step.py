@@ -39,9 +39,9 @@ def _pool_rows(bt, b, kv_len, page):
     return bt[b, p // page].astype(np.int64) * page + p % page
 
 
-def _check_full_step(fc, ac, page, sample):
+def _check_full_step(fc, ac, page, sample, fused=False):
     from block_token_eviction_amd.chain import FocusFullStep
-    say(f"full step {fc.name} batch={fc.batch} page={page} sample={len(sample)}")
+    say(f"full step {fc.name} batch={fc.batch} page={page} sample={len(sample)} fused={fused}")
     x = W.focus_full_inputs(fc, ac, page_size=page, device="cuda")
     n, B = fc.batch, fc.block
     bt = x["block_table"].cpu().numpy()
@@ -61,7 +61,8 @@ def _check_full_step(fc, ac, page, sample):
              rightmost_processed=x["rightmost_processed"], cached=x["cached"],
              per_token=per_token, new_k=x["new_k_full"], new_v=x["new_v_full"],
              q_kept=x["q_full"], pos_base=x["pos_base"], block_table=x["block_table"],
-             page_size=page, pool_k=x["pool_k"], pool_v=x["pool_v"], kv_len=x["kv_len"])
+             page_size=page, pool_k=x["pool_k"], pool_v=x["pool_v"], kv_len=x["kv_len"],
+             fused=fused)
     torch.cuda.synchronize()
     dec = x["decoded"].cpu().numpy().astype(bool)
     now = x["decoded_now"].cpu().numpy().astype(bool)
@@ -131,26 +132,33 @@ def _check_full_step(fc, ac, page, sample):
         assert_close(_f64(step.out[c0:c0 + cnt]), ref_o, f"attention seq {b}")
 
 
-def test_full_step_small_every_sequence():
+FUSED = pytest.mark.parametrize("fused", [False, True], ids=["scatter_then_attention",
+                                                              "fused_scatter_attention"])
+
+
+@FUSED
+def test_full_step_small_every_sequence(fused):
     fc = W.FocusCfg("full_small", seed=52, batch=40)
     ac = W.AttnCfg("full_small", seed=52, batch=40, kept=None, prefix_lo=20, prefix_hi=600)
-    _check_full_step(fc, ac, 16, list(range(40)))
+    _check_full_step(fc, ac, 16, list(range(40)), fused=fused)
 
 
-def test_full_step_b1024_sampled():
+@FUSED
+def test_full_step_b1024_sampled(fused):
     """The benchmarked extended step itself (batch 1024, prefixes 1024..4096, pages of 64)."""
     sample = sorted(np.random.default_rng(11).choice(1024, size=24, replace=False).tolist())
-    _check_full_step(W.CHAIN_FOCUS_B1024, W.CHAIN_ATTN_B1024, 64, sample)
+    _check_full_step(W.CHAIN_FOCUS_B1024, W.CHAIN_ATTN_B1024, 64, sample, fused=fused)
 
 
-def test_full_step_graph_replays_match_eager():
+@FUSED
+def test_full_step_graph_replays_match_eager(fused):
     """The extended step captured in a HIP graph and replayed three times, with the
     per-sequence state restored and the outputs cleared eagerly in between: every
     replay equals the eager step bit for bit (outputs, state, KV pool)."""
     from block_token_eviction_amd.chain import FocusFullStep
     fc = W.FocusCfg("full_graph", seed=53, batch=48)
     ac = W.AttnCfg("full_graph", seed=53, batch=48, kept=None, prefix_lo=30, prefix_hi=500)
-    say("extended step under graph capture")
+    say(f"extended step under graph capture fused={fused}")
     page = 16
     x = W.focus_full_inputs(fc, ac, page_size=page, device="cuda")
     per_token = [x["hidden_rows"], x["residual"], x["rope_pos"], x["cache_idx"]]
@@ -165,7 +173,8 @@ def test_full_step_graph_replays_match_eager():
                 rightmost_processed=x["rightmost_processed"], cached=x["cached"],
                 per_token=per_token, new_k=x["new_k_full"], new_v=x["new_v_full"],
                 q_kept=x["q_full"], pos_base=x["pos_base"], block_table=x["block_table"],
-                page_size=page, pool_k=x["pool_k"], pool_v=x["pool_v"], kv_len=x["kv_len"])
+                page_size=page, pool_k=x["pool_k"], pool_v=x["pool_v"], kv_len=x["kv_len"],
+                fused=fused)
 
     def reset():
         for t, t0 in zip(state, state0):

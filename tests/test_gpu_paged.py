@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import workloads as W
-from helpers import assert_close, dev, say
+from helpers import assert_close, dev, page_table as _page_table, pool as _pool, say
 
 pytestmark = pytest.mark.gpu
 
@@ -17,35 +17,6 @@ pytestmark = pytest.mark.gpu
 def _bte():
     import block_token_eviction_amd as bte
     return bte
-
-
-def _page_table(kv_len, page_size, seed, spare=5):
-    """Shuffled pages: block_table [batch, max_pages] (-1 past a sequence's
-    pages) and, for every pool row, the contiguous cache row it holds (-1 if
-    none)."""
-    r = np.random.default_rng(seed)
-    kv_len = np.asarray(kv_len, np.int64)
-    need = (kv_len + page_size - 1) // page_size
-    n_pages = int(need.sum()) + spare
-    perm = r.permutation(n_pages).astype(np.int32)
-    bt = np.full((len(kv_len), int(need.max())), -1, np.int32)
-    src = np.full(n_pages * page_size, -1, np.int64)
-    seq_start = np.concatenate([[0], np.cumsum(kv_len)[:-1]])
-    at = 0
-    for b in range(len(kv_len)):
-        pages = perm[at:at + need[b]]
-        at += need[b]
-        bt[b, :need[b]] = pages
-        p = np.arange(kv_len[b])
-        src[pages[p // page_size].astype(np.int64) * page_size + p % page_size] = seq_start[b] + p
-    return bt, src, n_pages
-
-
-def _pool(cache, src, n_pages, page_size):
-    pool = torch.randn((n_pages * page_size,) + tuple(cache.shape[1:]), device=cache.device).to(cache.dtype)
-    have = torch.from_numpy(np.flatnonzero(src >= 0)).to(cache.device)
-    pool[have] = cache[torch.from_numpy(src[src >= 0]).to(cache.device)]
-    return pool
 
 
 CFGS = [
