@@ -1,16 +1,30 @@
 """Work order of the reduced attention (oracle; test use only).
 
 Not part of the method's arithmetic: the GPU library starts the attention of
-the longest sequences first (greedy longest-processing-time scheduling), and
+the largest work items first (greedy longest-processing-time scheduling), and
 this is the order it must produce, by definition: sequence indices sorted by
-KV length descending, equal lengths by index ascending; negative lengths
-count as 0.
+estimated work descending, equal work by index ascending.
+
+Work of sequence i: its KV length (negative counts as 0); with the kept-row
+counts given, the length times the number of 64-row query passes over its
+keys, ceil(count_i * group / 64) (group = query heads per KV head; a negative
+count counts as 0), capped at 2^32 - 1. One attention wave holds 64 query rows,
+so a sequence with more rows per KV head streams its keys once per pass.
 """
 from __future__ import annotations
 
 import numpy as np
 
+PASS_ROWS = 64
+WORK_CAP = 2 ** 32 - 1
 
-def attention_order(kv_len) -> np.ndarray:
+
+def attention_order(kv_len, count=None, group: int = 1) -> np.ndarray:
     lens = [max(int(v), 0) for v in np.asarray(kv_len).reshape(-1)]
-    return np.array(sorted(range(len(lens)), key=lambda i: (-lens[i], i)), dtype=np.int32)
+    if count is None:
+        work = lens
+    else:
+        cnt = [max(int(v), 0) for v in np.asarray(count).reshape(-1)]
+        work = [min(lens[i] * -(-(cnt[i] * group) // PASS_ROWS), WORK_CAP)
+                for i in range(len(lens))]
+    return np.array(sorted(range(len(work)), key=lambda i: (-work[i], i)), dtype=np.int32)

@@ -138,6 +138,34 @@ def test_attention_order_invariants():
     assert np.all(o[:-1][tie] < o[1:][tie])
 
 
+def test_attention_order_by_work_hand_example():
+    """Worked by hand, group 4 (64 query rows per pass): counts 17, 3, 20, 0, 16 give
+    68, 12, 80, 0, 64 rows per KV head, so 2, 1, 2, 0, 1 passes; with lengths 100, 100,
+    60, 50, 130 the work is 200, 100, 120, 0, 130."""
+    got = oracle.attention_order(np.array([100, 100, 60, 50, 130], np.int32),
+                                 count=np.array([17, 3, 20, 0, 16], np.int32), group=4)
+    np.testing.assert_array_equal(got, [0, 4, 2, 1, 3])
+
+
+def test_attention_order_by_work_special_cases():
+    r = np.random.default_rng(12)
+    lens = r.integers(-2, 400, 500).astype(np.int32)
+    # one pass for every sequence that keeps rows: the length order, empty sequences last
+    cnt = r.integers(1, 17, 500).astype(np.int32)
+    np.testing.assert_array_equal(oracle.attention_order(lens, count=cnt, group=4),
+                                  oracle.attention_order(lens))
+    lens = np.maximum(lens, 1)             # zero work only from the counts below
+    cnt[::7] = 0
+    o = oracle.attention_order(lens, count=cnt, group=4)
+    tail = o[-int((cnt == 0).sum()):]
+    assert set(tail.tolist()) == set(np.flatnonzero(cnt == 0).tolist())
+    assert np.all(np.diff(tail) > 0)
+    # work saturates at 2^32 - 1: the two largest tie and keep index order
+    big = oracle.attention_order(np.array([2 ** 30, 2 ** 30 - 5, 7], np.int32),
+                                 count=np.array([64 * 8, 64 * 9, 1], np.int32), group=1)
+    np.testing.assert_array_equal(big, [0, 1, 2])
+
+
 def _paged_layout(r, kv_len, page_size, extra_pages=3):
     """A random page table over a pool with spare pages, and the pool filled so
     that every sequence reads the contiguous rows it stands for."""
