@@ -72,6 +72,8 @@ def main():
     fc, ac = W.CHAIN_FOCUS_B1024, W.CHAIN_ATTN_B1024
     log("generating inputs on the device")
     x = W.chain_inputs(fc, ac, device=dev)
+    # length order for the attention: with at most 12 kept rows (48 query rows per KV head)
+    # every sequence is one 64-row query pass, so weighing by passes would change nothing
     step = FocusStep(fc.batch, fc.block, fc.hidden, fc.hq, fc.head_dim, fc.k_hi, fc.dtype, dev)
     run_args = {k: x[k] for k in ("q0", "k0", "q1", "k1", "decoded", "k", "hidden_rows",
                                   "pool_kernel", "new_k", "new_v", "q_kept", "cache_k", "cache_v",
@@ -383,7 +385,7 @@ def full_step_leg(x, fc, ac, steps: int, warmup: int, dev):
     y = W.focus_full_inputs(fc, ac, page_size=PAGE, device=dev, base=x)
     per_token = [y["hidden_rows"], y["residual"], y["rope_pos"], y["cache_idx"]]
     st = FocusFullStep(fc.batch, fc.block, fc.hq, fc.head_dim,
-                       [(t.shape[2:], t.dtype) for t in per_token], fc.dtype, dev)
+                       [(t.shape[2:], t.dtype) for t in per_token], fc.dtype, dev, hkv=fc.hkv)
     state = [y[k] for k in ("token_sum", "total_steps", "rightmost_processed", "cached")]
     saved = [t.clone() for t in state]
     stages = [

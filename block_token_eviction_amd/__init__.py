@@ -43,7 +43,7 @@ _SIG = {
     "bte_gather_rows": ([_p, _p, _p, _p, _p, _i, _i, _i, _sz, _p], _i),
     "bte_kv_scatter": ([_p, _p, _p, _p, _p, _p, _i, _p, _p, _p, _i, _i, _sz, _p], _i),
     "bte_reduced_attention": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p], _i),
-    "bte_attention_order": ([_p, _i, _p, _p], _i),
+    "bte_attention_order": ([_p, _p, _i, _i, _p, _p], _i),
     "bte_reduced_attention_paged": ([_p, _p, _p, _p, _p, _p, _i, _i, _p, _p, _p, _i, _i, _i, _i, _i,
                                      _f, _i, _p], _i),
     "bte_kv_scatter_paged": ([_p, _p, _p, _p, _p, _p, _i, _p, _p, _i, _i, _p, _p, _i, _i, _sz, _p],
@@ -271,15 +271,21 @@ def kv_scatter_attention(q, count, cu, idx, n: int, pos_base, new_k, new_v, cach
     return out
 
 
-def attention_order(kv_len, out=None):
-    """kv_len int32 [batch] -> order int32 [batch]: sequences by length descending, index ascending."""
-    _dev(kv_len, out)
+def attention_order(kv_len, out=None, count=None, group: int = 1):
+    """kv_len int32 [batch] -> order int32 [batch]: sequences by work descending, index
+    ascending. Work is the length, or with the kept counts (int32 [batch]) and group =
+    hq / hkv the length times ceil(count * group / 64) query passes."""
+    _dev(kv_len, out, count)
     _want(kv_len, torch.int32, "kv_len")
     batch = kv_len.shape[0]
+    if count is not None:
+        _want(count, torch.int32, "count")
+        assert count.shape == (batch,)
     if out is None:
         out = torch.empty((batch,), dtype=torch.int32, device=kv_len.device)
     _want(out, torch.int32, "out")
-    _check("bte_attention_order", lib.bte_attention_order(_ptr(kv_len), batch, _ptr(out), _stream()))
+    _check("bte_attention_order", lib.bte_attention_order(_ptr(kv_len), _ptr(count), int(group),
+                                                          batch, _ptr(out), _stream()))
     return out
 
 

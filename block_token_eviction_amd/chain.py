@@ -51,8 +51,11 @@ from . import (attention_order, esdllm_score, focus_budget, focus_commit_mask,
 
 class FocusStep:
     def __init__(self, batch: int, block: int, hidden: int, hq: int, head_dim: int, k_max: int,
-                 dtype: torch.dtype, device):
+                 dtype: torch.dtype, device, hkv: int | None = None):
+        """hkv (KV heads): when given, the attention order weighs each sequence's length
+        by its query passes (attention_order with the kept counts)."""
         self.batch, self.block, self.k_max = batch, block, k_max
+        self.group = None if hkv is None else hq // hkv
         self.scale = 1.0 / math.sqrt(head_dim)
         i32 = dict(dtype=torch.int32, device=device)
         self.delta = torch.empty((batch, block), dtype=torch.float32, device=device)
@@ -76,9 +79,11 @@ class FocusStep:
         return kv_scatter(new_k, new_v, self.idx, self.count, self.cu, row_base, cache_k, cache_v)
 
     def schedule(self, kv_len):
-        """Longest-first work order of the step's attention calls (one per step:
-        every layer of the step sees the same lengths)."""
-        return attention_order(kv_len, out=self.order)
+        """Largest-first work order of the step's attention calls (one per step:
+        every layer of the step sees the same lengths and kept counts)."""
+        if self.group is None:
+            return attention_order(kv_len, out=self.order)
+        return attention_order(kv_len, out=self.order, count=self.count, group=self.group)
 
     def attend(self, q_kept, cache_k, cache_v, seq_start, kv_len):
         return reduced_attention(q_kept, self.count, self.cu, cache_k, cache_v, seq_start, kv_len,
@@ -115,9 +120,11 @@ class FocusFullStep:
     is the caller's and is updated in place."""
 
     def __init__(self, batch: int, block: int, hq: int, head_dim: int, row_shapes, dtype: torch.dtype,
-                 device):
-        """row_shapes: (shape of one row, dtype) of each per-token tensor to compact."""
+                 device, hkv: int | None = None):
+        """row_shapes: (shape of one row, dtype) of each per-token tensor to compact.
+        hkv (KV heads): when given, the attention order weighs lengths by query passes."""
         self.batch, self.block = batch, block
+        self.group = None if hkv is None else hq // hkv
         self.scale = 1.0 / math.sqrt(head_dim)
         i32 = dict(dtype=torch.int32, device=device)
         cap = batch * block
@@ -151,7 +158,9 @@ class FocusFullStep:
                                 page_size, pool_k, pool_v)
 
     def schedule(self, kv_len):
-        return attention_order(kv_len, out=self.order)
+        if self.group is None:
+            return attention_order(kv_len, out=self.order)
+        return attention_order(kv_len, out=self.order, count=self.count, group=self.group)
 
     def attend(self, q_kept, pool_k, pool_v, block_table, page_size, kv_len):
         return reduced_attention_paged(q_kept, self.count, self.cu, pool_k, pool_v, block_table,

@@ -801,9 +801,12 @@ int attention(const AttnArgs& a, int head_dim, bte_dtype dtype, hipStream_t stre
   return e == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
 }
 
-// Descending-length processing order. Sequence i's key is (length descending,
-// index ascending) packed in 64 bits, so keys are distinct and the position of
-// sequence i in the order is the number of keys below its own. A wave ranks
+// Descending-work processing order. Work is the KV length, or with the kept
+// counts the length times the 64-row query passes over the keys (a wave holds
+// 64 query rows; a sequence with more rows per KV head takes the query split,
+// whose waves each stream every key tile). Sequence i's key is (work
+// descending, index ascending) packed in 64 bits, so keys are distinct and the
+// position of sequence i in the order is the number of keys below its own. A wave ranks
 // kOrderPerWave sequences: its lanes take every 64th key (read straight from
 // kv_len, a few KB that stay in L2) and compare it with each of them, then the
 // counts are summed over the wave. A one-workgroup bitonic sort took 13 us at
@@ -813,16 +816,29 @@ constexpr int kOrderPerWave = 8;
 constexpr int kOrderPerBlock = kOrderThreads / kWave * kOrderPerWave;
 constexpr int kOrderMax = 16384;
 
-// The load is unconditional (index clamped into the batch) so that several can
-// be in flight at once; positions past the batch get the padding key ~0, above
-// every real key.
-__device__ __forceinline__ uint64_t order_key(const int32_t* kv_len, int i, int batch) {
-  const uint32_t len = (uint32_t)max(kv_len[min(i, batch - 1)], 0);
-  return i < batch ? ((uint64_t)(0xffffffffu - len) << 32) | (uint32_t)i : ~0ull;
+constexpr int kPassRows = 64;
+
+// The loads are unconditional (index clamped into the batch) so that several
+// can be in flight at once; positions past the batch get the padding key ~0,
+// above every real key. Work saturates at 2^32 - 1.
+template <bool kWork>
+__device__ __forceinline__ uint64_t order_key(const int32_t* kv_len, const int32_t* count,
+                                              int group, int i, int batch) {
+  const int c = min(i, batch - 1);
+  uint64_t work = (uint32_t)max(kv_len[c], 0);
+  if constexpr (kWork) {
+    const uint64_t rows = (uint64_t)(uint32_t)max(count[c], 0) * (uint32_t)group;
+    const uint64_t passes = (rows + kPassRows - 1) / kPassRows;   // < 2^57
+    work = passes > 0xffffffffull ? (work ? 0xffffffffull : 0ull)
+                                  : min(work * passes, 0xffffffffull);   // < 2^63 before the cap
+  }
+  return i < batch ? ((uint64_t)(0xffffffffu - (uint32_t)work) << 32) | (uint32_t)i : ~0ull;
 }
 
+template <bool kWork>
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __restrict__ kv_len,
-                                                             int batch,
+                                                             const int32_t* __restrict__ count,
+                                                             int group, int batch,
                                                              int32_t* __restrict__ order) {
   const int lane = threadIdx.x & (kWave - 1);
   const int i0 = blockIdx.x * kOrderPerBlock + (int)(threadIdx.x / kWave) * kOrderPerWave;
@@ -831,14 +847,14 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __r
   int cnt[kOrderPerWave];
 #pragma unroll
   for (int e = 0; e < kOrderPerWave; ++e) {
-    mine[e] = order_key(kv_len, i0 + e, batch);
+    mine[e] = order_key<kWork>(kv_len, count, group, i0 + e, batch);
     cnt[e] = 0;
   }
   // Eight keys per lane and pass, loaded together (one L2 round trip per pass).
   for (int j0 = lane; j0 < batch; j0 += 8 * kWave) {
     uint64_t kj[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) kj[u] = order_key(kv_len, j0 + u * kWave, batch);
+    for (int u = 0; u < 8; ++u) kj[u] = order_key<kWork>(kv_len, count, group, j0 + u * kWave, batch);
 #pragma unroll
     for (int u = 0; u < 8; ++u)
 #pragma unroll
@@ -855,13 +871,19 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __r
 }  // namespace
 }  // namespace bte
 
-extern "C" int bte_attention_order(const int32_t* kv_len, int batch, int32_t* order_out,
-                                   hipStream_t stream) {
+extern "C" int bte_attention_order(const int32_t* kv_len, const int32_t* count, int group,
+                                   int batch, int32_t* order_out, hipStream_t stream) {
   using namespace bte;
   if (!kv_len || !order_out) return BTE_ERR_NULL;
   if (batch <= 0 || batch > kOrderMax) return BTE_ERR_DIM;
-  hipLaunchKernelGGL(order_kernel, dim3((batch + kOrderPerBlock - 1) / kOrderPerBlock),
-                     dim3(kOrderThreads), 0, stream, kv_len, batch, order_out);
+  if (count && group <= 0) return BTE_ERR_DIM;
+  const dim3 grid((batch + kOrderPerBlock - 1) / kOrderPerBlock);
+  if (count)
+    hipLaunchKernelGGL(order_kernel<true>, grid, dim3(kOrderThreads), 0, stream, kv_len, count,
+                       group, batch, order_out);
+  else
+    hipLaunchKernelGGL(order_kernel<false>, grid, dim3(kOrderThreads), 0, stream, kv_len, count,
+                       group, batch, order_out);
   return hipGetLastError() == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
 }
 

@@ -309,7 +309,7 @@ int bte_kv_scatter_paged(const void* new_k, const void* new_v, const int32_t* id
  *   count [batch], cu [batch + 1] int32; seq_start [batch] int64;
  *   kv_len [batch] int32 (>= 1 for every sequence with count > 0)
  *   order [batch] int32 or NULL: the sequences in the order their work is
- *     started, normally from bte_attention_order (longest first). It only
+ *     started, normally from bte_attention_order (largest first). It only
  *     schedules: any permutation of 0..batch-1 gives the same results. An
  *     entry outside [0, batch) is clamped into it (wrong results, no stray
  *     memory access).
@@ -404,18 +404,28 @@ int bte_kv_scatter_attention_paged(const void* q, const int32_t* count, const in
                                    float scale, bte_dtype dtype, hipStream_t stream);
 
 /*
- * Work order for bte_reduced_attention:order_out[0..batch-1] = the sequence
- * indices sorted by kv_len descending, ties by index ascending. Starting the
- * longest sequences first keeps them out of the kernel's tail (greedy
- * longest-processing-time scheduling); the lengths are the same for every
- * layer of a denoising step, so one call serves all of the step's attention
- * calls. Negative lengths count as 0.
+ * Work order for the reduced attention calls: order_out[0..batch-1] = the
+ * sequence indices sorted by estimated work descending, ties by index
+ * ascending. Starting the largest items first keeps them out of the kernel's
+ * tail (greedy longest-processing-time scheduling); the lengths and counts are
+ * the same for every layer of a denoising step, so one call serves all of the
+ * step's attention calls. The order only schedules: any permutation gives the
+ * same attention results.
+ *   work[b] = max(kv_len[b], 0)                         (count == NULL)
+ *   work[b] = max(kv_len[b], 0) * ceil(max(count[b], 0) * group / 64)
+ * capped at 2^32 - 1: an attention wave holds 64 query rows, and a sequence
+ * with more kept query rows per KV head than that streams its keys once per
+ * 64-row pass (sequences with nothing kept go last).
  *
- *   kv_len [batch] int32; order_out [batch] int32 (4 byte alignment each)
- * Limits: 1 <= batch <= 16384.
- * Errors: NULL -> BTE_ERR_NULL; batch out of range -> BTE_ERR_DIM.
+ *   kv_len [batch] int32; count [batch] int32 or NULL (the kept counts of the
+ *   attention call); group = hq / hkv; order_out [batch] int32 (4 byte
+ *   alignment each)
+ * Limits: 1 <= batch <= 16384; group >= 1 when count is given.
+ * Errors: NULL kv_len/order_out -> BTE_ERR_NULL; batch out of range or
+ * group < 1 with a count -> BTE_ERR_DIM.
  */
-int bte_attention_order(const int32_t* kv_len, int batch, int32_t* order_out, hipStream_t stream);
+int bte_attention_order(const int32_t* kv_len, const int32_t* count, int group, int batch,
+                        int32_t* order_out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

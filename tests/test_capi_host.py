@@ -165,10 +165,12 @@ def test_scatter_attention_errors():
 
 def test_attention_order_errors():
     f = lib.bte_attention_order
-    assert f(None, 4, FAKE, None) == NULL
-    assert f(FAKE, 4, None, None) == NULL
-    assert f(FAKE, 0, FAKE, None) == DIM
-    assert f(FAKE, 16385, FAKE, None) == DIM
+    # kv_len, count, group, batch, order_out, stream
+    assert f(None, None, 1, 4, FAKE, None) == NULL
+    assert f(FAKE, None, 1, 4, None, None) == NULL
+    assert f(FAKE, None, 1, 0, FAKE, None) == DIM
+    assert f(FAKE, None, 1, 16385, FAKE, None) == DIM
+    assert f(FAKE, FAKE, 0, 4, FAKE, None) == DIM         # a count needs group >= 1
 
 
 def test_budget_select_errors():

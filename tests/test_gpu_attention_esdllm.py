@@ -116,6 +116,33 @@ def test_attention_order_matches_oracle(batch):
     np.testing.assert_array_equal(got, oracle.attention_order(lens))
 
 
+@pytest.mark.parametrize("batch", [1, 65, 1024, 5000, 16384])
+def test_attention_order_by_work_matches_oracle(batch):
+    """Kept counts 0..32 with group 4: up to two 64-row query passes; ties, zero counts,
+    negative lengths."""
+    bte = _bte()
+    r = np.random.default_rng(batch + 7)
+    lens = r.integers(-3, 300, batch).astype(np.int32)
+    cnt = r.integers(0, 33, batch).astype(np.int32)
+    say(f"attention_order by work batch={batch}")
+    got = bte.attention_order(torch.from_numpy(lens).cuda(), count=torch.from_numpy(cnt).cuda(),
+                              group=4).cpu().numpy()
+    np.testing.assert_array_equal(got, oracle.attention_order(lens, count=cnt, group=4))
+
+
+@pytest.mark.parametrize("lens,cnt,group", [
+    ([5, 0, 7, 2 ** 31 - 1], [2 ** 31 - 1, 2 ** 31 - 1, 1, 3], 2 ** 31 - 1),   # > 2^32 passes
+    ([2 ** 31 - 1, 2 ** 30, 9], [32, 64, 1], 2 ** 20),                         # product capped
+])
+def test_attention_order_by_work_saturates(lens, cnt, group):
+    bte = _bte()
+    lens, cnt = np.array(lens, np.int32), np.array(cnt, np.int32)
+    say(f"attention_order saturation lens={lens.tolist()} cnt={cnt.tolist()} group={group}")
+    got = bte.attention_order(torch.from_numpy(lens).cuda(), count=torch.from_numpy(cnt).cuda(),
+                              group=group).cpu().numpy()
+    np.testing.assert_array_equal(got, oracle.attention_order(lens, count=cnt, group=group))
+
+
 def test_attention_order_only_schedules():
     """Two different orders (same launch shape) give bit-identical outputs."""
     bte = _bte()

@@ -33,7 +33,8 @@ def _check_chain(fc, ac, sample, device="cuda", fused=False):
     for b in sample:                         # pre-images of the sampled sequences' caches
         r0, r1 = int(seq_start[b]), int(seq_start[b] + kv_len[b])
         cache_k0[int(b)] = (_bits(x["cache_k"][r0:r1]), _bits(x["cache_v"][r0:r1]))
-    step = FocusStep(fc.batch, fc.block, fc.hidden, fc.hq, fc.head_dim, fc.k_hi, fc.dtype, device)
+    step = FocusStep(fc.batch, fc.block, fc.hidden, fc.hq, fc.head_dim, fc.k_hi, fc.dtype, device,
+                     hkv=fc.hkv)
     step.run(q0=x["q0"], k0=x["k0"], q1=x["q1"], k1=x["k1"], decoded=x["decoded"], k=x["k"],
              hidden_rows=x["hidden_rows"], pool_kernel=fc.pool_kernel, new_k=x["new_k"],
              new_v=x["new_v"], q_kept=x["q_kept"], cache_k=x["cache_k"], cache_v=x["cache_v"],
@@ -113,7 +114,8 @@ def test_focus_step_graph_replays_match_eager(fused):
     ac = W.AttnCfg("graph", seed=81, batch=64, kept=None, prefix_lo=100, prefix_hi=600)
     say(f"focus step under graph capture fused={fused}")
     x = W.chain_inputs(fc, ac, device="cuda")
-    step = FocusStep(fc.batch, fc.block, fc.hidden, fc.hq, fc.head_dim, fc.k_hi, fc.dtype, "cuda")
+    step = FocusStep(fc.batch, fc.block, fc.hidden, fc.hq, fc.head_dim, fc.k_hi, fc.dtype, "cuda",
+                     hkv=fc.hkv)
     args = {k: x[k] for k in ("q0", "k0", "q1", "k1", "decoded", "k", "hidden_rows", "pool_kernel",
                               "new_k", "new_v", "q_kept", "cache_k", "cache_v", "seq_start",
                               "kv_len", "row_base")}

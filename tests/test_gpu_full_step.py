@@ -54,7 +54,8 @@ def _check_full_step(fc, ac, page, sample, fused=False):
                _bits(x["pool_v"][torch.from_numpy(r).cuda()])) for b, r in rows_of.items()}
     per_token = [x["hidden_rows"], x["residual"], x["rope_pos"], x["cache_idx"]]
     step = FocusFullStep(n, B, fc.hq, fc.head_dim,
-                         [(t.shape[2:], t.dtype) for t in per_token], fc.dtype, "cuda")
+                         [(t.shape[2:], t.dtype) for t in per_token], fc.dtype, "cuda",
+                         hkv=fc.hkv)
     step.run(q0=x["q0"], k0=x["k0"], q1=x["q1"], k1=x["k1"], decoded=x["decoded"],
              decoded_now=x["decoded_now"], pool_kernel=fc.pool_kernel, alpha=ALPHA,
              token_sum=x["token_sum"], total_steps=x["total_steps"],
@@ -163,7 +164,8 @@ def test_full_step_graph_replays_match_eager(fused):
     x = W.focus_full_inputs(fc, ac, page_size=page, device="cuda")
     per_token = [x["hidden_rows"], x["residual"], x["rope_pos"], x["cache_idx"]]
     step = FocusFullStep(fc.batch, fc.block, fc.hq, fc.head_dim,
-                         [(t.shape[2:], t.dtype) for t in per_token], fc.dtype, "cuda")
+                         [(t.shape[2:], t.dtype) for t in per_token], fc.dtype, "cuda",
+                         hkv=fc.hkv)
     state = [x[k] for k in ("token_sum", "total_steps", "rightmost_processed", "cached")]
     state0 = [t.clone() for t in state]
     pool0 = (x["pool_k"].clone(), x["pool_v"].clone())
