@@ -264,3 +264,42 @@ def test_esdllm_two_skip_layers():
         np.testing.assert_array_equal(bits(x["h_cache"][layer]).reshape(cfg.batch * L, -1), want_cache)
         surv, n = s_next.contiguous(), keep
     assert n == cfg.generated // 4
+
+
+def test_es_step_graph_replays_match_eager():
+    """The ES-dLLM step (score, top-K, gather, scatter at the batch-8 workload) captured in
+    a HIP graph and replayed three times, with the cache restored eagerly in between:
+    every replay equals the eager step bit for bit."""
+    from block_token_eviction_amd.chain import EsStep
+    cfg = W.ES_B8
+    ei = dev(W.esdllm_inputs(cfg))
+    say("ES-dLLM step under graph capture")
+    step = EsStep(cfg.batch, cfg.generated, cfg.hidden, cfg.keep, cfg.dtype, "cuda")
+    args = dict(h_new=ei["h_new"], h_prev=ei["h_prev"], surv_pos=ei["surv_pos"], conf=ei["conf"],
+                alpha=ei["alpha"], k=ei["k"], new_k=ei["new_k"], new_v=ei["new_v"],
+                row_base=ei["row_base"], cache_k=ei["cache_k"], cache_v=ei["cache_v"])
+    cache0 = (ei["cache_k"].clone(), ei["cache_v"].clone())
+    step.run(**args)
+    torch.cuda.synchronize()
+    n = int(step.cu[-1])
+    outs = lambda: [step.score, step.idx, step.count, step.cu, step.gathered[:n], ei["cache_k"],
+                    ei["cache_v"]]
+    want = [t.clone() for t in outs()]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step.run(**args)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step.run(**args)
+    for rep in range(3):
+        ei["cache_k"].copy_(cache0[0])
+        ei["cache_v"].copy_(cache0[1])
+        step.gathered.zero_()
+        step.score.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs(), want):
+            assert torch.equal(a, b), f"replay {rep}"
