@@ -126,6 +126,16 @@ __device__ __forceinline__ void lds_wait_tr(u32x2 (&v)[N]) {
 // the hint raises the streaming read rate by about a tenth on MI355X.
 constexpr int kStreamPolicy = 2;
 
+// Output stores use the sc0 sc1 nt policy (non-temporal, written through every
+// cache level). Among the K/V read stream this costs less than the plain
+// non-temporal store: the attention measured 1,722 against 1,740 us at batch
+// 1,024 (outputs bit-identical; the load policies tried alongside changed
+// nothing). The policy is reachable through buffer stores, so each workgroup
+// builds a raw buffer resource based at its first output row; the offsets
+// within it stay below 2^31 (the host limits k_max * hq * row bytes).
+constexpr int kOutPolicy = 1 | 2 | 16;               // sc0 | nt | sc1
+constexpr int kRsrcWord3 = 0x00020000;               // gfx9-family raw buffer: 32-bit data format
+
 __device__ __forceinline__ void copy16_to_lds(const char* src, char* lds_dst) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
                                    (void __attribute__((address_space(3)))*)lds_dst, 16, 0,
@@ -548,6 +558,11 @@ __device__ __forceinline__ void attn_body(
   // below reuses the stage memory.
   __builtin_amdgcn_s_waitcnt(kVmcntNoLgkm | vmcnt_bits(0));
 
+  // Output rows of this sequence, as a buffer resource (see kOutPolicy).
+  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+      out + (size_t)__builtin_amdgcn_readfirstlane(cub) * hq * C::kRowBytes, (short)0, 0x7fffffff,
+      kRsrcWord3);
+
   // Merge the 4 wave states: out = sum_w e^(m_w - M) O_w / sum_w e^(m_w - M) l_w.
   float* obuf = reinterpret_cast<float*>(smem);
   float* mbuf = obuf + kWaves * 32 * C::kOStride;
@@ -570,11 +585,11 @@ __device__ __forceinline__ void attn_body(
     __syncthreads();
     // Output: thread t writes 16-byte chunk t % kChunks of a row, so one store
     // instruction covers whole rows (bf16, D = 128: four 256-byte rows, which
-    // are the four query heads of one token, 1 KB contiguous), with the
-    // streaming hint. The output is 0.6 % of the bytes, but writes that reach
-    // DRAM in the middle of the K/V read stream are costly: with plain stores
-    // they took 10 % of the kernel's time (against 1 % for the same stores
-    // kept in L2), with streaming stores 6 %.
+    // are the four query heads of one token, 1 KB contiguous), non-temporal and
+    // written through (kOutPolicy). The output is 0.6 % of the bytes, but writes
+    // that reach DRAM in the middle of the K/V read stream are costly: with
+    // plain stores they took 10 % of the kernel's time (against 1 % for the
+    // same stores kept in L2), with non-temporal stores 6 %.
     constexpr int kChunks = C::kRowBytes / 16;          // 16-byte chunks per output row
     constexpr int kElems = 16 / C::ES;                  // elements per chunk
     // Rows written for this tq: 32 merged ones (key split) or the 32 of each wave.
@@ -605,7 +620,7 @@ __device__ __forceinline__ void attn_body(
         const float inv = 1.0f / Ls;
         const int tok = rho / G;
         const int head = g * G + (rho - tok * G);
-        char* dst = out + (((size_t)(cub + tok)) * hq + head) * C::kRowBytes + 16 * chunk;
+        const int voff = (tok * hq + head) * C::kRowBytes + 16 * chunk;
         float res[kElems];
 #pragma unroll
         for (int i = 0; i < kElems; ++i) {
@@ -624,7 +639,7 @@ __device__ __forceinline__ void attn_body(
 #pragma unroll
           for (int u = 0; u < 4; ++u) val[u] = __float_as_uint(res[u]);
         }
-        st16_stream(dst, val);
+        __builtin_amdgcn_raw_buffer_store_b128(val, orsrc, voff, 0, kOutPolicy);
       }
     }
   }
@@ -900,6 +915,9 @@ static int attention_args_ok(const void* q, const int32_t* count, const int32_t*
   if (dtype != BTE_F32 && dtype != BTE_BF16) return BTE_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(cache_k) || !aligned16(cache_v) || !aligned16(out))
     return BTE_ERR_ALIGN;
+  // one sequence's output rows are stored through a buffer resource of < 2^31 bytes
+  if ((long long)k_max * hq * head_dim * (dtype == BTE_BF16 ? 2 : 4) > 0x7fffffffLL)
+    return BTE_ERR_DIM;
   return BTE_OK;
 }
 

@@ -314,9 +314,11 @@ int bte_kv_scatter_paged(const void* new_k, const void* new_v, const int32_t* id
  *     entry outside [0, batch) is clamped into it (wrong results, no stray
  *     memory access).
  *   scale > 0 and finite (1/sqrt(head_dim) for the standard attention)
- * Limits: head_dim in {64, 128}; hq % hkv == 0.
- * Errors: NULL -> BTE_ERR_NULL; sizes <= 0, k_max < 0, hq % hkv != 0 or a
- * scale that is not positive and finite -> BTE_ERR_DIM; head_dim or dtype
+ * Limits: head_dim in {64, 128}; hq % hkv == 0; k_max * hq * head_dim *
+ * sizeof(dtype) < 2^31 (one sequence's output rows).
+ * Errors: NULL -> BTE_ERR_NULL; sizes <= 0, k_max < 0, hq % hkv != 0, a
+ * scale that is not positive and finite, or k_max beyond the output limit ->
+ * BTE_ERR_DIM; head_dim or dtype
  * unsupported -> BTE_ERR_UNSUPPORTED; q, caches or out not 16-byte aligned ->
  * BTE_ERR_ALIGN.
  */

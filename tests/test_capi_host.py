@@ -118,6 +118,7 @@ def test_attention_errors():
     assert call(a3=MIS) == ALIGN
     assert call(a10=0) == OK                  # nothing kept: no launch
     assert call(a7=None, a10=0) == OK         # the order is optional
+    assert call(a10=1 << 18) == DIM           # 2^18 * 32 heads * 256 B = 2^31 output bytes
 
 
 def test_scatter_attention_errors():
