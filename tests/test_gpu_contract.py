@@ -53,3 +53,40 @@ def test_checked_calls_match_and_violations_raise(monkeypatch):
     with pytest.raises(bte.contract.ContractError):
         bte.kv_scatter(g["new_k"], g["new_v"], g["idx"], g["count"], g["cu"], rb.cuda(),
                        g["cache_k"].clone(), g["cache_v"].clone())
+
+
+def test_checked_fused_scatter_attention(monkeypatch):
+    """The fused scatter + attention under BTE_CHECK=1: a valid call equals the unchecked
+    one (output and caches); a block position past kv_len and an index outside the block
+    raise before launching, leaving the caches untouched."""
+    bte = _bte()
+    cfg = W.AttnCfg("contract_fused", seed=92, batch=12, kept=None, k_lo=0, k_hi=12,
+                    prefix_lo=5, prefix_hi=200)
+    ai = W.attention_inputs(cfg)
+    g = dev(ai)
+    say("contract checks of the fused scatter + attention")
+    pb = ai["prefix"].to(torch.int32).cuda()
+    ck, cv = g["cache_k"].clone(), g["cache_v"].clone()
+    out = bte.kv_scatter_attention(g["q"], g["count"], g["cu"], g["idx"], cfg.block, pb,
+                                   g["new_k"], g["new_v"], ck, cv, g["seq_start"], g["kv_len"],
+                                   ai["k_max"])
+    monkeypatch.setenv("BTE_CHECK", "1")
+    ck2, cv2 = g["cache_k"].clone(), g["cache_v"].clone()
+    out2 = bte.kv_scatter_attention(g["q"], g["count"], g["cu"], g["idx"], cfg.block, pb,
+                                    g["new_k"], g["new_v"], ck2, cv2, g["seq_start"], g["kv_len"],
+                                    ai["k_max"])
+    n = int(ai["cu"][-1])
+    assert torch.equal(out2[:n], out[:n]) and torch.equal(ck2, ck) and torch.equal(cv2, cv)
+    b = int(np.flatnonzero(ai["count"].numpy() > 0)[0])
+    ck3, cv3 = g["cache_k"].clone(), g["cache_v"].clone()
+    late = pb.clone()
+    late[b] = int(ai["kv_len"][b])                         # every kept position at or past kv_len
+    bad_idx = ai["idx"].clone()
+    bad_idx[b, int(ai["count"][b]) - 1] = cfg.block        # outside [0, n)
+    for kw in (dict(pos_base=late, idx=g["idx"]), dict(pos_base=pb, idx=bad_idx.cuda())):
+        with pytest.raises(bte.contract.ContractError):
+            bte.kv_scatter_attention(g["q"], g["count"], g["cu"], kw["idx"], cfg.block,
+                                     kw["pos_base"], g["new_k"], g["new_v"], ck3, cv3,
+                                     g["seq_start"], g["kv_len"], ai["k_max"])
+    torch.cuda.synchronize()
+    assert torch.equal(ck3, g["cache_k"]) and torch.equal(cv3, g["cache_v"])
