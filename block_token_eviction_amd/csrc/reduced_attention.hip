@@ -196,7 +196,11 @@ __device__ __forceinline__ void wait_copies_behind(int behind) {
 // which also waits for every copy in flight: that variant is correct but
 // serialises the pipeline, so it is a separate kernel and the host picks it
 // only when a table has more than kPageCache entries.
-enum { kContig = 0, kPagedLds = 1, kPagedMem = 2 };
+enum { kContig = 0, kPagedLds = 1, kPagedMem = 2, kPagedBig = 3 };
+// kPagedBig: the table in LDS and pages of at least 32 rows, so that every
+// full key tile lies in one page (one lookup per tile, known at compile time).
+template <int kPaged>
+constexpr bool kLdsTable = kPaged == kPagedLds || kPaged == kPagedBig;
 constexpr int kPageCache = 2048;
 
 // One workgroup's work: sequence b, KV head g, the T 32-row query tiles from
@@ -238,7 +242,7 @@ __device__ __forceinline__ void attn_body(
       return (size_t)p;
     } else {
       const int lg = map.lg_page;
-      const int page = kPaged == kPagedLds ? lds_read_word(pages + (p >> lg)) : bt[p >> lg];
+      const int page = kLdsTable<kPaged> ? lds_read_word(pages + (p >> lg)) : bt[p >> lg];
       return ((size_t)page << lg) + (size_t)(p & ((1 << lg) - 1));
     }
   };
@@ -289,7 +293,7 @@ __device__ __forceinline__ void attn_body(
   // rows, since tiles start at multiples of 32) is 32 consecutive cache rows
   // from the row of its first position: one page lookup serves all its copies,
   // K and V. Smaller pages take one lookup per copy.
-  const bool tile_in_page = kPaged == kContig || map.lg_page >= 5;
+  const bool tile_in_page = kPaged == kContig || kPaged == kPagedBig || map.lg_page >= 5;
   // Fused scatter: whether key tile kt holds positions of the block, and the
   // kept row at block index j (-1 if j is not kept or outside the block).
   auto in_block = [&](int kt) { return kt * 32 < pb + sc.n && kt * 32 + 32 > pb; };
@@ -329,7 +333,7 @@ __device__ __forceinline__ void attn_body(
       const int p = kt * 32;
       const int lg = map.lg_page;
       const int page = __builtin_amdgcn_readfirstlane(
-          kPaged == kPagedLds ? lds_read_word(pages + (p >> lg)) : bt[p >> lg]);
+          kLdsTable<kPaged> ? lds_read_word(pages + (p >> lg)) : bt[p >> lg]);
       return ((size_t)page << lg) + (size_t)(p & ((1 << lg) - 1));
     }
   };
@@ -670,7 +674,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T =
     const int32_t* __restrict__ kv_len, const int32_t* __restrict__ order, char* __restrict__ out,
     int batch, int hq, int hkv, int n_rg, int rg_inner, float c, KvScatter sc) {
   __shared__ __attribute__((aligned(16))) char smem[Cfg<D, BF16, kWaves>::kLds];
-  __shared__ int32_t pages[kPaged == kPagedLds ? kPageCache : 1];
+  __shared__ int32_t pages[kLdsTable<kPaged> ? kPageCache : 1];
   int r, g, rg;                                        // r: position in the processing order
   if (rg_inner) {
     const int per_seq = hkv * n_rg;                    // workgroups per sequence
@@ -699,7 +703,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T =
   constexpr int kSpan = kQSplitOk ? 32 * T * kWaves : 32 * T;   // query rows per row group
   const int row0 = rg * kSpan;
   if (row0 >= rows) return;
-  if constexpr (kPaged == kPagedLds) {
+  if constexpr (kLdsTable<kPaged>) {
     const int n_pages = min((kv_len[b] + (1 << map.lg_page) - 1) >> map.lg_page, map.max_pages);
     const int32_t* bt = map.block_table + (size_t)b * map.max_pages;
     for (int i = threadIdx.x; i < n_pages; i += 64 * kWaves) pages[i] = bt[i];
@@ -957,8 +961,9 @@ extern "C" int bte_reduced_attention_paged(const void* q, const int32_t* count, 
   while ((1 << lg) < page_size) ++lg;
   const AttnArgs a{q, count, cu, cache_k, cache_v, KvMap{nullptr, block_table, max_pages, lg},
                    kv_len, order, out, batch, k_max, hq, hkv, scale * kLog2e, {}};
-  return max_pages <= kPageCache ? attention<kPagedLds>(a, head_dim, dtype, stream)
-                                  : attention<kPagedMem>(a, head_dim, dtype, stream);
+  if (max_pages > kPageCache) return attention<kPagedMem>(a, head_dim, dtype, stream);
+  return lg >= 5 ? attention<kPagedBig>(a, head_dim, dtype, stream)
+                 : attention<kPagedLds>(a, head_dim, dtype, stream);
 }
 
 // Host-side checks of the fused scatter's own arguments.
@@ -1014,6 +1019,7 @@ extern "C" int bte_kv_scatter_attention_paged(
              order, out, batch, k_max, hq, hkv, scale * kLog2e, {}};
   a.sc = KvScatter{(const char*)new_k, (const char*)new_v, idx, pos_base, (char*)cache_k,
                    (char*)cache_v, n, k_max};
-  return max_pages <= kPageCache ? attention<kPagedLds, true>(a, head_dim, dtype, stream)
-                                  : attention<kPagedMem, true>(a, head_dim, dtype, stream);
+  if (max_pages > kPageCache) return attention<kPagedMem, true>(a, head_dim, dtype, stream);
+  return lg >= 5 ? attention<kPagedBig, true>(a, head_dim, dtype, stream)
+                 : attention<kPagedLds, true>(a, head_dim, dtype, stream);
 }
