@@ -215,11 +215,14 @@ __device__ __forceinline__ void issue_tile(const char* __restrict__ q0, const ch
   }
 }
 
-template <int D, bool BF16, int R, int kWaves>
+// kFull: a block of exactly 32 positions, known at compile time, so that the
+// tile loop carries no code for padding keys and query rows.
+template <int D, bool BF16, int R, int kWaves, bool kFull>
 __global__ __launch_bounds__(64 * kWaves) void focus_delta_kernel(
     const char* __restrict__ q0, const char* __restrict__ k0, const char* __restrict__ q1,
     const char* __restrict__ k1, const uint8_t* __restrict__ decoded, float* __restrict__ out,
     int B, int hq, int hkv, int rt_r, float c) {
+  if constexpr (kFull) B = 32;
   using Tl = Tile<D, BF16>;
   using Row = HalfRow<D, BF16>;
   // Two LDS stages per wave when they fit in 128 KB.
@@ -326,9 +329,14 @@ template <int D, bool BF16, int R, int kWaves>
 hipError_t launch_w(const void* q0, const void* k0, const void* q1, const void* k1,
                     const uint8_t* decoded, float* out, int batch, int B, int hq, int hkv, int rt_r,
                     float c, hipStream_t stream) {
-  hipLaunchKernelGGL((focus_delta_kernel<D, BF16, R, kWaves>), dim3(batch), dim3(64 * kWaves), 0,
-                     stream, (const char*)q0, (const char*)k0, (const char*)q1, (const char*)k1,
-                     decoded, out, B, hq, hkv, rt_r, c);
+  if (B == 32)
+    hipLaunchKernelGGL((focus_delta_kernel<D, BF16, R, kWaves, true>), dim3(batch),
+                       dim3(64 * kWaves), 0, stream, (const char*)q0, (const char*)k0,
+                       (const char*)q1, (const char*)k1, decoded, out, B, hq, hkv, rt_r, c);
+  else
+    hipLaunchKernelGGL((focus_delta_kernel<D, BF16, R, kWaves, false>), dim3(batch),
+                       dim3(64 * kWaves), 0, stream, (const char*)q0, (const char*)k0,
+                       (const char*)q1, (const char*)k1, decoded, out, B, hq, hkv, rt_r, c);
   return hipGetLastError();
 }
 
