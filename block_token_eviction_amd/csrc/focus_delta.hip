@@ -216,13 +216,20 @@ __device__ __forceinline__ void issue_tile(const char* __restrict__ q0, const ch
 }
 
 // kFull: a block of exactly 32 positions, known at compile time, so that the
-// tile loop carries no code for padding keys and query rows.
-template <int D, bool BF16, int R, int kWaves, bool kFull>
+// tile loop carries no code for padding keys and query rows. kG > 0: kG query
+// heads per KV head and one KV group per wave (hkv == kWaves), so that every
+// wave's tile sequence (K of both layers, then the Q tiles) is known at
+// compile time.
+template <int D, bool BF16, int R, int kWaves, bool kFull, int kG>
 __global__ __launch_bounds__(64 * kWaves) void focus_delta_kernel(
     const char* __restrict__ q0, const char* __restrict__ k0, const char* __restrict__ q1,
     const char* __restrict__ k1, const uint8_t* __restrict__ decoded, float* __restrict__ out,
     int B, int hq, int hkv, int rt_r, float c) {
   if constexpr (kFull) B = 32;
+  if constexpr (kG > 0) {
+    hkv = kWaves;
+    hq = kG * kWaves;
+  }
   using Tl = Tile<D, BF16>;
   using Row = HalfRow<D, BF16>;
   // Two LDS stages per wave when they fit in 128 KB.
@@ -235,14 +242,14 @@ __global__ __launch_bounds__(64 * kWaves) void focus_delta_kernel(
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31;
   const int h = lane >> 5;
-  const int G = hq / hkv;
+  const int G = kG > 0 ? kG : hq / hkv;
   const int kj = 16 * ((n >> 2) & 1) + (n & 3) + 4 * (n >> 3);
   const bool qvalid = n < B;
   char* wring = ring + w * kStages * Tl::kBytes;
 
   // Tile t of group gi (this wave's gi-th group): t = 0, 1 -> K of layer 0, 1;
   // t = 2 + 2e + l -> Q of head e of the group, layer l.
-  const int ngroups = (hkv - w + kWaves - 1) / kWaves;
+  const int ngroups = kG > 0 ? 1 : (hkv - w + kWaves - 1) / kWaves;
   const int per_group = 2 + 2 * G;
   const int ntiles = ngroups * per_group;
   const int lrow = lane / Tl::kChunks;
@@ -329,12 +336,20 @@ template <int D, bool BF16, int R, int kWaves>
 hipError_t launch_w(const void* q0, const void* k0, const void* q1, const void* k1,
                     const uint8_t* decoded, float* out, int batch, int B, int hq, int hkv, int rt_r,
                     float c, hipStream_t stream) {
+  if constexpr (kWaves == 8) {
+    if (B == 32 && hkv == 8 && hq == 32) {
+      hipLaunchKernelGGL((focus_delta_kernel<D, BF16, R, kWaves, true, 4>), dim3(batch),
+                         dim3(64 * kWaves), 0, stream, (const char*)q0, (const char*)k0,
+                         (const char*)q1, (const char*)k1, decoded, out, B, hq, hkv, rt_r, c);
+      return hipGetLastError();
+    }
+  }
   if (B == 32)
-    hipLaunchKernelGGL((focus_delta_kernel<D, BF16, R, kWaves, true>), dim3(batch),
+    hipLaunchKernelGGL((focus_delta_kernel<D, BF16, R, kWaves, true, 0>), dim3(batch),
                        dim3(64 * kWaves), 0, stream, (const char*)q0, (const char*)k0,
                        (const char*)q1, (const char*)k1, decoded, out, B, hq, hkv, rt_r, c);
   else
-    hipLaunchKernelGGL((focus_delta_kernel<D, BF16, R, kWaves, false>), dim3(batch),
+    hipLaunchKernelGGL((focus_delta_kernel<D, BF16, R, kWaves, false, 0>), dim3(batch),
                        dim3(64 * kWaves), 0, stream, (const char*)q0, (const char*)k0,
                        (const char*)q1, (const char*)k1, decoded, out, B, hq, hkv, rt_r, c);
   return hipGetLastError();
