@@ -667,12 +667,20 @@ __device__ __forceinline__ void attn_body(
 // kQSplitOk: a row group spans 32*T*kWaves query rows; a workgroup with more
 // than 32*T real rows in it splits them over its waves (attn_body kQSplit),
 // one with fewer splits the keys as usual.
-template <int D, bool BF16, int T, int kWaves, int kPaged, bool kQSplitOk, bool kScatter>
+// kFixed: 32 query heads over 8 KV heads, known at compile time (constant row
+// strides and head mapping in the tile loop's address arithmetic).
+template <int D, bool BF16, int T, int kWaves, int kPaged, bool kQSplitOk, bool kScatter,
+          bool kFixed = false>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T == 1 ? 2 : 1))) void attn_kernel(
     const char* __restrict__ q, const int32_t* __restrict__ count, const int32_t* __restrict__ cu,
     const char* __restrict__ cache_k, const char* __restrict__ cache_v, KvMap map,
     const int32_t* __restrict__ kv_len, const int32_t* __restrict__ order, char* __restrict__ out,
     int batch, int hq, int hkv, int n_rg, int rg_inner, float c, KvScatter sc) {
+  if constexpr (kFixed) {
+    hq = 32;
+    hkv = 8;
+    rg_inner = 1;
+  }
   __shared__ __attribute__((aligned(16))) char smem[Cfg<D, BF16, kWaves>::kLds];
   __shared__ int32_t pages[kLdsTable<kPaged> ? kPageCache : 1];
   int r, g, rg;                                        // r: position in the processing order
@@ -771,6 +779,15 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   const long n_rg = (rows + span - 1) / span;
   const long grid = (long)((a.batch + kXcds - 1) / kXcds) * kXcds * a.hkv * n_rg;
   if (grid > 0x7fffffffL) return hipErrorInvalidValue;
+  if constexpr (BF16 && D == 128 && !kScatter && (kPaged == kContig || kPaged == kPagedBig)) {
+    if (a.hq == 32 && a.hkv == 8) {
+      hipLaunchKernelGGL((attn_kernel<D, BF16, T, kWaves, kPaged, kQSplitOk, kScatter, true>),
+                         dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, (const char*)a.q,
+                         a.count, a.cu, (const char*)a.ck, (const char*)a.cv, a.map, a.kl,
+                         a.order, (char*)a.out, a.batch, a.hq, a.hkv, (int)n_rg, 1, a.c, a.sc);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((attn_kernel<D, BF16, T, kWaves, kPaged, kQSplitOk, kScatter>),
                      dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, (const char*)a.q, a.count,
                      a.cu, (const char*)a.ck, (const char*)a.cv, a.map, a.kl, a.order,
