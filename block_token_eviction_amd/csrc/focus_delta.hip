@@ -266,7 +266,7 @@ __global__ __launch_bounds__(64 * kWaves) void focus_delta_kernel(
   Row K0, K1;
   if (ntiles > 0) issue(0, 0);
   if (kStages == 2 && ntiles > 1) issue(1, 1);
-  for (int tile = 0; tile < ntiles; ++tile) {
+  auto step = [&](int tile) __attribute__((always_inline)) {
     const int stage = kStages == 2 ? (tile & 1) : 0;
     if (kStages == 2 && tile + 1 < ntiles) {
       __builtin_amdgcn_s_waitcnt(kVmcntNoLgkm | vmcnt_bits(Tl::kCopies));
@@ -302,6 +302,13 @@ __global__ __launch_bounds__(64 * kWaves) void focus_delta_kernel(
       if (t & 1) pool_softmax_accumulate<R>(s, h, rt_r, B, c, qvalid, acc1);
       else pool_softmax_accumulate<R>(s, h, rt_r, B, c, qvalid, acc0);
     }
+  };
+  if constexpr (kG > 0) {
+    // the 2 + 2G tiles of the wave's one group, unrolled: each tile's kind is static
+#pragma unroll
+    for (int tile = 0; tile < 2 + 2 * kG; ++tile) step(tile);
+  } else {
+    for (int tile = 0; tile < ntiles; ++tile) step(tile);
   }
 
   // Sum over the 32 query rows held by each lane half (fixed butterfly order).
