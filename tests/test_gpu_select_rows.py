@@ -50,6 +50,20 @@ def test_topk_random_with_ties(n):
     _topk(s, k, min(n, 40))
 
 
+@pytest.mark.parametrize("n", [1, 7, 32, 64, 65, 200, 256, 257, 1024])
+@pytest.mark.parametrize("batch", [1, 2, 3, 8, 9, 32, 33])
+def test_topk_small_batches(n, batch):
+    """Small and odd batch sizes across the kernel's row-width classes (n <= 64, <= 256,
+    <= 1024): ties, -inf, NaN, K <= 0 and K > n; counts and cu also with k_max = 0."""
+    r = np.random.default_rng(1000 * n + batch)
+    s = r.integers(-3, 4, size=(batch, n)).astype(np.float32) * 0.5
+    s[r.uniform(size=s.shape) < 0.25] = -np.inf
+    s[r.uniform(size=s.shape) < 0.02] = np.nan
+    k = r.integers(-1, n + 2, size=batch)
+    _topk(s, k, min(n, 40))
+    _topk(s, k, 0)                                          # counts and cu only
+
+
 def test_topk_config_shapes_and_long_scan():
     r = np.random.default_rng(5)
     s = r.standard_normal((5000, 32)).astype(np.float32)                 # > 1024 rows: scan loops
