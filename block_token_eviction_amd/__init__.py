@@ -109,20 +109,59 @@ def _want(t, dtype, name):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _need(cond: bool, msg: str):
+    """Host-side argument check that survives ``python -O`` (unlike assert)."""
+    if not cond:
+        raise ValueError(msg)
+
+
+def _shape(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _i32(t, name, shape=None):
+    """An int32 index tensor (a wider integer would be read as pairs of int32)."""
+    if t is None:
+        return
+    _want(t, torch.int32, name)
+    if shape is not None:
+        _shape(t, shape, name)
+
+
+def _kept_lists(idx, count, cu, batch=None):
+    """idx int32 [batch, k_max], count int32 [batch], cu int32 [batch + 1] -> (batch, k_max)."""
+    _need(idx.dim() == 2, f"idx must be [batch, k_max], got {tuple(idx.shape)}")
+    b, k_max = idx.shape
+    if batch is not None:
+        _need(b == batch, f"idx has {b} rows for a batch of {batch}")
+    _i32(idx, "idx")
+    _i32(count, "count", (b,))
+    _i32(cu, "cu", (b + 1,))
+    return b, k_max
+
+
+def _row_bytes(t) -> int:
+    return t[0].numel() * t.element_size() if t.shape[0] else 0
+
+
 def focus_importance_delta(q0, k0, q1, k1, decoded, pool_kernel: int, out=None):
     """q* [batch, B, hq, D], k* [batch, B, hkv, D], decoded uint8 [batch, B] -> delta f32 [batch, B]."""
     _dev(q0, k0, q1, k1, decoded, out)
+    _need(q0.dim() == 4 and k0.dim() == 4, "q* must be [batch, B, hq, D] and k* [batch, B, hkv, D]")
     batch, block, hq, d = q0.shape
     hkv = k0.shape[2]
-    for t in (q1,):
-        assert t.shape == q0.shape and t.dtype == q0.dtype
-    for t in (k0, k1):
-        assert t.shape == (batch, block, hkv, d) and t.dtype == q0.dtype
+    _shape(q1, q0.shape, "q1")
+    _need(q1.dtype == q0.dtype, "q0 and q1 must share a dtype")
+    for name, t in (("k0", k0), ("k1", k1)):
+        _shape(t, (batch, block, hkv, d), name)
+        _need(t.dtype == q0.dtype, f"{name} must have the dtype of q0")
     _want(decoded, torch.uint8, "decoded")
-    assert decoded.shape == (batch, block)
+    _shape(decoded, (batch, block), "decoded")
     if out is None:
         out = torch.empty((batch, block), dtype=torch.float32, device=q0.device)
     _want(out, torch.float32, "out")
+    _shape(out, (batch, block), "out")
     _check("bte_focus_importance_delta", lib.bte_focus_importance_delta(
         _ptr(q0), _ptr(k0), _ptr(q1), _ptr(k1), _ptr(decoded), _ptr(out), batch, block, hq, hkv,
         d, pool_kernel, _dtype(q0), _stream()))
@@ -132,14 +171,18 @@ def focus_importance_delta(q0, k0, q1, k1, decoded, pool_kernel: int, out=None):
 def esdllm_score(h_new, h_prev, surv_pos, conf, alpha: float, out=None):
     """h_new [batch, n_surv, h], h_prev [batch, L, h], surv_pos int32, conf f32 [batch, L]."""
     _dev(h_new, h_prev, surv_pos, conf, out)
+    _need(h_new.dim() == 3 and h_prev.dim() == 3, "h_new and h_prev must be [batch, rows, hidden]")
     batch, n_surv, hidden = h_new.shape
     seq_len = h_prev.shape[1]
-    assert h_prev.shape == (batch, seq_len, hidden) and h_prev.dtype == h_new.dtype
-    _want(surv_pos, torch.int32, "surv_pos")
+    _shape(h_prev, (batch, seq_len, hidden), "h_prev")
+    _need(h_prev.dtype == h_new.dtype, "h_new and h_prev must share a dtype")
+    _i32(surv_pos, "surv_pos", (batch, n_surv))
     _want(conf, torch.float32, "conf")
-    assert surv_pos.shape == (batch, n_surv) and conf.shape == (batch, seq_len)
+    _shape(conf, (batch, seq_len), "conf")
     if out is None:
         out = torch.empty((batch, n_surv), dtype=torch.float32, device=h_new.device)
+    _want(out, torch.float32, "out")
+    _shape(out, (batch, n_surv), "out")
     if contract.enabled():
         contract.check_positions(surv_pos, h_prev.shape[1], "surv_pos")
     _check("bte_esdllm_score", lib.bte_esdllm_score(
@@ -152,8 +195,9 @@ def topk_select(scores, k, k_max: int, idx=None, count=None, cu=None):
     """scores f32 [batch, n], k int32 [batch] -> (idx [batch, k_max], count [batch], cu [batch+1])."""
     _dev(scores, k, idx, count, cu)
     _want(scores, torch.float32, "scores")
-    _want(k, torch.int32, "k")
+    _need(scores.dim() == 2, "scores must be [batch, n]")
     batch, n = scores.shape
+    _i32(k, "k", (batch,))
     dev = scores.device
     if idx is None:
         idx = torch.empty((batch, max(k_max, 0)), dtype=torch.int32, device=dev)
@@ -161,6 +205,9 @@ def topk_select(scores, k, k_max: int, idx=None, count=None, cu=None):
         count = torch.empty((batch,), dtype=torch.int32, device=dev)
     if cu is None:
         cu = torch.empty((batch + 1,), dtype=torch.int32, device=dev)
+    _i32(idx, "idx", (batch, max(k_max, 0)))
+    _i32(count, "count", (batch,))
+    _i32(cu, "cu", (batch + 1,))
     _check("bte_topk_select", lib.bte_topk_select(
         _ptr(scores), _ptr(k), _ptr(idx) if k_max > 0 else None, _ptr(count), _ptr(cu), batch, n,
         k_max, _stream()))
@@ -173,12 +220,14 @@ def gather_rows(src, idx, count, cu, out=None):
     Without `out`, the capacity is batch * k_max rows (the device-side total is
     not read back)."""
     _dev(src, idx, count, cu, out)
+    _need(src.dim() >= 3, "src must be [batch, n, ...]")
     batch, n = src.shape[:2]
-    k_max = idx.shape[1]
+    _, k_max = _kept_lists(idx, count, cu, batch)
     row_bytes = src[0, 0].numel() * src.element_size()
     if out is None:
         out = torch.empty((batch * k_max,) + tuple(src.shape[2:]), dtype=src.dtype, device=src.device)
-    assert out.dtype == src.dtype and out[0].numel() * out.element_size() == row_bytes
+    _need(out.dtype == src.dtype, "out must have the dtype of src")
+    _need(_row_bytes(out) == row_bytes, "out rows must be the size of src rows")
     if contract.enabled():
         contract.check_rows(idx, count, cu, k_max, n=n, out_rows=out.shape[0])
     _check("bte_gather_rows", lib.bte_gather_rows(
@@ -190,10 +239,21 @@ def gather_rows(src, idx, count, cu, out=None):
 def kv_scatter(new_k, new_v, idx, count, cu, row_base, cache_k, cache_v, pos_map=None):
     """Write new_k/new_v rows cu[b]+t into cache rows row_base[b] + pos (in place)."""
     _dev(new_k, new_v, idx, count, cu, row_base, cache_k, cache_v, pos_map)
+    batch, k_max = _kept_lists(idx, count, cu)
     _want(row_base, torch.int64, "row_base")
-    batch, k_max = idx.shape
-    row_bytes = cache_k[0].numel() * cache_k.element_size()
-    assert new_k[0].numel() * new_k.element_size() == row_bytes
+    _shape(row_base, (batch,), "row_base")
+    row_bytes = _row_bytes(cache_k)
+    _need(_row_bytes(new_k) == row_bytes, "new_k rows must be the size of cache_k rows")
+    _need(new_k.dtype == cache_k.dtype, "new_k must have the dtype of cache_k")
+    _need((new_v is None) == (cache_v is None), "give new_v and cache_v together")
+    if new_v is not None:
+        _shape(new_v, new_k.shape, "new_v")
+        _shape(cache_v, cache_k.shape, "cache_v")
+        _need(new_v.dtype == new_k.dtype and cache_v.dtype == cache_k.dtype,
+              "K and V tensors must share a dtype")
+    if pos_map is not None:
+        _i32(pos_map, "pos_map")
+        _need(pos_map.dim() == 2 and pos_map.shape[0] == batch, "pos_map must be [batch, n]")
     n = 0 if pos_map is None else pos_map.shape[1]
     if contract.enabled():
         contract.check_scatter(idx, count, cu, k_max, row_base, cache_k.shape[0], new_k.shape[0],
@@ -204,25 +264,59 @@ def kv_scatter(new_k, new_v, idx, count, cu, row_base, cache_k, cache_v, pos_map
     return cache_k, cache_v
 
 
+def _attn_shapes(q, count, cu, cache_k, cache_v):
+    """q [rows, hq, D], count int32 [batch], cu int32 [batch + 1], cache K/V [rows, hkv, D]
+    of q's dtype -> (hq, D, hkv, batch)."""
+    _need(q.dim() == 3 and cache_k.dim() == 3, "q must be [rows, hq, D] and the cache [rows, hkv, D]")
+    _need(count.dim() == 1, "count must be [batch]")
+    batch = count.shape[0]
+    _i32(count, "count")
+    _i32(cu, "cu", (batch + 1,))
+    hq, d = q.shape[1], q.shape[2]
+    hkv = cache_k.shape[1]
+    _need(cache_k.shape[2] == d, "the cache's head dim must equal q's")
+    _shape(cache_v, cache_k.shape, "cache_v")
+    _need(cache_k.dtype == q.dtype and cache_v.dtype == q.dtype, "the cache must have q's dtype")
+    return hq, d, hkv, batch
+
+
+def _attn_out(q, out):
+    if out is None:
+        return torch.empty_like(q)
+    _need(out.dtype == q.dtype and out.dim() == 3 and out.shape[1:] == q.shape[1:],
+          "out must be [rows, hq, D] with q's dtype")
+    return out
+
+
+def _fused_rows(idx, pos_base, new_k, new_v, q, cache_k, batch, k_max):
+    _i32(idx, "idx", (batch, k_max))
+    _i32(pos_base, "pos_base", (batch,))
+    _need(new_k.dim() == 3 and new_k.shape[1:] == cache_k.shape[1:],
+          "new_k must be [rows, hkv, D] like the cache")
+    _shape(new_v, new_k.shape, "new_v")
+    _need(new_k.dtype == q.dtype and new_v.dtype == q.dtype, "new_k/new_v must have q's dtype")
+
+
+def _page_table(block_table, batch):
+    _want(block_table, torch.int32, "block_table")
+    _need(block_table.dim() == 2 and block_table.shape[0] == batch,
+          "block_table must be [batch, max_pages]")
+
+
 def reduced_attention(q, count, cu, cache_k, cache_v, seq_start, kv_len, k_max: int,
                       scale: float | None = None, out=None, order=None):
     """q [capacity, hq, D], cache [rows, hkv, D] -> out [capacity, hq, D] (rows cu[b]+t written).
 
     `order` (int32 [batch], e.g. from attention_order) only schedules the work."""
     _dev(q, count, cu, cache_k, cache_v, seq_start, kv_len, out, order)
+    hq, d, hkv, batch = _attn_shapes(q, count, cu, cache_k, cache_v)
     _want(seq_start, torch.int64, "seq_start")
-    _want(kv_len, torch.int32, "kv_len")
-    hq, d = q.shape[1], q.shape[2]
-    hkv = cache_k.shape[1]
-    batch = count.shape[0]
-    assert cache_v.shape == cache_k.shape and cache_k.dtype == q.dtype
-    if order is not None:
-        _want(order, torch.int32, "order")
-        assert order.shape == (batch,)
+    _shape(seq_start, (batch,), "seq_start")
+    _i32(kv_len, "kv_len", (batch,))
+    _i32(order, "order", (batch,))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
+    out = _attn_out(q, out)
     if contract.enabled():
         contract.check_attention(count, cu, kv_len, k_max, min(q.shape[0], out.shape[0]),
                                  seq_start=seq_start, cache_rows=cache_k.shape[0], order=order)
@@ -241,24 +335,15 @@ def kv_scatter_attention(q, count, cu, idx, n: int, pos_base, new_k, new_v, cach
     idx int32 [batch, k_max] block indices in [0, n); pos_base int32 [batch]. The cache is
     updated in place and out [capacity, hq, D] (rows cu[b]+t) is the attention over it."""
     _dev(q, count, cu, idx, pos_base, new_k, new_v, cache_k, cache_v, seq_start, kv_len, out, order)
+    hq, d, hkv, batch = _attn_shapes(q, count, cu, cache_k, cache_v)
     _want(seq_start, torch.int64, "seq_start")
-    _want(kv_len, torch.int32, "kv_len")
-    _want(pos_base, torch.int32, "pos_base")
-    _want(idx, torch.int32, "idx")
-    hq, d = q.shape[1], q.shape[2]
-    hkv = cache_k.shape[1]
-    batch = count.shape[0]
-    assert idx.shape == (batch, k_max) and pos_base.shape == (batch,)
-    assert cache_v.shape == cache_k.shape and cache_k.dtype == q.dtype
-    assert new_k.shape[1:] == cache_k.shape[1:] and new_v.shape == new_k.shape
-    assert new_k.dtype == q.dtype and new_v.dtype == q.dtype
-    if order is not None:
-        _want(order, torch.int32, "order")
-        assert order.shape == (batch,)
+    _shape(seq_start, (batch,), "seq_start")
+    _i32(kv_len, "kv_len", (batch,))
+    _i32(order, "order", (batch,))
+    _fused_rows(idx, pos_base, new_k, new_v, q, cache_k, batch, k_max)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
+    out = _attn_out(q, out)
     if contract.enabled():
         contract.check_attention(count, cu, kv_len, k_max, min(q.shape[0], out.shape[0]),
                                  seq_start=seq_start, cache_rows=cache_k.shape[0], order=order)
@@ -276,14 +361,13 @@ def attention_order(kv_len, out=None, count=None, group: int = 1):
     ascending. Work is the length, or with the kept counts (int32 [batch]) and group =
     hq / hkv the length times ceil(count * group / 64) query passes."""
     _dev(kv_len, out, count)
-    _want(kv_len, torch.int32, "kv_len")
+    _need(kv_len.dim() == 1, "kv_len must be [batch]")
     batch = kv_len.shape[0]
-    if count is not None:
-        _want(count, torch.int32, "count")
-        assert count.shape == (batch,)
+    _i32(kv_len, "kv_len")
+    _i32(count, "count", (batch,))
     if out is None:
         out = torch.empty((batch,), dtype=torch.int32, device=kv_len.device)
-    _want(out, torch.int32, "out")
+    _i32(out, "out", (batch,))
     _check("bte_attention_order", lib.bte_attention_order(_ptr(kv_len), _ptr(count), int(group),
                                                           batch, _ptr(out), _stream()))
     return out
@@ -293,13 +377,13 @@ def focus_budget(delta, token_sum, total_steps, alpha: float, threshold_mode: in
     """delta f32 [batch, B], token_sum/total_steps int32 [batch] -> K int32 [batch]."""
     _dev(delta, token_sum, total_steps, out)
     _want(delta, torch.float32, "delta")
-    _want(token_sum, torch.int32, "token_sum")
-    _want(total_steps, torch.int32, "total_steps")
+    _need(delta.dim() == 2, "delta must be [batch, B]")
     batch, block = delta.shape
-    assert token_sum.shape == (batch,) and total_steps.shape == (batch,)
+    _i32(token_sum, "token_sum", (batch,))
+    _i32(total_steps, "total_steps", (batch,))
     if out is None:
         out = torch.empty((batch,), dtype=torch.int32, device=delta.device)
-    _want(out, torch.int32, "out")
+    _i32(out, "out", (batch,))
     _check("bte_focus_budget", lib.bte_focus_budget(
         _ptr(delta), _ptr(token_sum), _ptr(total_steps), float(alpha), int(threshold_mode),
         _ptr(out), batch, block, _stream()))
@@ -311,10 +395,11 @@ def focus_history_update(decoded_prev, decoded_now, token_sum, total_steps):
     _dev(decoded_prev, decoded_now, token_sum, total_steps)
     _want(decoded_prev, torch.uint8, "decoded_prev")
     _want(decoded_now, torch.uint8, "decoded_now")
-    _want(token_sum, torch.int32, "token_sum")
-    _want(total_steps, torch.int32, "total_steps")
+    _need(decoded_now.dim() == 2, "decoded_now must be [batch, B]")
     batch, block = decoded_now.shape
-    assert decoded_prev.shape == (batch, block)
+    _shape(decoded_prev, (batch, block), "decoded_prev")
+    _i32(token_sum, "token_sum", (batch,))
+    _i32(total_steps, "total_steps", (batch,))
     _check("bte_focus_history_update", lib.bte_focus_history_update(
         _ptr(decoded_prev), _ptr(decoded_now), _ptr(token_sum), _ptr(total_steps), batch, block,
         _stream()))
@@ -326,10 +411,12 @@ def focus_select(delta, k, decoded, rightmost_processed, idx=None, count=None, c
     -> (idx int32 [batch, B], count [batch], cu [batch + 1]); rightmost_processed updated in place."""
     _dev(delta, k, decoded, rightmost_processed, idx, count, cu)
     _want(delta, torch.float32, "delta")
-    _want(k, torch.int32, "k")
-    _want(decoded, torch.uint8, "decoded")
-    _want(rightmost_processed, torch.int32, "rightmost_processed")
+    _need(delta.dim() == 2, "delta must be [batch, B]")
     batch, block = delta.shape
+    _i32(k, "k", (batch,))
+    _want(decoded, torch.uint8, "decoded")
+    _shape(decoded, (batch, block), "decoded")
+    _i32(rightmost_processed, "rightmost_processed", (batch,))
     dev = delta.device
     if idx is None:
         idx = torch.empty((batch, block), dtype=torch.int32, device=dev)
@@ -337,6 +424,9 @@ def focus_select(delta, k, decoded, rightmost_processed, idx=None, count=None, c
         count = torch.empty((batch,), dtype=torch.int32, device=dev)
     if cu is None:
         cu = torch.empty((batch + 1,), dtype=torch.int32, device=dev)
+    _i32(idx, "idx", (batch, block))
+    _i32(count, "count", (batch,))
+    _i32(cu, "cu", (batch + 1,))
     _check("bte_focus_select", lib.bte_focus_select(
         _ptr(delta), _ptr(k), _ptr(decoded), _ptr(rightmost_processed), _ptr(idx), _ptr(count),
         _ptr(cu), batch, block, _stream()))
@@ -348,19 +438,13 @@ def reduced_attention_paged(q, count, cu, cache_k, cache_v, block_table, page_si
     """q [capacity, hq, D]; page pool cache [n_pages * page_size, hkv, D];
     block_table int32 [batch, max_pages] -> out [capacity, hq, D]."""
     _dev(q, count, cu, cache_k, cache_v, block_table, kv_len, out, order)
-    _want(block_table, torch.int32, "block_table")
-    _want(kv_len, torch.int32, "kv_len")
-    hq, d = q.shape[1], q.shape[2]
-    hkv = cache_k.shape[1]
-    batch = count.shape[0]
-    assert cache_v.shape == cache_k.shape and cache_k.dtype == q.dtype
-    assert block_table.shape[0] == batch
-    if order is not None:
-        _want(order, torch.int32, "order")
+    hq, d, hkv, batch = _attn_shapes(q, count, cu, cache_k, cache_v)
+    _page_table(block_table, batch)
+    _i32(kv_len, "kv_len", (batch,))
+    _i32(order, "order", (batch,))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
+    out = _attn_out(q, out)
     if contract.enabled():
         contract.check_attention(count, cu, kv_len, k_max, min(q.shape[0], out.shape[0]),
                                  cache_rows=cache_k.shape[0], block_table=block_table,
@@ -379,25 +463,14 @@ def kv_scatter_attention_paged(q, count, cu, idx, n: int, pos_base, new_k, new_v
     in one launch over the same page pool and table."""
     _dev(q, count, cu, idx, pos_base, new_k, new_v, cache_k, cache_v, block_table, kv_len, out,
          order)
-    _want(block_table, torch.int32, "block_table")
-    _want(kv_len, torch.int32, "kv_len")
-    _want(pos_base, torch.int32, "pos_base")
-    _want(idx, torch.int32, "idx")
-    hq, d = q.shape[1], q.shape[2]
-    hkv = cache_k.shape[1]
-    batch = count.shape[0]
-    assert idx.shape == (batch, k_max) and pos_base.shape == (batch,)
-    assert cache_v.shape == cache_k.shape and cache_k.dtype == q.dtype
-    assert new_k.shape[1:] == cache_k.shape[1:] and new_v.shape == new_k.shape
-    assert new_k.dtype == q.dtype and new_v.dtype == q.dtype
-    assert block_table.shape[0] == batch
-    if order is not None:
-        _want(order, torch.int32, "order")
-        assert order.shape == (batch,)
+    hq, d, hkv, batch = _attn_shapes(q, count, cu, cache_k, cache_v)
+    _page_table(block_table, batch)
+    _i32(kv_len, "kv_len", (batch,))
+    _i32(order, "order", (batch,))
+    _fused_rows(idx, pos_base, new_k, new_v, q, cache_k, batch, k_max)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
+    out = _attn_out(q, out)
     if contract.enabled():
         contract.check_attention(count, cu, kv_len, k_max, min(q.shape[0], out.shape[0]),
                                  cache_rows=cache_k.shape[0], block_table=block_table,
@@ -417,11 +490,21 @@ def kv_scatter_paged(new_k, new_v, idx, count, cu, pos_base, block_table, page_s
                      cache_k, cache_v, pos_map=None):
     """Write new_k/new_v rows cu[b]+t to the pool rows of logical positions pos_base[b] + pos."""
     _dev(new_k, new_v, idx, count, cu, pos_base, block_table, cache_k, cache_v, pos_map)
-    _want(pos_base, torch.int32, "pos_base")
-    _want(block_table, torch.int32, "block_table")
-    batch, k_max = idx.shape
-    row_bytes = cache_k[0].numel() * cache_k.element_size()
-    assert new_k[0].numel() * new_k.element_size() == row_bytes
+    batch, k_max = _kept_lists(idx, count, cu)
+    _i32(pos_base, "pos_base", (batch,))
+    _page_table(block_table, batch)
+    row_bytes = _row_bytes(cache_k)
+    _need(_row_bytes(new_k) == row_bytes, "new_k rows must be the size of cache_k rows")
+    _need(new_k.dtype == cache_k.dtype, "new_k must have the dtype of cache_k")
+    _need((new_v is None) == (cache_v is None), "give new_v and cache_v together")
+    if new_v is not None:
+        _shape(new_v, new_k.shape, "new_v")
+        _shape(cache_v, cache_k.shape, "cache_v")
+        _need(new_v.dtype == new_k.dtype and cache_v.dtype == cache_k.dtype,
+              "K and V tensors must share a dtype")
+    if pos_map is not None:
+        _i32(pos_map, "pos_map")
+        _need(pos_map.dim() == 2 and pos_map.shape[0] == batch, "pos_map must be [batch, n]")
     n = 0 if pos_map is None else pos_map.shape[1]
     if contract.enabled():
         contract.check_scatter_paged(idx, count, cu, k_max, pos_base, block_table, page_size,
@@ -439,12 +522,16 @@ def focus_commit_mask(decoded, cached, commit=None, block_done=None):
     _dev(decoded, cached, commit, block_done)
     _want(decoded, torch.uint8, "decoded")
     _want(cached, torch.uint8, "cached")
+    _need(decoded.dim() == 2, "decoded must be [batch, B]")
     batch, block = decoded.shape
-    assert cached.shape == (batch, block)
+    _shape(cached, (batch, block), "cached")
     if commit is None:
         commit = torch.empty_like(decoded)
     if block_done is None:
         block_done = torch.empty((batch,), dtype=torch.int32, device=decoded.device)
+    _want(commit, torch.uint8, "commit")
+    _shape(commit, (batch, block), "commit")
+    _i32(block_done, "block_done", (batch,))
     _check("bte_focus_commit_mask", lib.bte_focus_commit_mask(
         _ptr(decoded), _ptr(cached), _ptr(commit), _ptr(block_done), batch, block, _stream()))
     return commit, block_done
@@ -458,17 +545,20 @@ def gather_rows_multi(srcs, idx, count, cu, outs=None):
     """Each src [batch, n, ...] compacted with the same index set in one launch;
     returns the outputs [batch * k_max, ...] (rows cu[b]+t written)."""
     _dev(idx, count, cu, *srcs)
-    batch, k_max = idx.shape
+    batch, k_max = _kept_lists(idx, count, cu)
+    _need(len(srcs) >= 1 and srcs[0].dim() >= 2, "give at least one src [batch, n, ...]")
     n = srcs[0].shape[1]
     if outs is None:
         outs = [torch.empty((batch * k_max,) + tuple(s.shape[2:]), dtype=s.dtype, device=s.device)
                 for s in srcs]
+    _need(len(outs) == len(srcs), "give one output per source")
     _dev(*outs)
     descs = []
-    for s_, o in zip(srcs, outs):
-        assert s_.shape[:2] == (batch, n) and o.dtype == s_.dtype
+    for i, (s_, o) in enumerate(zip(srcs, outs)):
+        _need(s_.dim() >= 2 and tuple(s_.shape[:2]) == (batch, n), f"src {i} must be [batch, n, ...]")
+        _need(o.dtype == s_.dtype, f"output {i} must have the dtype of its source")
         rb = s_[0, 0].numel() * s_.element_size()
-        assert o[0].numel() * o.element_size() == rb
+        _need(_row_bytes(o) == rb, f"output {i} rows must be the size of its source rows")
         descs.append(_RowsTensor(s_.data_ptr(), o.data_ptr(), rb))
     if contract.enabled():
         contract.check_rows(idx, count, cu, k_max, n=n, out_rows=min(o.shape[0] for o in outs))

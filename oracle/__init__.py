@@ -18,8 +18,6 @@ operations of the path, written from the pages' definitions:
   exact KV cache (ES-dLLM notes page, key design 2; FOCUS paper App. E.2.4).
 * ``reduced_attention`` — attention of the kept queries over prefix plus
   block KV (FOCUS paper Section 2, Section 4.2; App. E.2.4).
-* ``attention_order`` — the longest-first work order the GPU attention is
-  scheduled by (a scheduling helper, not part of the method).
 * ``focus_budget``, ``history_update`` — FOCUS dynamic budget K and its
   per-sequence history (FOCUS notes page, key design 2; FOCUS paper
   Section 4.1, App. E.3.1).
@@ -48,11 +46,10 @@ from .budget import focus_budget, history_update
 from .rows import gather_rows, gather_rows_multi, kv_scatter
 from .cache_state import commit_mask
 from .attention import reduced_attention
-from .schedule import attention_order
 from .paged import kv_scatter_paged, reduced_attention_paged, physical_row
 
 __all__ = ["block_scores", "maxpool_keys", "softmax_keys", "importance",
            "focus_importance_delta", "esdllm_score", "topk_select", "gather_rows",
-           "kv_scatter", "reduced_attention", "attention_order", "focus_budget",
+           "kv_scatter", "reduced_attention", "focus_budget",
            "history_update", "focus_select", "kv_scatter_paged", "reduced_attention_paged",
            "physical_row", "commit_mask", "gather_rows_multi", "esdllm_skip_layer"]

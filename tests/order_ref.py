@@ -1,9 +1,11 @@
-"""Work order of the reduced attention (oracle; test use only).
+"""Reference of the reduced attention's work order (test helper).
 
-Not part of the method's arithmetic: the GPU library starts the attention of
-the largest work items first (greedy longest-processing-time scheduling), and
-this is the order it must produce, by definition: sequence indices sorted by
-estimated work descending, equal work by index ascending.
+A scheduling definition of the library, not part of the method (the pages
+define no order), so it lives with the tests rather than in the oracle: the
+GPU library starts the attention of the largest work items first (greedy
+longest-processing-time scheduling), and this is the order it must produce,
+by definition: sequence indices sorted by estimated work descending, equal
+work by index ascending. Any order gives the same attention outputs.
 
 Work of sequence i: its KV length (negative counts as 0); with the kept-row
 counts given, the length times the number of 64-row query passes over its

@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import oracle
+import order_ref
 import workloads as W
 from helpers import assert_close, dev, say
 
@@ -113,7 +114,7 @@ def test_attention_order_matches_oracle(batch):
     lens = np.random.default_rng(batch).integers(-3, 300, batch).astype(np.int32)   # ties, negatives
     say(f"attention_order batch={batch}")
     got = bte.attention_order(torch.from_numpy(lens).cuda()).cpu().numpy()
-    np.testing.assert_array_equal(got, oracle.attention_order(lens))
+    np.testing.assert_array_equal(got, order_ref.attention_order(lens))
 
 
 @pytest.mark.parametrize("batch", [1, 65, 1024, 5000, 16384])
@@ -127,7 +128,7 @@ def test_attention_order_by_work_matches_oracle(batch):
     say(f"attention_order by work batch={batch}")
     got = bte.attention_order(torch.from_numpy(lens).cuda(), count=torch.from_numpy(cnt).cuda(),
                               group=4).cpu().numpy()
-    np.testing.assert_array_equal(got, oracle.attention_order(lens, count=cnt, group=4))
+    np.testing.assert_array_equal(got, order_ref.attention_order(lens, count=cnt, group=4))
 
 
 @pytest.mark.parametrize("lens,cnt,group", [
@@ -140,7 +141,7 @@ def test_attention_order_by_work_saturates(lens, cnt, group):
     say(f"attention_order saturation lens={lens.tolist()} cnt={cnt.tolist()} group={group}")
     got = bte.attention_order(torch.from_numpy(lens).cuda(), count=torch.from_numpy(cnt).cuda(),
                               group=group).cpu().numpy()
-    np.testing.assert_array_equal(got, oracle.attention_order(lens, count=cnt, group=group))
+    np.testing.assert_array_equal(got, order_ref.attention_order(lens, count=cnt, group=group))
 
 
 def test_attention_order_only_schedules():

@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import oracle
+import order_ref
 
 
 def _sel(batch, n, k_max, seed):
@@ -125,12 +126,12 @@ def test_attention_order_brute_force():
                  if all(eff[p[i]] > eff[p[i + 1]] or (eff[p[i]] == eff[p[i + 1]] and p[i] < p[i + 1])
                         for i in range(len(p) - 1))]
         assert len(valid) == 1
-        np.testing.assert_array_equal(oracle.attention_order(np.array(lens, np.int32)), valid[0])
+        np.testing.assert_array_equal(order_ref.attention_order(np.array(lens, np.int32)), valid[0])
 
 
 def test_attention_order_invariants():
     lens = np.random.default_rng(8).integers(1, 50, 3000).astype(np.int32)
-    o = oracle.attention_order(lens)
+    o = order_ref.attention_order(lens)
     assert sorted(o.tolist()) == list(range(lens.size))
     d = lens[o]
     assert np.all(d[:-1] >= d[1:])
@@ -142,7 +143,7 @@ def test_attention_order_by_work_hand_example():
     """Worked by hand, group 4 (64 query rows per pass): counts 17, 3, 20, 0, 16 give
     68, 12, 80, 0, 64 rows per KV head, so 2, 1, 2, 0, 1 passes; with lengths 100, 100,
     60, 50, 130 the work is 200, 100, 120, 0, 130."""
-    got = oracle.attention_order(np.array([100, 100, 60, 50, 130], np.int32),
+    got = order_ref.attention_order(np.array([100, 100, 60, 50, 130], np.int32),
                                  count=np.array([17, 3, 20, 0, 16], np.int32), group=4)
     np.testing.assert_array_equal(got, [0, 4, 2, 1, 3])
 
@@ -152,16 +153,16 @@ def test_attention_order_by_work_special_cases():
     lens = r.integers(-2, 400, 500).astype(np.int32)
     # one pass for every sequence that keeps rows: the length order, empty sequences last
     cnt = r.integers(1, 17, 500).astype(np.int32)
-    np.testing.assert_array_equal(oracle.attention_order(lens, count=cnt, group=4),
-                                  oracle.attention_order(lens))
+    np.testing.assert_array_equal(order_ref.attention_order(lens, count=cnt, group=4),
+                                  order_ref.attention_order(lens))
     lens = np.maximum(lens, 1)             # zero work only from the counts below
     cnt[::7] = 0
-    o = oracle.attention_order(lens, count=cnt, group=4)
+    o = order_ref.attention_order(lens, count=cnt, group=4)
     tail = o[-int((cnt == 0).sum()):]
     assert set(tail.tolist()) == set(np.flatnonzero(cnt == 0).tolist())
     assert np.all(np.diff(tail) > 0)
     # work saturates at 2^32 - 1: the two largest tie and keep index order
-    big = oracle.attention_order(np.array([2 ** 30, 2 ** 30 - 5, 7], np.int32),
+    big = order_ref.attention_order(np.array([2 ** 30, 2 ** 30 - 5, 7], np.int32),
                                  count=np.array([64 * 8, 64 * 9, 1], np.int32), group=1)
     np.testing.assert_array_equal(big, [0, 1, 2])
 
