@@ -23,7 +23,8 @@
 // tile is the R boundary keys and two scalars with lane l^32. Column sums are
 // accumulated per lane over all tiles and reduced across lanes and waves once,
 // in a fixed order (no atomics), so results are bitwise reproducible and two
-// identical layers give dI = +0.0 exactly.
+// identical layers give dI = +0.0 exactly. Blocks of 33 to 64 positions take
+// a second kernel (two key and two query-row tiles; described below).
 #include <math.h>
 
 #include "bte_device.h"
@@ -87,15 +88,15 @@ __device__ __forceinline__ f32x16 score_tile(const HalfRow<D, BF16>& k, const Ha
   return acc;
 }
 
-// Max over windows of 2R+1 entries of ext (16 + 2R entries): out[r] covers
+// Max over windows of 2R+1 entries of ext (NK + 2R entries): out[r] covers
 // ext[r .. r + 2R]. Doubling: after the pass of width w, a[x] = max(ext[x..x+2w-1]).
-template <int R>
-__device__ __forceinline__ void sliding_max(float (&ext)[16 + 2 * R], float (&out)[16]) {
+template <int R, int NK>
+__device__ __forceinline__ void sliding_max(float (&ext)[NK + 2 * R], float (&out)[NK]) {
   constexpr int W = 2 * R + 1;
-  constexpr int N = 16 + 2 * R;
+  constexpr int N = NK + 2 * R;
   if constexpr (R == 0) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) out[r] = ext[r];
+    for (int r = 0; r < NK; ++r) out[r] = ext[r];
   } else {
     float a[N];
 #pragma unroll
@@ -110,7 +111,7 @@ __device__ __forceinline__ void sliding_max(float (&ext)[16 + 2 * R], float (&ou
       }
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) out[r] = fmaxf(a[r], a[r + W - w]);
+    for (int r = 0; r < NK; ++r) out[r] = fmaxf(a[r], a[r + W - w]);
   }
 }
 
@@ -140,7 +141,7 @@ __device__ __forceinline__ void pool_softmax_accumulate(const f32x16& s, int h, 
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) ext[R + r] = s[r];
-    sliding_max<R>(ext, p);
+    sliding_max<R, 16>(ext, p);
   } else {
     // Any radius: bring the whole 32-key row into the lane.
     float full[32];
@@ -339,6 +340,274 @@ __global__ __launch_bounds__(64 * kWaves) void focus_delta_kernel(
   }
 }
 
+// ---- Blocks of 33 to 64 positions -------------------------------------------
+//
+// The B keys of a row span two MFMA key tiles and the B query rows two query
+// tiles. Key tile u feeds MFMA row m from block key
+//   32*((m/4)%2) + 16*u + m%4 + 4*(m/8),
+// so that lane l holds the 32 contiguous keys 32*(l/32) .. +31 of its query
+// row: key 32*(l/32) + 16*u + r in register r of tile u's product. In LDS,
+// row r of key tile u holds block key r + 16*(r >= 16) + 16*u, which keeps
+// the operand read of the 32-key kernel (row pi(m)). Pooling, the row max,
+// exp and the row sum stay in-lane, with the same boundary exchange as the
+// 32-key kernel. A group's tiles run layer by layer (both key tiles, then the
+// query tiles of each head, two row tiles per head), so only one layer's keys
+// are held in registers; the column sums of a layer are folded into LDS at
+// its last tile, in a fixed order.
+
+// Pool, softmax and accumulate one query row of up to 64 keys: s[r] is the
+// score with key 32*h + r (keys >= B already -inf); lanes l and l^32 together
+// hold the row.
+template <int R, bool kFull>
+__device__ __forceinline__ void pool_softmax_accumulate_wide(const float (&s)[32], int h, int rt_r,
+                                                             int B, float c, bool row_ok,
+                                                             float (&acc)[32]) {
+  float m = s[0];
+#pragma unroll
+  for (int r = 1; r < 32; ++r) m = fmaxf(m, s[r]);
+  m = fmaxf(m, swap_halves(m));
+
+  float p[32];
+  if constexpr (R >= 0) {
+    float ext[32 + 2 * R];
+    if constexpr (R > 0) {
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        const float recv = swap_halves(h ? s[t] : s[32 - R + t]);
+        ext[t] = h ? recv : -INFINITY;                 // keys 32h - R + t
+        ext[R + 32 + t] = h ? -INFINITY : recv;        // keys 32h + 32 + t
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 32; ++r) ext[R + r] = s[r];
+    sliding_max<R, 32>(ext, p);
+  } else if (rt_r >= B - 1) {
+    // The window of every key covers the whole row: each pooled value is the row max.
+#pragma unroll
+    for (int r = 0; r < 32; ++r) p[r] = m;
+  } else {
+    // Any other radius: rt_r rounds of a radius-1 max. Rounds compose exactly
+    // (round t gives the max over [j - t, j + t]), and the lane pair trades one
+    // edge key each per round.
+#pragma unroll
+    for (int r = 0; r < 32; ++r) p[r] = s[r];
+    for (int it = 0; it < rt_r; ++it) {
+      const float left = swap_halves(p[31]);       // key 31, for the upper half
+      const float right = swap_halves(p[0]);       // key 32, for the lower half
+      float q[32];
+#pragma unroll
+      for (int x = 0; x < 32; ++x) {
+        const float lo = x > 0 ? p[x - 1] : (h ? left : -INFINITY);
+        const float hi = x < 31 ? p[x + 1] : (h ? -INFINITY : right);
+        q[x] = fmaxf(p[x], fmaxf(lo, hi));
+      }
+#pragma unroll
+      for (int x = 0; x < 32; ++x) p[x] = q[x];
+    }
+  }
+  if constexpr (!kFull) {
+#pragma unroll
+    for (int r = 0; r < 32; ++r) p[r] = (32 * h + r < B) ? p[r] : -INFINITY;
+  }
+
+  const float mc = m * c;
+  float e[32];
+  float sum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    e[r] = fast_exp2(fmaf(p[r], c, -mc));
+    sum += e[r];
+  }
+  sum += swap_halves(sum);
+  const float inv = row_ok ? 1.0f / sum : 0.0f;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) acc[r] = fmaf(e[r], inv, acc[r]);
+}
+
+// Copies tile u of one layer's tiles of KV group g of sequence b into LDS at
+// dst: u = 0, 1 -> key tile u of that layer (k); u = 2 + 2e + qt -> query rows
+// 32*qt .. +31 of the group's query head e (q). Lane (lrow, lslot) copies as in
+// issue_tile. Rows past the block repeat its last row (their scores are masked).
+template <int D, bool BF16>
+__device__ __forceinline__ void issue_tile_wide(const char* __restrict__ q,
+                                                const char* __restrict__ k, int b, int B, int hq,
+                                                int hkv, int g, int u, char* dst, int lrow,
+                                                int lslot) {
+  using Tl = Tile<D, BF16>;
+  const char* src;
+  uint32_t stride;
+  int qt = 0;
+  if (u < 2) {
+    src = k + ((size_t)b * B * hkv + g) * Tl::kRowBytes;
+    stride = (uint32_t)hkv * Tl::kRowBytes;
+  } else {
+    const int e = (u - 2) >> 1;
+    qt = (u - 2) & 1;
+    src = q + ((size_t)b * B * hq + (size_t)g * (hq / hkv) + e) * Tl::kRowBytes;
+    stride = (uint32_t)hq * Tl::kRowBytes;
+  }
+#pragma unroll
+  for (int i = 0; i < Tl::kCopies; ++i) {
+    const int row = Tl::kRpi * i + lrow;
+    const int brow = u < 2 ? row + 16 * (row >= 16) + 16 * u : 32 * qt + row;
+    const int srow = brow < B ? brow : B - 1;
+    __builtin_amdgcn_global_load_lds(
+        (const void __attribute__((address_space(1)))*)(src + srow * stride + 16 * swz(row, lslot)),
+        (void __attribute__((address_space(3)))*)(dst + 1024 * i), 16, 0, kStreamPolicy);
+  }
+}
+
+// kFull: B = 64 at compile time. kG > 0: kG query heads per KV head and one
+// group per wave (hkv == kWaves), so the tile sequence is static and unrolled.
+template <int D, bool BF16, int R, int kWaves, bool kFull, int kG>
+__global__ __launch_bounds__(64 * kWaves) void focus_delta_wide_kernel(
+    const char* __restrict__ q0, const char* __restrict__ k0, const char* __restrict__ q1,
+    const char* __restrict__ k1, const uint8_t* __restrict__ decoded, float* __restrict__ out,
+    int B, int hq, int hkv, int rt_r, float c) {
+  if constexpr (kFull) B = 64;
+  if constexpr (kG > 0) {
+    hkv = kWaves;
+    hq = kG * kWaves;
+  }
+  using Tl = Tile<D, BF16>;
+  using Row = HalfRow<D, BF16>;
+  constexpr int kStages = kWaves * 2 * Tl::kBytes <= 128 * 1024 ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) char ring[kWaves * kStages * Tl::kBytes];
+  __shared__ float red[kWaves][2][64];
+
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31;
+  const int h = lane >> 5;
+  const int G = kG > 0 ? kG : hq / hkv;
+  const int kj = 16 * ((n >> 2) & 1) + (n & 3) + 4 * (n >> 3);
+  char* wring = ring + w * kStages * Tl::kBytes;
+
+  // Tile t of group gi: layer l = t / per_layer, u = t % per_layer (u = 0, 1:
+  // key tiles; u = 2 + 2e + qt: query tile qt of head e).
+  const int ngroups = kG > 0 ? 1 : (hkv - w + kWaves - 1) / kWaves;
+  const int per_layer = 2 + 2 * G;
+  const int per_group = 2 * per_layer;
+  const int ntiles = ngroups * per_group;
+  const int lrow = lane / Tl::kChunks;
+  const int lslot = lane % Tl::kChunks;
+  float acc[32];
+#pragma unroll
+  for (int r = 0; r < 32; ++r) acc[r] = 0.f;
+
+  auto issue = [&](int tile, int stage) __attribute__((always_inline)) {
+    const int gi = tile / per_group;
+    const int t = tile - gi * per_group;
+    const int l = t >= per_layer;
+    issue_tile_wide<D, BF16>(l ? q1 : q0, l ? k1 : k0, b, B, hq, hkv, w + gi * kWaves,
+                             t - l * per_layer, wring + stage * Tl::kBytes, lrow, lslot);
+  };
+  Row KA, KB;
+  if (ntiles > 0) issue(0, 0);
+  if (kStages == 2 && ntiles > 1) issue(1, 1);
+  auto step = [&](int tile) __attribute__((always_inline)) {
+    const int stage = kStages == 2 ? (tile & 1) : 0;
+    if (kStages == 2 && tile + 1 < ntiles) {
+      __builtin_amdgcn_s_waitcnt(kVmcntNoLgkm | vmcnt_bits(Tl::kCopies));
+    } else {
+      __builtin_amdgcn_s_waitcnt(kVmcntNoLgkm | vmcnt_bits(0));
+    }
+    __builtin_amdgcn_wave_barrier();
+    const char* src = wring + stage * Tl::kBytes;
+    const int gi = tile / per_group;
+    const int t = tile - gi * per_group;
+    const int l = t >= per_layer;
+    const int u = t - l * per_layer;
+    auto refill = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      __builtin_amdgcn_wave_barrier();
+      if (tile + kStages < ntiles) issue(tile + kStages, stage);
+    };
+    if (u < 2) {
+      if (u == 0) read_half<D, BF16>(KA, src, kj, h);
+      else read_half<D, BF16>(KB, src, kj, h);
+      refill();
+      return;
+    }
+    Row Q;
+    read_half<D, BF16>(Q, src, n, h);
+    refill();
+    const f32x16 sa = score_tile<D, BF16>(KA, Q);
+    const f32x16 sb = score_tile<D, BF16>(KB, Q);
+    float s[32];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = sa[r];
+      s[16 + r] = sb[r];
+    }
+    if constexpr (!kFull) {
+#pragma unroll
+      for (int r = 0; r < 32; ++r) s[r] = (32 * h + r < B) ? s[r] : -INFINITY;
+    }
+    const bool row_ok = kFull || 32 * ((u - 2) & 1) + n < B;
+    pool_softmax_accumulate_wide<R, kFull>(s, h, rt_r, B, c, row_ok, acc);
+    if (u == per_layer - 1) {
+      // The layer's last tile: sum the 32 query rows of each lane half (fixed
+      // butterfly order) and fold the group's column sums into LDS.
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+#pragma unroll
+        for (int x = 1; x < 32; x <<= 1) acc[r] += __shfl_xor(acc[r], x, kWave);
+      }
+      if (n == 0) {
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+          float* slot = &red[w][l][32 * h + r];
+          *slot = gi == 0 ? acc[r] : *slot + acc[r];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 32; ++r) acc[r] = 0.f;
+    }
+  };
+  if constexpr (kG > 0) {
+#pragma unroll
+    for (int tile = 0; tile < 2 * (2 + 2 * kG); ++tile) step(tile);
+  } else {
+    for (int tile = 0; tile < ntiles; ++tile) step(tile);
+  }
+
+  __syncthreads();
+  if (threadIdx.x < B) {
+    const int j = threadIdx.x;
+    float i0 = 0.f, i1 = 0.f;
+    for (int v = 0; v < kWaves; ++v) {
+      i0 += red[v][0][j];
+      i1 += red[v][1][j];
+    }
+    out[(size_t)b * B + j] = decoded[(size_t)b * B + j] ? -INFINITY : i1 - i0;
+  }
+}
+
+template <int D, bool BF16, int R, int kWaves>
+hipError_t launch_wide_w(const void* q0, const void* k0, const void* q1, const void* k1,
+                         const uint8_t* decoded, float* out, int batch, int B, int hq, int hkv,
+                         int rt_r, float c, hipStream_t stream) {
+  if constexpr (kWaves == 8 && R >= 0) {
+    if (B == 64 && hkv == 8 && hq == 32) {
+      hipLaunchKernelGGL((focus_delta_wide_kernel<D, BF16, R, kWaves, true, 4>), dim3(batch),
+                         dim3(64 * kWaves), 0, stream, (const char*)q0, (const char*)k0,
+                         (const char*)q1, (const char*)k1, decoded, out, B, hq, hkv, rt_r, c);
+      return hipGetLastError();
+    }
+  }
+  if (B == 64)
+    hipLaunchKernelGGL((focus_delta_wide_kernel<D, BF16, R, kWaves, true, 0>), dim3(batch),
+                       dim3(64 * kWaves), 0, stream, (const char*)q0, (const char*)k0,
+                       (const char*)q1, (const char*)k1, decoded, out, B, hq, hkv, rt_r, c);
+  else
+    hipLaunchKernelGGL((focus_delta_wide_kernel<D, BF16, R, kWaves, false, 0>), dim3(batch),
+                       dim3(64 * kWaves), 0, stream, (const char*)q0, (const char*)k0,
+                       (const char*)q1, (const char*)k1, decoded, out, B, hq, hkv, rt_r, c);
+  return hipGetLastError();
+}
+
 template <int D, bool BF16, int R, int kWaves>
 hipError_t launch_w(const void* q0, const void* k0, const void* q1, const void* k1,
                     const uint8_t* decoded, float* out, int batch, int B, int hq, int hkv, int rt_r,
@@ -370,6 +639,12 @@ hipError_t launch_r(const void* q0, const void* k0, const void* q1, const void* 
                     const uint8_t* decoded, float* out, int batch, int B, int hq, int hkv, int rt_r,
                     float c, hipStream_t stream) {
   constexpr bool kWide = BF16 || D < 128;
+  if (B > 32) {
+    if (kWide && hkv >= 8) return launch_wide_w<D, BF16, R, kWide ? 8 : 4>(q0, k0, q1, k1, decoded, out, batch, B, hq, hkv, rt_r, c, stream);
+    if (hkv >= 4) return launch_wide_w<D, BF16, R, 4>(q0, k0, q1, k1, decoded, out, batch, B, hq, hkv, rt_r, c, stream);
+    if (hkv >= 2) return launch_wide_w<D, BF16, R, 2>(q0, k0, q1, k1, decoded, out, batch, B, hq, hkv, rt_r, c, stream);
+    return launch_wide_w<D, BF16, R, 1>(q0, k0, q1, k1, decoded, out, batch, B, hq, hkv, rt_r, c, stream);
+  }
   if (kWide && hkv >= 8) return launch_w<D, BF16, R, kWide ? 8 : 4>(q0, k0, q1, k1, decoded, out, batch, B, hq, hkv, rt_r, c, stream);
   if (hkv >= 4) return launch_w<D, BF16, R, 4>(q0, k0, q1, k1, decoded, out, batch, B, hq, hkv, rt_r, c, stream);
   if (hkv >= 2) return launch_w<D, BF16, R, 2>(q0, k0, q1, k1, decoded, out, batch, B, hq, hkv, rt_r, c, stream);
@@ -399,14 +674,14 @@ extern "C" int bte_focus_importance_delta(const void* q0, const void* k0, const 
   using namespace bte;
   if (!q0 || !k0 || !q1 || !k1 || !decoded || !delta_out) return BTE_ERR_NULL;
   if (batch <= 0 || hq <= 0 || hkv <= 0 || block < 1 || hq % hkv != 0) return BTE_ERR_DIM;
-  if (block > 32) return BTE_ERR_UNSUPPORTED;
+  if (block > 64) return BTE_ERR_DIM;
   if (head_dim != 64 && head_dim != 128) return BTE_ERR_UNSUPPORTED;
   if (pool_kernel < 1 || pool_kernel % 2 == 0) return BTE_ERR_UNSUPPORTED;
   if (dtype != BTE_F32 && dtype != BTE_BF16) return BTE_ERR_UNSUPPORTED;
   if (!aligned16(q0) || !aligned16(k0) || !aligned16(q1) || !aligned16(k1)) return BTE_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(delta_out) & 3u) != 0) return BTE_ERR_ALIGN;
-  // Radii beyond the block are all equivalent to "whole row".
-  const int r = (pool_kernel - 1) / 2 > 32 ? 32 : (pool_kernel - 1) / 2;
+  // Radii of a block's length or more are all equivalent to "whole row".
+  const int r = (pool_kernel - 1) / 2 > 64 ? 64 : (pool_kernel - 1) / 2;
   const float c = (float)(1.4426950408889634 / sqrt((double)head_dim));
   hipError_t e;
   if (dtype == BTE_BF16) {

@@ -64,7 +64,8 @@ int bte_version(void);
  *   k0, k1   [batch, block, hkv, head_dim]  dtype
  *   decoded  [batch, block] uint8 (1 byte alignment)
  *   delta_out[batch, block] float32 (4 byte alignment)
- * Limits: 1 <= block <= 32; head_dim in {64, 128}; hq % hkv == 0;
+ * Limits: 1 <= block <= 64 (the FOCUS paper runs blocks of 16, 32 and 64,
+ * Section 5.3 "Impact of Block Size"); head_dim in {64, 128}; hq % hkv == 0;
  * pool_kernel odd and >= 1 (>= 2*block-1 pools the whole row).
  * Errors: NULL pointer -> BTE_ERR_NULL; batch/hq/hkv <= 0, block out of
  * range or hq % hkv != 0 -> BTE_ERR_DIM; head_dim, even pool_kernel or

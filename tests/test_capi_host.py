@@ -51,7 +51,7 @@ def test_focus_errors():
     assert _focus(batch=0) == DIM
     assert _focus(hq=6, hkv=4) == DIM
     assert _focus(block=0) == DIM
-    assert _focus(block=33) == UNSUP
+    assert _focus(block=65) == DIM             # blocks of 1..64 positions
     assert _focus(d=96) == UNSUP
     assert _focus(pool=4) == UNSUP
     assert _focus(pool=0) == UNSUP

@@ -104,3 +104,83 @@ def test_all_decoded_and_spike_closed_form():
     dec[:] = 1
     got = bte.focus_importance_delta(q0.cuda(), k0.cuda(), q1.cuda(), k1.cuda(), dec.cuda(), 7).cpu().numpy()
     assert np.all(np.isneginf(got))
+
+
+# Blocks of 33..64 positions (the FOCUS paper runs blocks of 16, 32 and 64,
+# Section 5.3 "Impact of Block Size"): two key tiles and two query-row tiles.
+WIDE_CASES = [
+    # block, hq, hkv, head_dim, pool, dtype
+    (64, 32, 8, 128, 7, W.BF16),      # the workload head shape, static tile sequence
+    (64, 32, 8, 128, 1, W.BF16),
+    (64, 32, 8, 128, 3, W.BF16),
+    (64, 32, 8, 128, 5, W.BF16),
+    (63, 32, 8, 128, 7, W.BF16),      # one padding key and query row
+    (48, 32, 8, 128, 7, W.BF16),
+    (33, 32, 8, 128, 3, W.BF16),      # one real row in the second tiles
+    (64, 32, 8, 128, 9, W.BF16),      # runtime radius 4 (dilation rounds)
+    (64, 32, 8, 128, 127, W.BF16),    # window covers the whole row
+    (40, 16, 4, 64, 41, W.BF16),      # runtime radius 20 on a ragged block
+    (50, 8, 2, 64, 99, W.BF16),       # whole row on a ragged block
+    (64, 16, 16, 128, 7, W.BF16),     # more KV heads than waves
+    (64, 12, 4, 128, 7, W.BF16),      # odd group size 3
+    (64, 64, 8, 128, 7, W.BF16),      # 8 query heads per KV head
+    (37, 4, 1, 64, 7, W.BF16),        # single KV head
+    (64, 4, 4, 64, 7, W.F32),
+    (48, 8, 8, 128, 5, W.F32),        # fp32 at head dim 128
+    (64, 8, 2, 128, 11, W.F32),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=[str(c[:5]) for c in WIDE_CASES])
+def test_wide_blocks(case):
+    B, hq, hkv, D, pool, dt = case
+    cfg = W.FocusCfg("wide", seed=13, batch=5, block=B, hq=hq, hkv=hkv, head_dim=D, dtype=dt,
+                     pool_kernel=pool, hidden=64)
+    got, ref, _ = _run(cfg)
+    assert_close(got, ref, str(case))
+
+
+def test_focus_b64_full_size():
+    """Batch 256, block 64, 32q/8kv heads, head dim 128, bf16, MaxPool 7: every output."""
+    cfg = W.FocusCfg("focus_b256_block64", seed=2, batch=256, block=64)
+    got, ref, _ = _run(cfg)
+    assert_close(got, ref, "focus_b256_block64")
+
+
+@pytest.mark.parametrize("B,p,pool", [(64, 40, 7), (64, 0, 7), (64, 63, 3), (48, 47, 9), (64, 20, 1)])
+def test_wide_spike_closed_form(B, p, pool):
+    """Spike input (layer-0 queries zero, layer-1 rows e0, one key s*sqrt(D)*e0): the delta
+    is Hq (B e^s / Z - 1) inside the pooling window around p and Hq (B / Z - 1) outside,
+    Z = n_w e^s + B - n_w."""
+    bte = _bte()
+    hq, D = 4, 64
+    q0 = torch.zeros((1, B, hq, D))
+    k0 = torch.randn((1, B, hq, D), generator=torch.Generator().manual_seed(2))
+    q1 = torch.zeros((1, B, hq, D)); q1[..., 0] = 1.0
+    k1 = torch.zeros((1, B, hq, D)); k1[0, p, :, 0] = 5.5          # s = 5.5 / sqrt(64)
+    dec = torch.zeros((1, B), dtype=torch.uint8)
+    say(f"wide spike B={B} p={p} pool={pool}")
+    got = bte.focus_importance_delta(q0.cuda(), k0.cuda(), q1.cuda(), k1.cuda(), dec.cuda(),
+                                     pool).cpu().numpy()[0]
+    r = (pool - 1) // 2
+    es = np.exp(5.5 / 8.0)
+    nw = min(B - 1, p + r) - max(0, p - r) + 1
+    Z = nw * es + B - nw
+    want = np.where(np.abs(np.arange(B) - p) <= r, hq * (B * es / Z - 1), hq * (B / Z - 1))
+    assert_close(got, want, f"spike B={B} p={p}")
+
+
+def test_wide_identical_layers_give_exact_zero_and_runs_are_bitwise_equal():
+    bte = _bte()
+    cfg = W.FocusCfg("det_wide", seed=14, batch=16, block=64)
+    g = dev(W.focus_inputs(cfg))
+    say("focus determinism, block 64")
+    a = bte.focus_importance_delta(g["q0"], g["k0"], g["q0"], g["k0"], g["decoded"], 7)
+    b1 = bte.focus_importance_delta(g["q0"], g["k0"], g["q1"], g["k1"], g["decoded"], 7)
+    b2 = bte.focus_importance_delta(g["q0"], g["k0"], g["q1"], g["k1"], g["decoded"], 7)
+    torch.cuda.synchronize()
+    a = a.cpu().numpy()
+    dec = g["decoded"].cpu().numpy() != 0
+    assert np.all(np.isneginf(a[dec]))
+    assert np.all(a[~dec] == 0.0) and not np.any(np.signbit(a[~dec]))
+    assert torch.equal(b1, b2)

@@ -53,10 +53,13 @@ def test_spike_closed_form(case):
         assert d[j] == pytest.approx(want, abs=1e-12)
 
 
-@pytest.mark.parametrize("pool_kernel,p,es", [(3, 5, 3.0), (5, 31, 1.5), (9, 1, 7.0)])
-def test_spike_general(pool_kernel, p, es):
-    """Same closed form for other windows, edge positions and spike heights e^s > 1."""
-    B, hq, hkv, D = 32, 8, 2, 64
+@pytest.mark.parametrize("B,pool_kernel,p,es", [(32, 3, 5, 3.0), (32, 5, 31, 1.5), (32, 9, 1, 7.0),
+                                                 (64, 7, 40, 2.0), (64, 1, 63, 3.0), (64, 9, 0, 1.5),
+                                                 (48, 13, 33, 2.5), (33, 7, 32, 4.0)])
+def test_spike_general(B, pool_kernel, p, es):
+    """Same closed form for other windows, edge positions, spike heights e^s > 1 and
+    block sizes up to 64 (the FOCUS paper runs blocks of 16, 32 and 64, Section 5.3)."""
+    hq, hkv, D = 8, 2, 64
     s = math.log(es)
     q0 = np.zeros((1, B, hq, D))
     q1 = np.zeros((1, B, hq, D)); q1[..., 0] = 1.0
@@ -70,10 +73,11 @@ def test_spike_general(pool_kernel, p, es):
         assert d[j] == pytest.approx(want, abs=1e-12)
 
 
+@pytest.mark.parametrize("B", [32, 64])
 @pytest.mark.parametrize("pool_kernel", [1, 3, 5, 7, 9])
-def test_maxpool_matches_torch(pool_kernel):
-    S = _rand((2, 3, 5, 32), pool_kernel)
-    ref = torch.nn.functional.max_pool1d(torch.from_numpy(S).reshape(-1, 1, 32),
+def test_maxpool_matches_torch(pool_kernel, B):
+    S = _rand((2, 3, 5, B), pool_kernel)
+    ref = torch.nn.functional.max_pool1d(torch.from_numpy(S).reshape(-1, 1, B),
                                          pool_kernel, stride=1, padding=pool_kernel // 2)
     np.testing.assert_array_equal(oracle.maxpool_keys(S, pool_kernel),
                                   ref.reshape(S.shape).numpy())
@@ -86,10 +90,10 @@ def test_pool1_is_plain_softmax_column_sum():
     np.testing.assert_allclose(oracle.importance(q, k, 4, 2, 1), want, rtol=1e-12)
 
 
-@pytest.mark.parametrize("pool_kernel", [63, 65, 101])
-def test_pool_whole_row_is_uniform(pool_kernel):
+@pytest.mark.parametrize("B,pool_kernel", [(32, 63), (32, 65), (32, 101), (64, 127), (48, 95)])
+def test_pool_whole_row_is_uniform(B, pool_kernel):
     """k >= 2B-1: every pooled entry is the row max, softmax uniform, I_j = Hq."""
-    q, k = _rand((3, 32, 8, 16), 4), _rand((3, 32, 2, 16), 5)
+    q, k = _rand((3, B, 8, 16), 4), _rand((3, B, 2, 16), 5)
     np.testing.assert_allclose(oracle.importance(q, k, 8, 2, pool_kernel), 8.0, rtol=1e-13)
 
 
