@@ -23,7 +23,8 @@ __all__ = ["lib", "LIB_PATH", "BteError", "status_string", "focus_importance_del
            "esdllm_score", "topk_select", "gather_rows", "kv_scatter", "reduced_attention",
            "attention_order", "reduced_attention_paged", "kv_scatter_paged", "focus_budget",
            "focus_history_update", "focus_select", "focus_commit_mask", "gather_rows_multi",
-           "kv_scatter_attention", "kv_scatter_attention_paged", "BTE_F32", "BTE_BF16", "contract"]
+           "kv_scatter_attention", "kv_scatter_attention_paged", "esdllm_score_update",
+           "esdllm_schedule", "gather_rows_multi_ragged", "BTE_F32", "BTE_BF16", "contract"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbte.so")
 BTE_F32, BTE_BF16 = 0, 1
@@ -57,7 +58,11 @@ _SIG = {
                                   _i, _i, _i, _f, _i, _p], _i),
     "bte_kv_scatter_attention_paged": ([_p, _p, _p, _p, _i, _p, _p, _p, _p, _p, _p, _i, _i, _p, _p,
                                         _p, _i, _i, _i, _i, _i, _f, _i, _p], _i),
+    "bte_esdllm_score_update": ([_p, _p, _p, _p, _p, _p, _f, _p, _i, _i, _i, _i, _i, _p], _i),
+    "bte_esdllm_schedule": ([_p, _p, _i, _i, _p, _i, _p, _p, _p, _p, _p, _i, _p], _i),
+    "bte_gather_rows_multi_ragged": ([_p, _i, _p, _p, _p, _p, _i, _i, _p], _i),
 }
+ES_MAX_SKIP_LAYERS = 8
 for _name, (_args, _res) in _SIG.items():
     _fn = getattr(lib, _name)
     _fn.argtypes = _args
@@ -566,4 +571,115 @@ def gather_rows_multi(srcs, idx, count, cu, outs=None):
     _check("bte_gather_rows_multi", lib.bte_gather_rows_multi(
         ctypes.cast(arr, ctypes.c_void_p), len(descs), _ptr(idx), _ptr(count), _ptr(cu), batch, n,
         k_max, _stream()))
+    return outs
+
+
+def esdllm_score_update(h_new, h_cache, surv_pos, conf, alpha: float, count=None, cu=None,
+                        cap: int | None = None, out=None):
+    """Score the survivors against h_cache [batch, L, h] and write their new states into it.
+
+    Without count/cu: h_new [batch, cap, h] and surv_pos int32 [batch, cap] (every slot a
+    survivor). With count (int32 [batch]) and cu (int32 [batch + 1]): h_new [rows, h] and
+    surv_pos int32 [rows], sequence b's survivors at rows cu[b] .. cu[b] + count[b] - 1, and
+    `cap` slots per sequence in the output. -> score f32 [batch, cap] (-inf past count)."""
+    _dev(h_new, h_cache, surv_pos, conf, count, cu, out)
+    _need(h_cache.dim() == 3, "h_cache must be [batch, seq_len, hidden]")
+    batch, seq_len, hidden = h_cache.shape
+    _need(h_new.dtype == h_cache.dtype, "h_new and h_cache must share a dtype")
+    _need(h_new.data_ptr() != h_cache.data_ptr(), "h_new must not be h_cache")
+    _want(conf, torch.float32, "conf")
+    _shape(conf, (batch, seq_len), "conf")
+    _need((count is None) == (cu is None), "give count and cu together")
+    if count is None:
+        _need(h_new.dim() == 3 and tuple(h_new.shape[::2]) == (batch, hidden),
+              "h_new must be [batch, cap, hidden]")
+        cap = h_new.shape[1]
+        _i32(surv_pos, "surv_pos", (batch, cap))
+    else:
+        _need(cap is not None and cap > 0, "give cap (survivor slots per sequence) with count")
+        _i32(count, "count", (batch,))
+        _i32(cu, "cu", (batch + 1,))
+        _need(h_new.dim() == 2 and h_new.shape[1] == hidden, "h_new must be [rows, hidden]")
+        _i32(surv_pos, "surv_pos")
+        _need(surv_pos.dim() == 1 and surv_pos.shape[0] == h_new.shape[0],
+              "surv_pos must be [rows] like h_new")
+    if out is None:
+        out = torch.empty((batch, cap), dtype=torch.float32, device=h_new.device)
+    _want(out, torch.float32, "out")
+    _shape(out, (batch, cap), "out")
+    if contract.enabled():
+        contract.check_survivors(surv_pos, seq_len, count, cu, cap, rows=h_new.shape[0])
+    _check("bte_esdllm_score_update", lib.bte_esdllm_score_update(
+        _ptr(h_new), _ptr(h_cache), _ptr(surv_pos), _ptr(count), _ptr(cu), _ptr(conf),
+        float(alpha), _ptr(out), batch, cap, seq_len, hidden, _dtype(h_new), _stream()))
+    return out
+
+
+def esdllm_schedule(iter_, block_start, block_len: int, period: int, keep, surv_pos=None,
+                    count=None, cu=None, keep_out=None, refresh=None):
+    """One iteration's bookkeeping: iter_ int32 [batch] (advanced in place), block_start int32
+    [batch], keep = the skip layers' keep counts (host ints) -> (surv_pos [batch, block_len],
+    count [batch], cu [batch + 1], keep_out [n_layers, batch] int32, refresh uint8 [batch])."""
+    _dev(iter_, block_start, surv_pos, count, cu, keep_out, refresh)
+    _need(iter_.dim() == 1, "iter must be [batch]")
+    batch = iter_.shape[0]
+    _i32(iter_, "iter")
+    _i32(block_start, "block_start", (batch,))
+    keep = [int(v) for v in keep]
+    n_layers = len(keep)
+    _need(n_layers <= ES_MAX_SKIP_LAYERS, f"at most {ES_MAX_SKIP_LAYERS} skip layers")
+    dev, i32 = iter_.device, torch.int32
+    if surv_pos is None:
+        surv_pos = torch.empty((batch, block_len), dtype=i32, device=dev)
+    if count is None:
+        count = torch.empty((batch,), dtype=i32, device=dev)
+    if cu is None:
+        cu = torch.empty((batch + 1,), dtype=i32, device=dev)
+    if keep_out is None:
+        keep_out = torch.empty((max(n_layers, 1), batch), dtype=i32, device=dev)
+    if refresh is None:
+        refresh = torch.empty((batch,), dtype=torch.uint8, device=dev)
+    _i32(surv_pos, "surv_pos", (batch, block_len))
+    _i32(count, "count", (batch,))
+    _i32(cu, "cu", (batch + 1,))
+    _i32(keep_out, "keep_out")
+    _need(keep_out.dim() == 2 and keep_out.shape[1] == batch and keep_out.shape[0] >= n_layers,
+          "keep_out must be [n_layers, batch]")
+    _want(refresh, torch.uint8, "refresh")
+    _shape(refresh, (batch,), "refresh")
+    karr = (ctypes.c_int32 * max(n_layers, 1))(*keep) if n_layers else None
+    _check("bte_esdllm_schedule", lib.bte_esdllm_schedule(
+        _ptr(iter_), _ptr(block_start), int(block_len), int(period),
+        ctypes.cast(karr, ctypes.c_void_p) if karr is not None else None, n_layers, _ptr(surv_pos),
+        _ptr(count), _ptr(cu), _ptr(keep_out), _ptr(refresh), batch, _stream()))
+    return surv_pos, count, cu, keep_out, refresh
+
+
+def gather_rows_multi_ragged(srcs, src_cu, idx, count, cu, outs=None):
+    """Each src [rows, ...], compacted by sequence (sequence b's rows start at src_cu[b]),
+    gathered with one index set in one launch: out[cu[b] + t] = src[src_cu[b] + idx[b, t]].
+    Returns the outputs [batch * k_max, ...]."""
+    _dev(src_cu, idx, count, cu, *srcs)
+    batch, k_max = _kept_lists(idx, count, cu)
+    _i32(src_cu, "src_cu")
+    _need(src_cu.dim() == 1 and src_cu.shape[0] >= batch, "src_cu must be [batch] (or [batch + 1])")
+    _need(len(srcs) >= 1, "give at least one source")
+    if outs is None:
+        outs = [torch.empty((batch * k_max,) + tuple(s.shape[1:]), dtype=s.dtype, device=s.device)
+                for s in srcs]
+    _need(len(outs) == len(srcs), "give one output per source")
+    _dev(*outs)
+    descs = []
+    for i, (s_, o) in enumerate(zip(srcs, outs)):
+        _need(s_.dim() >= 1 and o.dtype == s_.dtype, f"output {i} must have the dtype of its source")
+        rb = _row_bytes(s_)
+        _need(_row_bytes(o) == rb, f"output {i} rows must be the size of its source rows")
+        descs.append(_RowsTensor(s_.data_ptr(), o.data_ptr(), rb))
+    if contract.enabled():
+        contract.check_rows(idx, count, cu, k_max, out_rows=min(o.shape[0] for o in outs))
+        contract.check_ragged_source(src_cu, idx, count, min(s_.shape[0] for s_ in srcs))
+    arr = (_RowsTensor * len(descs))(*descs)
+    _check("bte_gather_rows_multi_ragged", lib.bte_gather_rows_multi_ragged(
+        ctypes.cast(arr, ctypes.c_void_p), len(descs), _ptr(src_cu), _ptr(idx), _ptr(count),
+        _ptr(cu), batch, k_max, _stream()))
     return outs

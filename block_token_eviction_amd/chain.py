@@ -30,8 +30,16 @@ ES-dLLM skip layer (the same page: at a skip layer the survivors are scored,
 the layer's hidden-state cache is updated in place at every survivor, and
 only the top (1 - r)|S| survivors go on to the next layer):
 
-    esdllm_score -> kv_scatter (hidden cache, all survivors) -> topk_select
+    esdllm_score_update (score + hidden-cache update in one pass) -> topk_select
         -> gather_rows_multi (kept hidden rows + their positions)
+
+ES-dLLM iteration (the same page, key design 2: the initial full pass and a
+periodic refresh run without skipping; every iteration starts from the whole
+block). Per-sequence counters make survivor sets ragged within a batch, so the
+survivors of each layer are compacted by sequence (count, cu):
+
+    esdllm_schedule -> [esdllm_score_update -> topk_select
+        -> gather_rows_multi_ragged] per skip layer
 
 Every call enqueues HIP kernels on the current stream; nothing here reads
 device data back or synchronises. Per-sequence counts stay on the device, so
@@ -43,10 +51,11 @@ import math
 
 import torch
 
-from . import (attention_order, esdllm_score, focus_budget, focus_commit_mask,
-               focus_history_update, focus_importance_delta, focus_select, gather_rows,
-               gather_rows_multi, kv_scatter, kv_scatter_attention, kv_scatter_attention_paged,
-               kv_scatter_paged, reduced_attention, reduced_attention_paged, topk_select)
+from . import (attention_order, esdllm_schedule, esdllm_score, esdllm_score_update, focus_budget,
+               focus_commit_mask, focus_history_update, focus_importance_delta, focus_select,
+               gather_rows, gather_rows_multi, gather_rows_multi_ragged, kv_scatter,
+               kv_scatter_attention, kv_scatter_attention_paged, kv_scatter_paged,
+               reduced_attention, reduced_attention_paged, topk_select)
 
 
 class FocusStep:
@@ -238,19 +247,67 @@ class EsSkipLayer:
         self.cu = torch.empty((batch + 1,), **i32)
         self.h_next = torch.empty((batch * keep, hidden), dtype=dtype, device=device)
         self.surv_next = torch.empty((batch * keep,), **i32)
-        # every survivor, for the hidden-cache update
-        self.all_idx = torch.arange(n_surv, **i32).repeat(batch, 1).contiguous()
-        self.all_count = torch.full((batch,), n_surv, **i32)
-        self.all_cu = torch.arange(batch + 1, **i32) * n_surv
-        self.row_base = torch.arange(batch, dtype=torch.int64, device=device) * seq_len
 
     def run(self, h_surv, h_cache, surv_pos, conf, alpha: float):
         """h_surv [batch, n_surv, hidden] this iteration's states of the survivors."""
-        b, n = self.batch, self.n_surv
-        esdllm_score(h_surv, h_cache, surv_pos, conf, alpha, out=self.score)
-        kv_scatter(h_surv.view(b * n, -1), None, self.all_idx, self.all_count, self.all_cu,
-                   self.row_base, h_cache.view(b * self.seq_len, -1), None, pos_map=surv_pos)
+        b = self.batch
+        esdllm_score_update(h_surv, h_cache, surv_pos, conf, alpha, out=self.score)
         topk_select(self.score, self.k, self.keep, self.idx, self.count, self.cu)
         gather_rows_multi([h_surv, surv_pos], self.idx, self.count, self.cu,
                           outs=[self.h_next, self.surv_next])
         return self.h_next.view(b, self.keep, -1), self.surv_next.view(b, self.keep)
+
+
+class EsIteration:
+    """One iteration of ES-dLLM's skip pipeline with its device-side bookkeeping,
+    on preallocated buffers. The caller owns the per-sequence iteration counters
+    (`iter`, int32 [batch], advanced in place) and the block starts; each skip
+    layer l has its hidden-state cache h_caches[l] [batch, seq_len, hidden],
+    updated in place. keep: the skip iterations' keep counts per skip layer
+    (floor((1 - r_l)|S_l|)); refresh iterations keep every survivor."""
+
+    def __init__(self, batch: int, block_len: int, hidden: int, keep, period: int,
+                 dtype: torch.dtype, device):
+        self.batch, self.block_len, self.keep, self.period = batch, block_len, list(keep), period
+        i32 = dict(dtype=torch.int32, device=device)
+        n_l = len(self.keep)
+        cap = batch * block_len
+        self.surv0 = torch.empty((batch, block_len), **i32)
+        self.count0 = torch.empty((batch,), **i32)
+        self.cu0 = torch.empty((batch + 1,), **i32)
+        self.keep_out = torch.empty((max(n_l, 1), batch), **i32)
+        self.refresh = torch.empty((batch,), dtype=torch.uint8, device=device)
+        self.score = [torch.empty((batch, block_len), dtype=torch.float32, device=device)
+                      for _ in range(n_l)]
+        self.idx = [torch.empty((batch, block_len), **i32) for _ in range(n_l)]
+        self.count = [torch.empty((batch,), **i32) for _ in range(n_l)]
+        self.cu = [torch.empty((batch + 1,), **i32) for _ in range(n_l)]
+        self.h_next = [torch.empty((cap, hidden), dtype=dtype, device=device) for _ in range(n_l)]
+        self.surv_next = [torch.empty((cap,), **i32) for _ in range(n_l)]
+
+    def schedule(self, iter_, block_start):
+        return esdllm_schedule(iter_, block_start, self.block_len, self.period, self.keep,
+                               self.surv0, self.count0, self.cu0, self.keep_out, self.refresh)
+
+    def layer(self, l: int, h_rows, surv_rows, count, cu, h_cache, conf, alpha: float):
+        """Skip layer l on survivors compacted by (count, cu): h_rows [rows, hidden] their
+        states, surv_rows int32 [rows] their positions. Returns the kept survivors
+        (h_next, surv_next, count, cu), compacted the same way."""
+        esdllm_score_update(h_rows, h_cache, surv_rows, conf, alpha, count=count, cu=cu,
+                            cap=self.block_len, out=self.score[l])
+        topk_select(self.score[l], self.keep_out[l], self.block_len, self.idx[l], self.count[l],
+                    self.cu[l])
+        gather_rows_multi_ragged([h_rows, surv_rows], cu, self.idx[l], self.count[l], self.cu[l],
+                                 outs=[self.h_next[l], self.surv_next[l]])
+        return self.h_next[l], self.surv_next[l], self.count[l], self.cu[l]
+
+    def run(self, iter_, block_start, layer_states, h_caches, conf, alpha: float):
+        """layer_states(l, surv_rows, count, cu) -> h_rows: the model's output of the layer
+        before skip layer l for the survivors (outside this library)."""
+        surv, count, cu, _, _ = self.schedule(iter_, block_start)
+        rows = surv.view(-1)
+        h = None
+        for l in range(len(self.keep)):
+            h_rows = layer_states(l, rows, count, cu)
+            h, rows, count, cu = self.layer(l, h_rows, rows, count, cu, h_caches[l], conf, alpha)
+        return h, rows, count, cu

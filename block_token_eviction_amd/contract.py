@@ -204,3 +204,39 @@ def check_fused_scatter(idx, count, cu, k_max: int, n: int, pos_base, kv_len, ne
         if (hit != b).any():
             _fail(f"sequence {int(b)} reads a cache row that sequence "
                   f"{int(hit[hit != b][0])} writes in the same launch")
+
+
+def check_survivors(surv_pos, seq_len: int, count=None, cu=None, cap: int | None = None,
+                    rows: int | None = None):
+    """Skip-layer survivors: per sequence, positions in [0, seq_len) and
+    distinct (each survivor's new state is written to its own cache row).
+    With count/cu: 0 <= count[b] <= cap, cu the exclusive prefix sum of
+    count, and the compacted rows cu[-1] within `rows`."""
+    sp = _np(surv_pos)
+    if count is None:
+        lists = [sp[b] for b in range(sp.shape[0])]
+    else:
+        cnt, c = _np(count).astype(np.int64), _np(cu).astype(np.int64)
+        if c.shape[0] != cnt.shape[0] + 1 or c[0] != 0 or not np.array_equal(np.diff(c), cnt):
+            _fail("cu is not the exclusive prefix sum of count")
+        if cap is not None and ((cnt < 0) | (cnt > cap)).any():
+            _fail(f"a survivor count is outside [0, cap = {cap}]")
+        if rows is not None and int(c[-1]) > rows:
+            _fail(f"{int(c[-1])} survivor rows exceed the input's {rows}")
+        lists = [sp[int(c[b]):int(c[b]) + int(cnt[b])] for b in range(cnt.shape[0])]
+    for b, p in enumerate(lists):
+        p = np.asarray(p, np.int64)
+        if p.size and (p.min() < 0 or p.max() >= seq_len):
+            _fail(f"survivor positions of sequence {b} leave [0, {seq_len})")
+        if np.unique(p).size != p.size:
+            _fail(f"survivor positions of sequence {b} repeat")
+
+
+def check_ragged_source(src_cu, idx, count, src_rows: int):
+    """Gather from compacted sources: every src_cu[b] + idx[b, t], t < count[b],
+    inside [0, src_rows)."""
+    sc, cnt = _np(src_cu).astype(np.int64), _np(count).astype(np.int64)
+    pos = _positions(idx, count, None)
+    for b, p in enumerate(pos):
+        if p.size and (sc[b] + p.min() < 0 or sc[b] + p.max() >= src_rows):
+            _fail(f"sequence {b} gathers a source row outside [0, {src_rows})")

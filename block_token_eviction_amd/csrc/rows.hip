@@ -114,12 +114,15 @@ struct MultiRows {
   int n_tensors;
 };
 
+// Source row of kept slot t: b * n + idx, or src_cu[b] + idx when the source
+// rows are themselves compacted by sequence.
 __global__ __launch_bounds__(kThreads) void gather_multi_kernel(
     MultiRows m, const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
-    const int32_t* __restrict__ cu, int batch, int n, int k_max) {
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ src_cu, int batch, int n,
+    int k_max) {
   int b, t;
   if (!xcd_seq_part(batch, k_max, b, t) || t >= count[b]) return;
-  const size_t src_row = (size_t)b * n + idx[(size_t)b * k_max + t];
+  const size_t src_row = (src_cu ? (size_t)src_cu[b] : (size_t)b * n) + idx[(size_t)b * k_max + t];
   const size_t dst_row = (size_t)cu[b] + t;
   for (int k = 0; k < m.n_tensors; ++k) {
     const size_t rb = m.row_bytes[k];
@@ -284,9 +287,9 @@ extern "C" int bte_kv_scatter_paged(const void* new_k, const void* new_v, const 
                               cache_v, batch, k_max, row_bytes, stream);
 }
 
-extern "C" int bte_gather_rows_multi(const bte_rows_tensor* tensors, int n_tensors,
-                                     const int32_t* idx, const int32_t* count, const int32_t* cu,
-                                     int batch, int n, int k_max, hipStream_t stream) {
+static int gather_multi(const bte_rows_tensor* tensors, int n_tensors, const int32_t* src_cu,
+                        const int32_t* idx, const int32_t* count, const int32_t* cu, int batch,
+                        int n, int k_max, hipStream_t stream) {
   using namespace bte;
   if (!tensors || !idx || !count || !cu) return BTE_ERR_NULL;
   if (n_tensors < 1 || n_tensors > kMaxTensors || batch <= 0 || n <= 0 || k_max < 0)
@@ -308,6 +311,20 @@ extern "C" int bte_gather_rows_multi(const bte_rows_tensor* tensors, int n_tenso
   const size_t grid = (size_t)(batch + kXcds - 1) / kXcds * kXcds * (size_t)k_max;
   if (grid > 0x7fffffffu) return BTE_ERR_DIM;
   hipLaunchKernelGGL(gather_multi_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, m, idx,
-                     count, cu, batch, n, k_max);
+                     count, cu, src_cu, batch, n, k_max);
   return hipGetLastError() == hipSuccess ? BTE_OK : BTE_ERR_LAUNCH;
+}
+
+extern "C" int bte_gather_rows_multi(const bte_rows_tensor* tensors, int n_tensors,
+                                     const int32_t* idx, const int32_t* count, const int32_t* cu,
+                                     int batch, int n, int k_max, hipStream_t stream) {
+  return gather_multi(tensors, n_tensors, nullptr, idx, count, cu, batch, n, k_max, stream);
+}
+
+extern "C" int bte_gather_rows_multi_ragged(const bte_rows_tensor* tensors, int n_tensors,
+                                            const int32_t* src_cu, const int32_t* idx,
+                                            const int32_t* count, const int32_t* cu, int batch,
+                                            int k_max, hipStream_t stream) {
+  if (!src_cu) return BTE_ERR_NULL;
+  return gather_multi(tensors, n_tensors, src_cu, idx, count, cu, batch, 1, k_max, stream);
 }

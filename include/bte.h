@@ -98,6 +98,67 @@ int bte_esdllm_score(const void* h_new, const void* h_prev, const int32_t* surv_
                      int seq_len, int hidden, bte_dtype dtype, hipStream_t stream);
 
 /*
+ * ES-dLLM skip-layer score with the in-place hidden-cache update (ES-dLLM
+ * notes page, key designs 1 and 2: every survivor of a skip layer is scored
+ * against the layer's cached state of the previous iteration, and its new
+ * state then replaces the cached one; positions that were skipped keep
+ * theirs). For sequence b and survivor slot s < cap:
+ *   s < n_b (n_b = count[b], or cap without count):
+ *     r = cu ? cu[b] + s : b * cap + s;  p = surv_pos[r]
+ *     score_out[b,s] = alpha * conf[b,p] + (1 - alpha) * |x - y|_1 / (sqrt(hidden) * |y|_2)
+ *     with x = h_new[r,:] and y = h_cache[b,p,:] as it was before this call;
+ *     then h_cache[b,p,:] = x.
+ *   s >= n_b: score_out[b,s] = -INFINITY (ineligible for the top-K); nothing written.
+ * The score arithmetic is bte_esdllm_score's: the same inputs give the same bits.
+ *
+ *   h_new [rows, hidden] dtype (rows as above); h_cache [batch, seq_len, hidden]
+ *   dtype, updated in place; surv_pos [rows] int32 in [0, seq_len), distinct
+ *   within a sequence; count [batch] (<= cap) and cu [batch] int32, both or
+ *   neither; conf [batch, seq_len] float32; score_out [batch, cap] float32.
+ * Limits: hidden * sizeof(dtype) a multiple of 16; h_new and h_cache 16-byte
+ * aligned and not overlapping.
+ * Errors: NULL (or only one of count/cu) -> BTE_ERR_NULL; sizes <= 0 ->
+ * BTE_ERR_DIM; dtype or hidden unsupported -> BTE_ERR_UNSUPPORTED; alignment
+ * -> BTE_ERR_ALIGN.
+ */
+int bte_esdllm_score_update(const void* h_new, void* h_cache, const int32_t* surv_pos,
+                            const int32_t* count, const int32_t* cu, const float* conf,
+                            float alpha, float* score_out, int batch, int cap, int seq_len,
+                            int hidden, bte_dtype dtype, hipStream_t stream);
+
+/* Most skip layers bte_esdllm_schedule plans for. */
+#define BTE_ES_MAX_SKIP_LAYERS 8
+
+/*
+ * ES-dLLM iteration bookkeeping (ES-dLLM notes page, key design 2: a full
+ * forward at the start initialises the caches, and a full refresh without
+ * skipping at a fixed period keeps skip errors from accumulating). Per
+ * sequence b, with it = iter[b] (the iterations the sequence has run):
+ *   refresh = (it == 0) || (period > 0 && it % period == 0)
+ *   surv_pos_out[b, j] = block_start[b] + j for j < block_len  (every
+ *     iteration starts from the whole current block); count_out[b] = block_len;
+ *   cu_out[b] = b * block_len, cu_out[batch] = batch * block_len
+ *   keep_out[l, b] = refresh ? block_len : keep[l]   for skip layer l < n_layers
+ *   refresh_out[b] = refresh; iter[b] = it + 1
+ * keep[] holds the skip iterations' keep counts floor((1 - r_l) |S_l|) of
+ * the skip layers in order (the pages: r = 0.5 at two layers, so 128 and 64
+ * of a 256-position block).
+ *
+ *   iter [batch] int32 >= 0, updated in place; block_start [batch] int32;
+ *   keep: HOST array [n_layers] int32; surv_pos_out [batch, block_len],
+ *   count_out [batch], cu_out [batch + 1], keep_out [n_layers, batch] int32;
+ *   refresh_out [batch] uint8.
+ * Limits: 0 <= n_layers <= BTE_ES_MAX_SKIP_LAYERS; period >= 0 (0: only the
+ * initial pass runs without skipping); 0 <= keep[l] <= keep[l-1] <= block_len;
+ * batch * block_len < 2^31.
+ * Errors: NULL -> BTE_ERR_NULL; sizes or keep counts out of range -> BTE_ERR_DIM.
+ */
+int bte_esdllm_schedule(int32_t* iter, const int32_t* block_start, int block_len, int period,
+                        const int32_t* keep, int n_layers, int32_t* surv_pos_out,
+                        int32_t* count_out, int32_t* cu_out, int32_t* keep_out,
+                        uint8_t* refresh_out, int batch, hipStream_t stream);
+
+/*
  * Per-sequence top-K (FOCUS paper Section 4.2: top-K masked tokens by delta;
  * ES-dLLM notes page, key design 1: keep the top-(1-r)|S| survivors) and the
  * prefix sum that places each sequence's kept rows (FOCUS paper App. E.2.3).
@@ -244,6 +305,21 @@ typedef struct {
 int bte_gather_rows_multi(const bte_rows_tensor* tensors, int n_tensors, const int32_t* idx,
                           const int32_t* count, const int32_t* cu, int batch, int n, int k_max,
                           hipStream_t stream);
+
+/*
+ * The same compaction from sources that are themselves compacted by sequence
+ * (ES-dLLM notes page, key design 2: a skip layer's output exists only for
+ * its survivors, and the next layer takes the kept ones). For t < count[b]:
+ *   tensors[k].dst[cu[b] + t, :] = tensors[k].src[src_cu[b] + idx[b,t], :]
+ *
+ *   src [>= max_b(src_cu[b] + idx[b, count[b]-1]) + 1, row_bytes];
+ *   src_cu [batch] int32 (first source row of each sequence; e.g. the previous
+ *   selection's cu); other arguments and limits as bte_gather_rows_multi.
+ * Errors: as bte_gather_rows_multi; src_cu NULL -> BTE_ERR_NULL.
+ */
+int bte_gather_rows_multi_ragged(const bte_rows_tensor* tensors, int n_tensors,
+                                 const int32_t* src_cu, const int32_t* idx, const int32_t* count,
+                                 const int32_t* cu, int batch, int k_max, hipStream_t stream);
 
 /*
  * In-place scatter of the kept rows' new K/V into the exact KV cache

@@ -9,7 +9,10 @@ operations of the path, written from the pages' definitions:
 * ``esdllm_score`` — ES-dLLM importance score (ES-dLLM notes page, key
   design 1); ``esdllm_skip_layer`` — one skip layer of its early skipping
   (score, partial hidden-cache update, top-(1-r)|S|, survivor compaction;
-  key designs 1 and 2).
+  key designs 1 and 2), ``esdllm_skip_layer_ragged`` the same on survivor
+  sets of per-sequence size; ``esdllm_schedule`` — the per-sequence iteration
+  bookkeeping (initial full pass, periodic refresh without skipping, survivor
+  reset; key design 2); ``esdllm_iteration`` — both composed.
 * ``topk_select`` — per-sequence top-K of masked tokens (FOCUS paper
   Section 4.2; ES-dLLM notes page, key design 1 "top-(1-r_l)|S|").
 * ``gather_rows`` — Gather of the kept block hidden rows into H_reduced
@@ -28,7 +31,8 @@ operations of the path, written from the pages' definitions:
 * ``commit_mask`` — the neighbour-aware delayed commit of block KV states
   (FOCUS paper Section 4.3, App. E.3.1, App. E.3.3).
 * ``gather_rows_multi`` — several row tensors compacted with one index set
-  (FOCUS paper App. E.2.3).
+  (FOCUS paper App. E.2.3); ``gather_rows_ragged`` — a gather from sources
+  compacted by sequence.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package. The product path
@@ -40,10 +44,11 @@ closed forms, hand-worked examples, library routines and invariants.
 """
 from .focus import (block_scores, maxpool_keys, softmax_keys, importance,
                     focus_importance_delta)
-from .esdllm import esdllm_score, esdllm_skip_layer
+from .esdllm import (esdllm_score, esdllm_skip_layer, esdllm_schedule, esdllm_skip_layer_ragged,
+                     esdllm_iteration)
 from .selection import topk_select, focus_select
 from .budget import focus_budget, history_update
-from .rows import gather_rows, gather_rows_multi, kv_scatter
+from .rows import gather_rows, gather_rows_multi, gather_rows_ragged, kv_scatter
 from .cache_state import commit_mask
 from .attention import reduced_attention
 from .paged import kv_scatter_paged, reduced_attention_paged, physical_row
@@ -52,4 +57,5 @@ __all__ = ["block_scores", "maxpool_keys", "softmax_keys", "importance",
            "focus_importance_delta", "esdllm_score", "topk_select", "gather_rows",
            "kv_scatter", "reduced_attention", "focus_budget",
            "history_update", "focus_select", "kv_scatter_paged", "reduced_attention_paged",
-           "physical_row", "commit_mask", "gather_rows_multi", "esdllm_skip_layer"]
+           "physical_row", "commit_mask", "gather_rows_multi", "esdllm_skip_layer",
+           "esdllm_schedule", "esdllm_skip_layer_ragged", "esdllm_iteration", "gather_rows_ragged"]

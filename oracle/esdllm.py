@@ -81,3 +81,86 @@ def esdllm_skip_layer(h_surv, h_cache, surv_pos, conf, alpha: float, keep: int, 
     h_next = gather_rows(h_surv, idx, count, cu)
     surv_next = gather_rows(surv_pos[:, :, None], idx, count, cu)[:, 0]
     return score, idx, count, cu, h_next, surv_next, new_cache.reshape(h_cache.shape)
+
+
+def esdllm_schedule(iter_, block_start, block_len: int, period: int, keep):
+    """Iteration bookkeeping of ES-dLLM's skipping (ES-dLLM notes page, key
+    design 2): generation starts with one full forward that initialises the
+    caches, and after it a full refresh without skipping runs at a fixed
+    period, so that skip errors do not pile up over the iterations.
+
+    Reading taken: a sequence's iteration counter counts the iterations it
+    has run; iteration 0 is the initial full pass, and with period > 0 every
+    iteration whose count is a multiple of the period is a refresh (period 0:
+    only the initial pass). A refresh skips nothing, so every skip layer keeps
+    all of its survivors (keep = |S| = the block length); other iterations
+    keep the given counts floor((1 - r_l) |S_l|). Every iteration starts from
+    the whole current block: the first skip layer's survivors are positions
+    block_start .. block_start + block_len - 1.
+
+    Returns dict(surv_pos [batch, block_len], count [batch], cu [batch + 1],
+    keep [n_layers, batch], refresh [batch] bool, iter [batch] advanced).
+    """
+    iter_ = np.asarray(iter_, dtype=np.int64)
+    block_start = np.asarray(block_start, dtype=np.int64)
+    batch = iter_.shape[0]
+    refresh = np.array([it == 0 or (period > 0 and it % period == 0) for it in iter_], dtype=bool)
+    surv = block_start[:, None] + np.arange(block_len)[None, :]
+    keep_out = np.array([[block_len if refresh[b] else int(kl) for b in range(batch)]
+                         for kl in keep], dtype=np.int64).reshape(len(keep), batch)
+    return dict(surv_pos=surv, count=np.full(batch, block_len), cu=np.arange(batch + 1) * block_len,
+                keep=keep_out, refresh=refresh, iter=iter_ + 1)
+
+
+def esdllm_skip_layer_ragged(h_rows, h_cache, surv_rows, count, cu, conf, alpha: float, k,
+                             cap: int):
+    """One skip layer on survivor sets of different sizes per sequence (a
+    sequence refreshing this iteration keeps every survivor while another
+    skips half): the same steps as ``esdllm_skip_layer``.
+
+    h_rows [rows, h]: the survivors' states of this iteration, sequence b's at
+    rows cu[b] .. cu[b] + count[b] - 1; surv_rows [rows] their positions;
+    h_cache [batch, L, h]; k [batch] the keep counts; cap: survivor slots per
+    sequence. Returns (score [batch, cap] with -inf past count, idx, count',
+    cu', h_next [sum(count'), h], surv_next [sum(count')], h_cache updated copy).
+    """
+    from .selection import topk_select
+    from .rows import gather_rows_ragged
+
+    h_rows = np.asarray(h_rows)
+    h_cache = np.asarray(h_cache)
+    surv_rows = np.asarray(surv_rows)
+    batch = len(count)
+    score = np.full((batch, cap), -np.inf)
+    new_cache = h_cache.copy()
+    for b in range(batch):
+        lo, n = int(cu[b]), int(count[b])
+        if n == 0:
+            continue
+        score[b, :n] = esdllm_score(h_rows[lo:lo + n][None], h_cache[b][None],
+                                    surv_rows[lo:lo + n][None], np.asarray(conf)[b][None], alpha)[0]
+        for s in range(n):
+            new_cache[b, int(surv_rows[lo + s])] = h_rows[lo + s]
+    idx, count2, cu2 = topk_select(score, np.asarray(k), cap)
+    h_next = gather_rows_ragged(h_rows, cu, idx, count2, cu2)
+    surv_next = gather_rows_ragged(surv_rows[:, None], cu, idx, count2, cu2)[:, 0]
+    return score, idx, count2, cu2, h_next, surv_next, new_cache
+
+
+def esdllm_iteration(iter_, block_start, block_len: int, period: int, keep, layer_states,
+                     h_caches, conf, alpha: float):
+    """One iteration of the skip pipeline: the bookkeeping, then each skip
+    layer in turn on the survivors the previous one kept. layer_states(l,
+    surv_rows, count, cu) stands for the model's layer output for the
+    survivors (compacted rows). Returns (schedule dict, per-layer results of
+    ``esdllm_skip_layer_ragged``)."""
+    sch = esdllm_schedule(iter_, block_start, block_len, period, keep)
+    rows, cnt, cu = sch["surv_pos"].reshape(-1), sch["count"], sch["cu"]
+    out = []
+    for l in range(len(keep)):
+        h = layer_states(l, rows, cnt, cu)
+        res = esdllm_skip_layer_ragged(h, h_caches[l], rows, cnt, cu, conf, alpha, sch["keep"][l],
+                                       block_len)
+        out.append(res)
+        rows, cnt, cu = res[5], res[2], res[3]
+    return sch, out

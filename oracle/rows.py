@@ -37,6 +37,21 @@ def gather_rows(src: np.ndarray, idx, count, cu) -> np.ndarray:
     return d.view(src.dtype).reshape((total,) + src.shape[2:])
 
 
+def gather_rows_ragged(src: np.ndarray, src_cu, idx, count, cu) -> np.ndarray:
+    """Gather from rows that are themselves compacted by sequence (a skip
+    layer's output exists only for its survivors, ES-dLLM notes page, key
+    design 2): dst[cu[b] + t] = src[src_cu[b] + idx[b, t]] for t < count[b]."""
+    rows = src.shape[0]
+    s = _bytes(src, rows)
+    batch = len(count)
+    total = int(cu[batch])
+    d = np.zeros((total, s.shape[1]), dtype=np.uint8)
+    for b in range(batch):
+        for t in range(int(count[b])):
+            d[int(cu[b]) + t] = s[int(src_cu[b]) + int(idx[b, t])]
+    return d.view(src.dtype).reshape((total,) + src.shape[1:])
+
+
 def gather_rows_multi(srcs, idx, count, cu):
     """Each src [batch, n, ...] gathered with the same index set (FOCUS paper
     App. E.2.3: hidden states, residual, RoPE positions and cache indices are

@@ -25,7 +25,7 @@ def declared():
 
 def test_every_declared_symbol_is_exported():
     names = declared()
-    assert len(names) == 18
+    assert len(names) == 21
     for name in names:
         assert hasattr(lib, name), name
 
@@ -232,3 +232,46 @@ def test_commit_and_multi_errors():
     nul = (T * 1)(T(None, 1 << 21, 8))
     assert g(ctypes.cast(nul, ctypes.c_void_p), 1, FAKE, FAKE, FAKE, 4, 32, 8, None) == NULL
     assert g(ctypes.cast(ok, ctypes.c_void_p), 2, FAKE, FAKE, FAKE, 4, 32, 0, None) == OK
+
+
+def test_esdllm_score_update_errors():
+    f = lib.bte_esdllm_score_update
+    a = [FAKE, FAKE, FAKE, None, None, FAKE, ctypes.c_float(0.5), FAKE, 1, 4, 8, 4096, 1, None]
+    call = lambda **kw: f(*[kw.get(f"a{i}", v) for i, v in enumerate(a)])
+    assert call(a0=None) == NULL
+    assert call(a1=None) == NULL
+    assert call(a3=FAKE) == NULL              # count without cu
+    assert call(a4=FAKE) == NULL              # cu without count
+    assert call(a8=0) == DIM
+    assert call(a9=0) == DIM
+    assert call(a11=4100) == UNSUP
+    assert call(a12=7) == UNSUP
+    assert call(a1=MIS) == ALIGN
+
+
+def test_esdllm_schedule_errors():
+    f = lib.bte_esdllm_schedule
+    keep = (ctypes.c_int32 * 3)(128, 64, 80)
+    kp = ctypes.cast(keep, ctypes.c_void_p)
+    a = [FAKE, FAKE, 256, 3, kp, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None]
+    call = lambda **kw: f(*[kw.get(f"a{i}", v) for i, v in enumerate(a)])
+    assert call(a0=None) == NULL
+    assert call(a4=None) == NULL              # keep counts needed with n_layers > 0
+    assert call(a9=None) == NULL
+    assert call(a11=0) == DIM
+    assert call(a2=0) == DIM
+    assert call(a3=-1) == DIM
+    assert call(a5=9) == DIM                  # more than BTE_ES_MAX_SKIP_LAYERS
+    assert call(a5=3) == DIM                  # keep[2] = 80 > keep[1] = 64
+    big = (ctypes.c_int32 * 1)(300)
+    assert call(a4=ctypes.cast(big, ctypes.c_void_p), a5=1) == DIM   # keep > block_len
+    assert call(a2=1 << 20, a11=1 << 12) == DIM                      # batch * block >= 2^31
+
+
+def test_gather_rows_multi_ragged_errors():
+    f = lib.bte_gather_rows_multi_ragged
+    ok = (bte._RowsTensor * 1)(bte._RowsTensor(1 << 20, 1 << 21, 8192))
+    arr = ctypes.cast(ok, ctypes.c_void_p)
+    assert f(arr, 1, None, FAKE, FAKE, FAKE, 4, 8, None) == NULL
+    assert f(arr, 0, FAKE, FAKE, FAKE, FAKE, 4, 8, None) == DIM
+    assert f(arr, 1, FAKE, FAKE, FAKE, FAKE, 0, 8, None) == DIM
