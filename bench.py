@@ -13,16 +13,23 @@ launched call by call, is reported beside it), per-kernel average durations
 from HIP events recorded on the launch stream in the eager loop, the
 roofline of the dominant kernel (reduced attention, HBM-bound) from its
 algorithmic bytes, and the CPU oracle timed on a bounded sample of the same
-workload. The ES-dLLM mode (score -> top-K -> gather -> scatter, batch 8) is
-timed as well and reported under "es_mode", two ES-dLLM skip layers
-(256 -> 128 -> 64 survivors) under "es_pipeline", the KV scatter fused into
-the attention (one launch) against the two launches of the main step under
-"fused_scatter_attention", and the extended FOCUS step
-(device budget, constrained selection, one compaction launch for four
-per-token tensors, paged KV pool, delayed commit mask, history update) on the
-same batch-1024 workload under "full_step".
+workload.
+
+Other legs, each reported under its own key:
+  focus_b256           FOCUS scoring at batch 256 (delta -> top-K -> gather),
+  attn_b256            KV scatter -> order -> attention at batch 256,
+  focus_b1024_block64  the scoring path with blocks of 64 positions,
+  es_mode              ES-dLLM score -> top-K -> gather -> KV scatter, batch 8,
+  es_pipeline          two ES-dLLM skip layers (256 -> 128 -> 64 survivors),
+  es_iteration         ES-dLLM iterations with the device bookkeeping and a
+                       refresh every third iteration,
+  fused_scatter_attention, full_step, score_resident (see their functions).
+The batch-256, block-64 and ES legs write a 1 GiB buffer before every timed
+iteration (outside the events), so their inputs come from HBM and not from the
+256 MB Infinity Cache, and time each kernel with HIP events (medians).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--legs all|main|name,name,...]
 """
 from __future__ import annotations
 
@@ -30,6 +37,7 @@ import argparse
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -40,7 +48,11 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 ALPHA = 1.5                    # FOCUS budget multiplier of the pages' worked example
 PAGE = 64                      # KV pool page size (rows) of the extended step
+FLUSH_BYTES = 1 << 30          # written before each timed iteration of the flushed legs
+LEG_ITERS = 30                 # timed iterations of each flushed leg
 METRIC = "block tokens/s through score→top-K→gather→reduced attn; % of HBM/MFMA roofline"
+LEGS = ["focus_b256", "attn_b256", "focus_b1024_block64", "es_mode", "es_pipeline",
+        "es_iteration", "fused_scatter_attention", "full_step", "score_resident"]
 
 
 def log(msg):
@@ -55,17 +67,24 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 256 MiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--legs", default="all",
+                    help="'all', 'main' (the main step only) or a comma list of leg names")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path shards by sequence with no exchange, "
               "so run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    legs = LEGS if args.legs == "all" else ([] if args.legs == "main" else args.legs.split(","))
+    unknown = [l for l in legs if l not in LEGS]
+    if unknown:
+        print(f"unknown legs {unknown}; known: {LEGS}", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
     import torch
 
     import block_token_eviction_amd as bte
-    from block_token_eviction_amd.chain import EsSkipLayer, EsStep, FocusStep
+    from block_token_eviction_amd.chain import FocusStep
     import workloads as W
 
     dev = torch.device("cuda:0")
@@ -116,16 +135,14 @@ def main():
     es = 2
     B, hq, hkv, D, H = fc.block, fc.hq, fc.hkv, fc.head_dim, fc.hidden
     bytes_ = {
-        "focus_importance_delta": 2 * fc.batch * B * (hq + hkv) * D * es + fc.batch * B * (1 + 4),
+        "focus_importance_delta": delta_bytes(fc.batch, B, hq, hkv, D, es),
         "topk_select": fc.batch * B * 4 + fc.batch * 4 + fc.batch * (fc.k_hi + 2) * 4,
         "gather_rows": 2 * sum_k * H * es,
         "kv_scatter": 2 * 2 * sum_k * hkv * D * es,
         "attention_order": 2 * fc.batch * 4,
-        "reduced_attention": int(kv_len.sum()) * hkv * D * es * 2 + 2 * sum_k * hq * D * es,
+        "reduced_attention": attention_bytes(kv_len, sum_k, hq, hkv, D, es),
     }
-    flops_attn = 0
-    for b in range(fc.batch):
-        flops_attn += 4 * int(count[b]) * hq * int(kv_len[b]) * D
+    flops_attn = attention_flops(count, kv_len, hq, D)
     kernels = {n: {"ms": round(stage_ms[n], 4), "algo_bytes": int(bytes_[n]),
                    "GB/s": round(bytes_[n] / (stage_ms[n] * 1e-3) / 1e9, 1),
                    "hbm_frac": round(bytes_[n] / (stage_ms[n] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -140,8 +157,9 @@ def main():
     achieved = bytes_[dom] / (stage_ms[dom] * 1e-3) / 1e9
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "algo_bytes_per_launch": int(bytes_[dom]),
+                "algo_bytes_per_launch": int(bytes_[dom]), "event_us": round(stage_ms[dom] * 1e3, 1),
                 "tflops": round(flops_attn / (stage_ms[dom] * 1e-3) / 1e12, 2)}
+    roofline.update(trace_roofline(dom, bytes_[dom]))
     copy_gbs = copy_bandwidth(dev)
     roofline["copy_GBps"] = round(copy_gbs, 1)
     roofline["frac_of_copy"] = round(achieved / copy_gbs, 4)
@@ -150,100 +168,29 @@ def main():
     # kernels in the same order, without the host's per-launch gaps (the way a
     # serving loop runs the step). `value` is taken from this replay; the eager
     # loop above gives the per-kernel event times and the eager step time.
-    graph_ms = None
-    try:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step.run(**run_args)
-        torch.cuda.current_stream().wait_stream(side)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for _ in range(args.steps):
-                step.run(**run_args)
-        graph.replay()                       # warm-up replay
-        torch.cuda.synchronize()
-        log(f"timing {args.steps} steps as one graph replay")
-        g0 = time.perf_counter()
-        graph.replay()
-        torch.cuda.synchronize()
-        graph_ms = (time.perf_counter() - g0) * 1e3 / args.steps
-        del graph
-    except RuntimeError as err:            # capture unsupported: report, keep the eager numbers
-        log(f"graph capture failed: {err}")
+    graph_ms = graph_step_ms(lambda: step.run(**run_args), args.steps)
     timing = "hip_graph" if graph_ms is not None else "eager"
     ms_value = graph_ms if graph_ms is not None else ms_step
     value = fc.batch * fc.block / (ms_value * 1e-3)
 
-    # ES-dLLM mode (auxiliary): batch 8, 256 survivors, keep 128
-    ec = W.ES_B8
-    ei = W.esdllm_inputs(ec, device=dev)
-    es_step = EsStep(ec.batch, ec.generated, ec.hidden, ec.keep, ec.dtype, dev)
-    es_args = dict(h_new=ei["h_new"], h_prev=ei["h_prev"], surv_pos=ei["surv_pos"], conf=ei["conf"],
-                   alpha=ei["alpha"], k=ei["k"], new_k=ei["new_k"], new_v=ei["new_v"],
-                   row_base=ei["row_base"], cache_k=ei["cache_k"], cache_v=ei["cache_v"])
-    for _ in range(3):
-        es_step.run(**es_args)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        es_step.run(**es_args)
-    e1.record()
-    torch.cuda.synchronize()
-    es_eager_ms = e0.elapsed_time(e1) / args.steps
-    es_graph_ms = graph_step_ms(lambda: es_step.run(**es_args), args.steps)
-    es_ms = es_graph_ms if es_graph_ms is not None else es_eager_ms
-    es_mode = {"workload": "esdllm_b8 (batch 8, 512+256 positions, hidden 4096, keep 128 of 256)",
-               "ms_per_step": round(es_ms, 4), "timing": "hip_graph" if es_graph_ms else "eager",
-               "eager_ms_per_step": round(es_eager_ms, 4),
-               "survivor positions/s": round(ec.batch * ec.generated / (es_ms * 1e-3), 1)}
-
-    # ES-dLLM skip layers (auxiliary): r = 0.5 at two layers, 256 -> 128 -> 64 survivors.
-    # Each layer's survivor states stand for the model layers before it; they are
-    # prepared outside the timed region with the library's gather.
-    px = W.es_pipeline_inputs(ec, layers=2, device=dev)
-    L = ec.prompt + ec.generated
-    sizes = [ec.generated, ec.generated // 2, ec.generated // 4]
-    skip = [EsSkipLayer(ec.batch, sizes[i], sizes[i + 1], L, ec.hidden, ec.dtype, dev) for i in range(2)]
-    arange = torch.arange(ec.batch + 1, dtype=torch.int32, device=dev)
-
-    def survivor_states(layer, surv):
-        n = surv.shape[1]
-        cnt = torch.full((ec.batch,), n, dtype=torch.int32, device=dev)
-        return bte.gather_rows(px["h_cur"][layer], surv, cnt, arange * n).view(ec.batch, n, -1)
-
-    h0 = survivor_states(0, px["surv_pos"])
-    _, s1 = skip[0].run(h0, px["h_cache"][0], px["surv_pos"], px["conf"], px["alpha"])
-    s1 = s1.clone()
-    h1 = survivor_states(1, s1)
-    torch.cuda.synchronize()
-    lev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2)]
-    lay_ms = [0.0, 0.0]
-    for _ in range(args.steps):
-        for i, (h, sv) in enumerate(((h0, px["surv_pos"]), (h1, s1))):
-            lev[i][0].record()
-            skip[i].run(h, px["h_cache"][i], sv, px["conf"], px["alpha"])
-            lev[i][1].record()
+    flush = Flush(dev)
+    out_legs = {}
+    leg_fns = {
+        "focus_b256": lambda: focus_b256_leg(dev, flush),
+        "attn_b256": lambda: attn_b256_leg(dev, flush),
+        "focus_b1024_block64": lambda: focus_block64_leg(dev, flush),
+        "es_mode": lambda: es_mode_leg(dev, flush, args.steps),
+        "es_pipeline": lambda: es_pipeline_leg(dev, flush, args.steps),
+        "es_iteration": lambda: es_iteration_leg(dev, flush),
+        "fused_scatter_attention": lambda: fused_scatter_attention_leg(step, x, args.steps, bytes_),
+        "full_step": lambda: full_step_leg(x, fc, ac, args.steps, args.warmup, dev),
+        "score_resident": lambda: score_resident_leg(dev),
+    }
+    for name in legs:
+        log(f"leg {name}")
+        out_legs[name] = leg_fns[name]()
         torch.cuda.synchronize()
-        for i in range(2):
-            lay_ms[i] += lev[i][0].elapsed_time(lev[i][1]) / args.steps
-    def both_layers():
-        skip[0].run(h0, px["h_cache"][0], px["surv_pos"], px["conf"], px["alpha"])
-        skip[1].run(h1, px["h_cache"][1], s1, px["conf"], px["alpha"])
-    pipe_graph_ms = graph_step_ms(both_layers, args.steps)
-    pipe_ms = pipe_graph_ms if pipe_graph_ms is not None else sum(lay_ms)
-    es_pipeline = {"workload": "esdllm_b8 skip layers (r = 0.5 at two layers: 256 -> 128 -> 64 "
-                               "survivors, hidden 4096, bf16)",
-                   "layer_ms": [round(v, 4) for v in lay_ms],
-                   "ms_per_iteration": round(pipe_ms, 4),
-                   "timing": "hip_graph" if pipe_graph_ms else "eager",
-                   "eager_ms_per_iteration": round(sum(lay_ms), 4),
-                   "survivor positions/s": round(ec.batch * ec.generated / (pipe_ms * 1e-3), 1)}
-
-    fused = fused_scatter_attention_leg(step, x, args.steps, bytes_)
-    full = full_step_leg(x, fc, ac, args.steps, args.warmup, dev)
-    score_resident = score_resident_leg(dev)
+    del flush
 
     if args.copy_calibration:
         src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device=dev)
@@ -266,17 +213,357 @@ def main():
                    "hkv": hkv, "head_dim": D, "hidden": H, "pool_kernel": fc.pool_kernel,
                    "k_range": [fc.k_lo, fc.k_hi], "prefix_range": [ac.prefix_lo, ac.prefix_hi],
                    "kept_rows": sum_k, "kv_rows": int(kv_len.sum()), "parallelism": "none (1 GPU)"},
-        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "es_mode": es_mode,
-        "es_pipeline": es_pipeline, "timing": timing,
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "timing": timing,
         "eager_ms_per_step": round(ms_step, 4),
         "graph_ms_per_step": round(graph_ms, 4) if graph_ms is not None else None,
         "eager_step_ms_p10_p50_p90": [round(percentile(step_ms, q), 4) for q in (10, 50, 90)],
-        "full_step": full, "fused_scatter_attention": fused, "score_resident": score_resident,
     }
+    line.update(out_legs)
     print(json.dumps(line), flush=True)
 
 
 COPY_CAL_BYTES = 256 << 20
+
+
+def delta_bytes(batch: int, block: int, hq: int, hkv: int, head_dim: int, es: int) -> int:
+    """Importance delta: Q and K of both layers read once, the mask read and the delta written."""
+    return 2 * batch * block * (hq + hkv) * head_dim * es + batch * block * (1 + 4)
+
+
+def attention_bytes(kv_len, sum_k: int, hq: int, hkv: int, head_dim: int, es: int) -> int:
+    """Reduced attention: every K and V row of every sequence read once, the kept queries
+    read and their outputs written."""
+    return int(kv_len.sum()) * hkv * head_dim * es * 2 + 2 * sum_k * hq * head_dim * es
+
+
+def attention_flops(count, kv_len, hq: int, head_dim: int) -> int:
+    return int(sum(4 * int(c) * hq * int(l) * head_dim for c, l in zip(count, kv_len)))
+
+
+class Flush:
+    """A 1 GiB device buffer written (one fill kernel) before each timed iteration of
+    a flushed leg, so that the leg's inputs are not served from the L2 or the 256 MB
+    Infinity Cache."""
+
+    def __init__(self, dev, nbytes: int = FLUSH_BYTES):
+        import torch
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.v = 0
+
+    def __call__(self):
+        self.v ^= 1
+        self.buf.fill_(self.v)
+
+
+def timed_stages(stages, iters: int, flush, warm: int = 3, between=None):
+    """Per-stage HIP-event times (ms) of `iters` iterations, with flush() before each
+    (outside the events). between(i) runs before stage i (outside the events: work that
+    stands for the model, not the path). Returns ({stage: sorted times}, sorted step
+    times from the first stage's start to the last one's end, [per-iteration sums])."""
+    import torch
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    for _ in range(warm):
+        flush()
+        for i, (_, fn) in enumerate(stages):
+            if between:
+                between(i)
+            fn()
+    torch.cuda.synchronize()
+    ev = [[(E(), E()) for _ in stages] for _ in range(iters)]
+    for it in range(iters):
+        flush()
+        for i, (_, fn) in enumerate(stages):
+            if between:
+                between(i)
+            ev[it][i][0].record()
+            fn()
+            ev[it][i][1].record()
+    torch.cuda.synchronize()
+    per = {name: sorted(ev[it][i][0].elapsed_time(ev[it][i][1]) for it in range(iters))
+           for i, (name, _) in enumerate(stages)}
+    sums = [sum(ev[it][i][0].elapsed_time(ev[it][i][1]) for i in range(len(stages)))
+            for it in range(iters)]
+    step = sorted(ev[it][0][0].elapsed_time(ev[it][-1][1]) for it in range(iters))
+    return per, step, sums
+
+
+def leg_kernels(per: dict, bytes_: dict, flops: dict | None = None) -> dict:
+    """Median time, algorithmic bytes, the HBM bound on that many bytes (8 TB/s) and the
+    achieved fraction of it, per kernel."""
+    out = {}
+    for name, ts in per.items():
+        ms = percentile(ts, 50)
+        b = int(bytes_[name])
+        k = {"ms_p50": round(ms, 4), "ms_p10_p90": [round(percentile(ts, 10), 4),
+                                                    round(percentile(ts, 90), 4)],
+             "algo_bytes": b, "bound_us": round(b / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
+             "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
+             "hbm_frac": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if flops and name in flops:
+            k["tflops"] = round(flops[name] / (ms * 1e-3) / 1e12, 2)
+            k["frac_of_bf16_dense_peak"] = round(flops[name] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+        out[name] = k
+    return out
+
+
+FLUSHED = "eager, 1 GiB buffer written before each iteration, per-kernel HIP events (medians)"
+
+
+def focus_b256_leg(dev, flush):
+    """FOCUS scoring at batch 256 (32 query / 8 KV heads, head dim 128, bf16, MaxPool 7,
+    K ~ U{4..12}, hidden 4096): importance delta -> top-K -> gather."""
+    import torch
+    from block_token_eviction_amd.chain import FocusStep
+    import workloads as W
+
+    cfg = W.FOCUS_B256
+    fi = W.focus_inputs(cfg, device=dev)
+    st = FocusStep(cfg.batch, cfg.block, cfg.hidden, cfg.hq, cfg.head_dim, cfg.k_hi, cfg.dtype, dev)
+    stages = [
+        ("focus_importance_delta", lambda: st.score(fi["q0"], fi["k0"], fi["q1"], fi["k1"], fi["decoded"], cfg.pool_kernel)),
+        ("topk_select", lambda: st.select(fi["k"])),
+        ("gather_rows", lambda: st.gather(fi["hidden"])),
+    ]
+    per, step, _ = timed_stages(stages, LEG_ITERS, flush)
+    sum_k = int(st.count.sum().item())
+    n, B = cfg.batch, cfg.block
+    bytes_ = {"focus_importance_delta": delta_bytes(n, B, cfg.hq, cfg.hkv, cfg.head_dim, 2),
+              "topk_select": n * B * 4 + n * 4 + n * (cfg.k_hi + 2) * 4,
+              "gather_rows": 2 * sum_k * cfg.hidden * 2}
+    flops = {"focus_importance_delta": score_flops(n, B, cfg.hq, cfg.head_dim)}
+    med = percentile(step, 50)
+    return {"workload": "focus_b256 (batch 256, block 32, 32q/8kv heads, head dim 128, bf16, "
+                        "MaxPool 7, K ~ U{4..12}, hidden 4096)", "timing": FLUSHED,
+            "kept_rows": sum_k,
+            "ms_per_step_p10_p50_p90": [round(percentile(step, q), 4) for q in (10, 50, 90)],
+            "block tokens/s": round(n * B / (med * 1e-3), 1),
+            "kernels": leg_kernels(per, bytes_, flops)}
+
+
+def attn_b256_leg(dev, flush):
+    """KV scatter + reduced attention at batch 256: 8 kept queries per sequence, 32q/8kv
+    heads, head dim 128, bf16, prefixes ~ U{256..2048} plus the 32-position block."""
+    import numpy as np
+    import torch
+    import block_token_eviction_amd as bte
+    import workloads as W
+
+    cfg = W.ATTN_B256
+    ai = W.attention_inputs(cfg, device=dev)
+    order = torch.empty((cfg.batch,), dtype=torch.int32, device=dev)
+    out = torch.empty_like(ai["q"])
+    stages = [
+        ("kv_scatter", lambda: bte.kv_scatter(ai["new_k"], ai["new_v"], ai["idx"], ai["count"], ai["cu"], ai["row_base"], ai["cache_k"], ai["cache_v"])),
+        ("attention_order", lambda: bte.attention_order(ai["kv_len"], out=order)),
+        ("reduced_attention", lambda: bte.reduced_attention(ai["q"], ai["count"], ai["cu"], ai["cache_k"], ai["cache_v"], ai["seq_start"], ai["kv_len"], ai["k_max"], out=out, order=order)),
+    ]
+    per, step, _ = timed_stages(stages, LEG_ITERS, flush)
+    count = ai["count"].cpu().numpy().astype(np.int64)
+    kv_len = ai["kv_len"].cpu().numpy().astype(np.int64)
+    sum_k = int(count.sum())
+    bytes_ = {"kv_scatter": 2 * 2 * sum_k * cfg.hkv * cfg.head_dim * 2,
+              "attention_order": 2 * cfg.batch * 4,
+              "reduced_attention": attention_bytes(kv_len, sum_k, cfg.hq, cfg.hkv, cfg.head_dim, 2)}
+    flops = {"reduced_attention": attention_flops(count, kv_len, cfg.hq, cfg.head_dim)}
+    med = percentile(step, 50)
+    return {"workload": "attn_b256 (batch 256, 8 kept per sequence, 32q/8kv heads, head dim 128, "
+                        "bf16, prefixes U{256..2048} + 32)", "timing": FLUSHED,
+            "kept_rows": sum_k, "kv_rows": int(kv_len.sum()),
+            "ms_per_step_p10_p50_p90": [round(percentile(step, q), 4) for q in (10, 50, 90)],
+            "block tokens/s": round(cfg.batch * cfg.block / (med * 1e-3), 1),
+            "kernels": leg_kernels(per, bytes_, flops)}
+
+
+def focus_block64_leg(dev, flush):
+    """The scoring path with blocks of 64 positions (the FOCUS paper's largest block):
+    batch 1024, 32q/8kv heads, head dim 128, bf16, MaxPool 7, K ~ U{8..24} (the batch-256
+    budget range scaled with the block), hidden 4096: delta -> top-K -> gather."""
+    import torch
+    from block_token_eviction_amd.chain import FocusStep
+    import workloads as W
+
+    cfg = W.FocusCfg("focus_b1024_block64", seed=6, batch=1024, block=64, k_lo=8, k_hi=24)
+    fi = W.focus_inputs(cfg, device=dev)
+    st = FocusStep(cfg.batch, cfg.block, cfg.hidden, cfg.hq, cfg.head_dim, cfg.k_hi, cfg.dtype, dev)
+    stages = [
+        ("focus_importance_delta", lambda: st.score(fi["q0"], fi["k0"], fi["q1"], fi["k1"], fi["decoded"], cfg.pool_kernel)),
+        ("topk_select", lambda: st.select(fi["k"])),
+        ("gather_rows", lambda: st.gather(fi["hidden"])),
+    ]
+    per, step, _ = timed_stages(stages, LEG_ITERS // 2, flush)
+    sum_k = int(st.count.sum().item())
+    n, B = cfg.batch, cfg.block
+    bytes_ = {"focus_importance_delta": delta_bytes(n, B, cfg.hq, cfg.hkv, cfg.head_dim, 2),
+              "topk_select": n * B * 4 + n * 4 + n * (cfg.k_hi + 2) * 4,
+              "gather_rows": 2 * sum_k * cfg.hidden * 2}
+    flops = {"focus_importance_delta": score_flops(n, B, cfg.hq, cfg.head_dim)}
+    med = percentile(step, 50)
+    res = {"workload": "focus_b1024_block64 (batch 1024, block 64, 32q/8kv heads, head dim 128, "
+                       "bf16, MaxPool 7, K ~ U{8..24}, hidden 4096)", "timing": FLUSHED,
+           "kept_rows": sum_k,
+           "ms_per_step_p10_p50_p90": [round(percentile(step, q), 4) for q in (10, 50, 90)],
+           "block tokens/s": round(n * B / (med * 1e-3), 1),
+           "kernels": leg_kernels(per, bytes_, flops)}
+    del fi
+    return res
+
+
+def es_mode_leg(dev, flush, steps: int):
+    """ES-dLLM mode at batch 8 (512 prompt + 256 generated positions, hidden 4096, keep 128
+    of 256): score -> top-K -> gather -> KV scatter (32 heads x 128). Flushed per-kernel
+    events; the K-step HIP-graph replay without flushes is reported beside them."""
+    import torch
+    from block_token_eviction_amd.chain import EsStep
+    import workloads as W
+
+    ec = W.ES_B8
+    ei = W.esdllm_inputs(ec, device=dev)
+    st = EsStep(ec.batch, ec.generated, ec.hidden, ec.keep, ec.dtype, dev)
+    args = dict(h_new=ei["h_new"], h_prev=ei["h_prev"], surv_pos=ei["surv_pos"], conf=ei["conf"],
+                alpha=ei["alpha"], k=ei["k"], new_k=ei["new_k"], new_v=ei["new_v"],
+                row_base=ei["row_base"], cache_k=ei["cache_k"], cache_v=ei["cache_v"])
+    import block_token_eviction_amd as bte
+    stages = [
+        ("esdllm_score", lambda: bte.esdllm_score(ei["h_new"], ei["h_prev"], ei["surv_pos"], ei["conf"], ei["alpha"], out=st.score)),
+        ("topk_select", lambda: bte.topk_select(st.score, ei["k"], st.k_max, st.idx, st.count, st.cu)),
+        ("gather_rows", lambda: bte.gather_rows(ei["h_new"], st.idx, st.count, st.cu, out=st.gathered)),
+        ("kv_scatter", lambda: bte.kv_scatter(ei["new_k"], ei["new_v"], st.idx, st.count, st.cu, ei["row_base"], ei["cache_k"], ei["cache_v"], pos_map=ei["surv_pos"])),
+    ]
+    per, step, _ = timed_stages(stages, LEG_ITERS, flush)
+    graph_ms = graph_step_ms(lambda: st.run(**args), steps)
+    n_s, kept, h = ec.batch * ec.generated, int(st.count.sum().item()), ec.hidden
+    bytes_ = {"esdllm_score": 2 * n_s * h * 2 + n_s * (4 + 4 + 4),
+              "topk_select": n_s * 4 + ec.batch * (ec.keep + 3) * 4,
+              "gather_rows": 2 * kept * h * 2,
+              "kv_scatter": 2 * 2 * kept * ec.heads * ec.head_dim * 2}
+    med = percentile(step, 50)
+    return {"workload": "esdllm_b8 (batch 8, 512+256 positions, hidden 4096, keep 128 of 256)",
+            "timing": FLUSHED,
+            "ms_per_step_p10_p50_p90": [round(percentile(step, q), 4) for q in (10, 50, 90)],
+            "survivor positions/s": round(n_s / (med * 1e-3), 1),
+            "graph_ms_per_step_unflushed": round(graph_ms, 4) if graph_ms is not None else None,
+            "kernels": leg_kernels(per, bytes_)}
+
+
+def es_pipeline_leg(dev, flush, steps: int):
+    """Two ES-dLLM skip layers (r = 0.5 each: 256 -> 128 -> 64 survivors, hidden 4096,
+    bf16), each score + in-place hidden-cache update -> top-K -> compaction of the kept
+    rows and positions. Each layer's survivor states stand for the model's layers before
+    it; they are prepared once, outside the timed region."""
+    import torch
+    import block_token_eviction_amd as bte
+    from block_token_eviction_amd.chain import EsSkipLayer
+    import workloads as W
+
+    ec = W.ES_B8
+    px = W.es_pipeline_inputs(ec, layers=2, device=dev)
+    L = ec.prompt + ec.generated
+    sizes = [ec.generated, ec.generated // 2, ec.generated // 4]
+    skip = [EsSkipLayer(ec.batch, sizes[i], sizes[i + 1], L, ec.hidden, ec.dtype, dev) for i in range(2)]
+    arange = torch.arange(ec.batch + 1, dtype=torch.int32, device=dev)
+
+    def survivor_states(layer, surv):
+        n = surv.shape[1]
+        cnt = torch.full((ec.batch,), n, dtype=torch.int32, device=dev)
+        return bte.gather_rows(px["h_cur"][layer], surv, cnt, arange * n).view(ec.batch, n, -1)
+
+    h0 = survivor_states(0, px["surv_pos"])
+    _, s1 = skip[0].run(h0, px["h_cache"][0], px["surv_pos"], px["conf"], px["alpha"])
+    s1 = s1.view(ec.batch, -1).clone()
+    h1 = survivor_states(1, s1)
+    torch.cuda.synchronize()
+    stages = []
+    for i, (h, sv) in enumerate(((h0, px["surv_pos"]), (h1, s1))):
+        sk = skip[i]
+        stages += [
+            (f"layer{i}_esdllm_score_update", lambda sk=sk, h=h, sv=sv, i=i: bte.esdllm_score_update(h, px["h_cache"][i], sv, px["conf"], px["alpha"], out=sk.score)),
+            (f"layer{i}_topk_select", lambda sk=sk: bte.topk_select(sk.score, sk.k, sk.keep, sk.idx, sk.count, sk.cu)),
+            (f"layer{i}_gather_rows_multi", lambda sk=sk, h=h, sv=sv: bte.gather_rows_multi([h, sv], sk.idx, sk.count, sk.cu, outs=[sk.h_next, sk.surv_next])),
+        ]
+    per, step, _ = timed_stages(stages, LEG_ITERS, flush)
+
+    def both_layers():
+        skip[0].run(h0, px["h_cache"][0], px["surv_pos"], px["conf"], px["alpha"])
+        skip[1].run(h1, px["h_cache"][1], s1, px["conf"], px["alpha"])
+    graph_ms = graph_step_ms(both_layers, steps)
+    bytes_ = {}
+    for i in range(2):
+        n, k, h = ec.batch * sizes[i], ec.batch * sizes[i + 1], ec.hidden
+        bytes_[f"layer{i}_esdllm_score_update"] = 3 * n * h * 2 + n * (4 + 4 + 4)
+        bytes_[f"layer{i}_topk_select"] = n * 4 + ec.batch * (sizes[i + 1] + 3) * 4
+        bytes_[f"layer{i}_gather_rows_multi"] = 2 * k * (h * 2 + 4)
+    med = percentile(step, 50)
+    return {"workload": "esdllm_b8 skip layers (r = 0.5 at two layers: 256 -> 128 -> 64 "
+                        "survivors, hidden 4096, bf16)", "timing": FLUSHED,
+            "ms_per_iteration_p10_p50_p90": [round(percentile(step, q), 4) for q in (10, 50, 90)],
+            "survivor positions/s": round(ec.batch * ec.generated / (med * 1e-3), 1),
+            "graph_ms_per_iteration_unflushed": round(graph_ms, 4) if graph_ms is not None else None,
+            "kernels": leg_kernels(per, bytes_)}
+
+
+def es_iteration_leg(dev, flush, iters: int = 12, period: int = 3):
+    """ES-dLLM iterations with the device-side bookkeeping (batch 8, a 256-position block
+    after a 512-token prompt, hidden 4096, bf16, two skip layers keeping 128 and 64, a
+    refresh without skipping every third iteration; the sequences' counters start at
+    0..7, so each iteration mixes refreshing and skipping sequences). Each skip layer's
+    survivor states stand for the model's layer output: they are taken from a fixed
+    tensor by torch indexing between the library calls, outside the events. Reports the
+    library's time per iteration (sum of its kernels' events)."""
+    import numpy as np
+    import torch
+    import block_token_eviction_amd as bte
+    from block_token_eviction_amd.chain import EsIteration
+    import workloads as W
+
+    ec = W.ES_B8
+    batch, L, h, blk, keep = ec.batch, ec.prompt + ec.generated, ec.hidden, ec.generated, [128, 64]
+    px = W.es_pipeline_inputs(ec, layers=2, device=dev)
+    it = torch.arange(batch, dtype=torch.int32, device=dev)
+    start = torch.full((batch,), ec.prompt, dtype=torch.int32, device=dev)
+    run = EsIteration(batch, blk, h, keep, period, ec.dtype, dev)
+    state = {}
+
+    def states(l, rows, cu):
+        r = torch.arange(rows.shape[0], device=dev, dtype=torch.int32)
+        b = torch.searchsorted(cu[1:].contiguous(), r, right=True).clamp_(max=batch - 1)
+        return px["h_cur"][l].view(batch * L, h).index_select(0, b * L + rows.long().clamp(0, L - 1))
+
+    def between(i):                       # the model's layer output for the survivors
+        if i == 1:
+            state["rows"], state["cnt"], state["cu"] = run.surv0.view(-1), run.count0, run.cu0
+            state["h"] = states(0, state["rows"], state["cu"])
+        elif i == 4:
+            state["rows"], state["cnt"], state["cu"] = run.surv_next[0], run.count[0], run.cu[0]
+            state["h"] = states(1, state["rows"], state["cu"])
+
+    def layer_stages(l):
+        return [
+            (f"layer{l}_esdllm_score_update", lambda: bte.esdllm_score_update(state["h"], px["h_cache"][l], state["rows"], px["conf"], px["alpha"], count=state["cnt"], cu=state["cu"], cap=blk, out=run.score[l])),
+            (f"layer{l}_topk_select", lambda: bte.topk_select(run.score[l], run.keep_out[l], blk, run.idx[l], run.count[l], run.cu[l])),
+            (f"layer{l}_gather_rows_multi_ragged", lambda: bte.gather_rows_multi_ragged([state["h"], state["rows"]], state["cu"], run.idx[l], run.count[l], run.cu[l], outs=[run.h_next[l], run.surv_next[l]])),
+        ]
+    stages = [("esdllm_schedule", lambda: run.schedule(it, start))] + layer_stages(0) + layer_stages(1)
+    for i, (_, fn) in enumerate(stages):          # one untimed pass, then counters back to 0..7
+        between(i)
+        fn()
+    it.copy_(torch.arange(batch, dtype=torch.int32, device=dev))
+    refresh = []
+    per, _, sums = timed_stages(stages, iters, flush, warm=0, between=between)
+    it_host = it.cpu().numpy()
+    # the counters ran 0..7 + iters: refreshes per iteration follow from them
+    for i in range(iters):
+        c = np.arange(batch) + i
+        refresh.append(int(((c == 0) | (c % period == 0)).sum()))
+    per_ms = float(np.median(sums))
+    return {"workload": "esdllm_b8 iterations (block 256 after 512 prompt positions, hidden 4096, "
+                        "keep 128 -> 64, refresh every 3rd iteration, counters 0..7)",
+            "timing": FLUSHED + "; model stand-in between the calls is not timed",
+            "iterations": iters, "refreshing_sequences_per_iteration": refresh,
+            "counters_after": it_host.tolist(),
+            "library_ms_per_iteration_p50": round(per_ms, 4),
+            "library_ms_per_iteration_min_max": [round(min(sums), 4), round(max(sums), 4)],
+            "survivor positions/s": round(batch * blk / (per_ms * 1e-3), 1),
+            "kernels_ms_p50": {k: round(percentile(v, 50), 4) for k, v in per.items()}}
 
 
 def fused_scatter_attention_leg(step, x, steps: int, bytes_: dict):
@@ -491,7 +778,8 @@ def full_step_leg(x, fc, ac, steps: int, warmup: int, dev):
             "kernels": kernels}
 KERNEL_SOURCES = {"reduced_attention": ["reduced_attention.hip", "bte_device.h"],
                   "focus_importance_delta": ["focus_delta.hip", "bte_device.h"],
-                  "rows": ["rows.hip", "bte_device.h"]}
+                  "rows": ["rows.hip", "bte_device.h"],
+                  "esdllm": ["esdllm_score.hip", "bte_device.h"]}
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -503,22 +791,50 @@ def kernel_source_hash(kernel: str) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch from the committed counter summary (FETCH_SIZE +
-    WRITE_SIZE, scaled by a plain copy of known size), or None when the
-    kernel's sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_chain_b1024_counters.json")
+def _profile_record(name: str):
+    """A committed profile summary (profiles/<name>.json), or None when missing or when the
+    kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{name}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    if rec.get("kernel_sources_sha1") != kernel_source_hash(kernel):
+    key = rec.get("source_key", "reduced_attention")
+    if rec.get("kernel_sources_sha1") != kernel_source_hash(key):
         return None
-    return rec.get("traffic_bytes_per_launch")
+    return rec
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, scaled by a plain copy of known size), or None when the
+    kernel's sources changed since the counters were taken."""
+    rec = _profile_record(f"{kernel}_chain_b1024_counters")
+    return None if rec is None else rec.get("traffic_bytes_per_launch")
+
+
+def trace_roofline(kernel: str, algo_bytes: int) -> dict:
+    """The kernel's average duration over the eager timed loop's dispatches in a committed
+    rocprofv3 kernel trace of this bench (same dispatches as the events above), and the
+    roofline fraction it gives; None while the kernel's sources differ from the traced ones."""
+    rec = _profile_record(f"{kernel}_chain_b1024_trace")
+    if rec is None:
+        return {"trace_us": None, "frac_trace": None}
+    us = rec["trace_avg_us"]
+    return {"trace_us": round(us, 1), "frac_trace": round(algo_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "trace_dispatches": rec.get("dispatches"),
+            "trace_run_event_us": rec.get("events_same_run_us")}
 
 
 def cpu_model() -> str:
-    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    """The host CPU's model name (lscpu's "Model name", else /proc/cpuinfo), or "unknown"."""
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         with open("/proc/cpuinfo") as fh:
             for line in fh:
@@ -529,12 +845,13 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(x, fc, ac, budget_s: float = 12.0):
-    """The float64 oracle on the first sequences of the same workload, chunk by
-    chunk until about `budget_s` seconds of CPU work; block tokens/s of that sample."""
+def cpu_baseline(x, fc, ac, budget_s: float = 12.0, single_budget_s: float = 5.0):
+    """The float64 oracle on the first sequences of the same workload, chunk by chunk until
+    about `budget_s` seconds of CPU work, with its BLAS on every thread it is given; then
+    the same at one thread for about `single_budget_s`. Block tokens/s of each sample."""
     import numpy as np
     import torch
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle.chain as oc
 
@@ -546,29 +863,44 @@ def cpu_baseline(x, fc, ac, budget_s: float = 12.0):
 
     seq_start = x["seq_start"].cpu().numpy()
     kv_len = x["kv_len"].cpu().numpy()
-    done, elapsed, chunk = 0, 0.0, 16
+
+    def run(budget, chunk):
+        done, elapsed = 0, 0.0
+        while done < fc.batch and elapsed < budget:
+            lo, hi = done, min(fc.batch, done + chunk)
+            r0, r1 = int(seq_start[lo]), int(seq_start[hi - 1] + kv_len[hi - 1])
+            cap = (hi - lo) * fc.k_hi
+            inp = dict(q0=f64(x["q0"][lo:hi]), k0=f64(x["k0"][lo:hi]), q1=f64(x["q1"][lo:hi]),
+                       k1=f64(x["k1"][lo:hi]), decoded=x["decoded"][lo:hi].cpu().numpy(),
+                       k=x["k"][lo:hi].cpu().numpy(), hidden_rows=bits(x["hidden_rows"][lo:hi]),
+                       pool_kernel=fc.pool_kernel, new_k=bits(x["new_k"][:cap]),
+                       new_v=bits(x["new_v"][:cap]), q_kept=bits(x["q_kept"][:cap]),
+                       cache_k=bits(x["cache_k"][r0:r1]), cache_v=bits(x["cache_v"][r0:r1]),
+                       seq_start=seq_start[lo:hi] - r0, kv_len=kv_len[lo:hi],
+                       row_base=x["row_base"][lo:hi].cpu().numpy() - r0)
+            t0 = time.perf_counter()
+            oc.focus_step(**inp, hq=fc.hq, hkv=fc.hkv, k_max=fc.k_hi,
+                          scale=1.0 / math.sqrt(fc.head_dim))
+            elapsed += time.perf_counter() - t0
+            done = hi
+        return done, elapsed
+
     log("cpu baseline (oracle)")
-    while done < fc.batch and elapsed < budget_s:
-        lo, hi = done, min(fc.batch, done + chunk)
-        r0, r1 = int(seq_start[lo]), int(seq_start[hi - 1] + kv_len[hi - 1])
-        cap = (hi - lo) * fc.k_hi
-        inp = dict(q0=f64(x["q0"][lo:hi]), k0=f64(x["k0"][lo:hi]), q1=f64(x["q1"][lo:hi]),
-                   k1=f64(x["k1"][lo:hi]), decoded=x["decoded"][lo:hi].cpu().numpy(),
-                   k=x["k"][lo:hi].cpu().numpy(), hidden_rows=bits(x["hidden_rows"][lo:hi]),
-                   pool_kernel=fc.pool_kernel, new_k=bits(x["new_k"][:cap]),
-                   new_v=bits(x["new_v"][:cap]), q_kept=bits(x["q_kept"][:cap]),
-                   cache_k=bits(x["cache_k"][r0:r1]), cache_v=bits(x["cache_v"][r0:r1]),
-                   seq_start=seq_start[lo:hi] - r0, kv_len=kv_len[lo:hi],
-                   row_base=x["row_base"][lo:hi].cpu().numpy() - r0)
-        t0 = time.perf_counter()
-        oc.focus_step(**inp, hq=fc.hq, hkv=fc.hkv, k_max=fc.k_hi, scale=1.0 / math.sqrt(fc.head_dim))
-        elapsed += time.perf_counter() - t0
-        done = hi
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    done, elapsed = run(budget_s, 16)
+    with threadpool_limits(limits=1):
+        done1, elapsed1 = run(single_budget_s, 4)
+    affinity = len(os.sched_getaffinity(0))
     return {"value": round(done * fc.block / elapsed, 1), "unit": "block tokens/s",
             "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
+            "affinity_cpus": affinity,
             "sample": f"first {done} of {fc.batch} sequences of chain_b1024, whole step, "
-                      f"{elapsed:.1f} s (numpy float64; BLAS threads = {threads})"}
+                      f"{elapsed:.1f} s (numpy float64; BLAS threads = {threads} of "
+                      f"{affinity} CPUs in this process's affinity mask)",
+            "one_thread": {"value": round(done1 * fc.block / elapsed1, 1),
+                           "unit": "block tokens/s", "cores": 1,
+                           "sample": f"first {done1} sequences, {elapsed1:.1f} s, BLAS limited "
+                                     f"to one thread"}}
 
 
 if __name__ == "__main__":

@@ -1,7 +1,12 @@
 """Summarise rocprofv3 output of bench.py into profiles/ (text + counter JSON).
 
+This is the evidence generator for profiles/: every summary there names the
+rocprofv3 command it was made from and the call of this script that wrote it.
+
 Usage:
-  python profile_summary.py trace  <kernel_stats.csv> <out.md> "<command>"
+  python profile_summary.py trace  <kernel_stats.csv> <out.md> "<command>" [<dispatches.json>]
+  python profile_summary.py dispatches <kernel_trace.csv> <kernel-substring> <source-key>
+        <skip> <count> <bench_json_line_file> <stage> <out.json> "<command>"
   python profile_summary.py counters <fetch_counter_collection.csv> <write_counter_collection.csv>
         <kernel-substring> <source-key> <out.json> "<fetch command>" "<write command>"
         [grid=<work-items>] [first=<n>]
@@ -36,11 +41,22 @@ def _rows(path):
         return list(csv.DictReader(fh))
 
 
-def trace(stats_csv: str, out_md: str, command: str):
+def trace(stats_csv: str, out_md: str, command: str, dispatches_json: str | None = None):
     rows = _rows(stats_csv)
     lines = [f"# rocprofv3 kernel trace summary", "", f"Command: `{command}`", "",
-             "| kernel | calls | avg (us) | min (us) | max (us) | share |",
-             "|---|---|---|---|---|---|"]
+             f"Written by: `python profile_summary.py trace <out>/trace_kernel_stats.csv {out_md} "
+             f"\"<command>\"" + (f" {dispatches_json}`" if dispatches_json else "`"), ""]
+    if dispatches_json:
+        d = json.load(open(dispatches_json))
+        lines += [f"The dominant kernel over the main step's eager timed loop (its dispatches "
+                  f"{d['selected'][0] + 1} to {d['selected'][1]} in start order, the launches the "
+                  f"HIP events time): average {d['trace_avg_us']:.1f} us (min "
+                  f"{d['trace_min_us']:.1f}, max {d['trace_max_us']:.1f}); HIP events of the same "
+                  f"run {d['events_same_run_us']:.1f} us. The table's average over all "
+                  f"{d['dispatches_in_trace']} dispatches ({d['trace_all_dispatches_avg_us']:.1f} us) "
+                  f"also holds the warm-up steps, the graph replays and the other legs' launches.", ""]
+    lines += ["| kernel | calls | avg (us) | min (us) | max (us) | share |",
+              "|---|---|---|---|---|---|"]
     for r in rows:
         name = r["Name"].replace("(anonymous namespace)::", "")
         short = name.split("(")[0]
@@ -50,6 +66,28 @@ def trace(stats_csv: str, out_md: str, command: str):
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['Percentage']):.1f}% |")
     open(out_md, "w").write("\n".join(lines) + "\n")
+
+
+def dispatches(trace_csv, sub, source_key, skip, count, bench_json, stage, out_json, command):
+    """Duration of the named kernel's dispatches number skip .. skip + count - 1 (in start
+    order) of a rocprofv3 kernel trace: for bench.py's main step with --warmup W and
+    --steps K, skip = W and count = K select exactly the eager timed loop's launches.
+    Records their average next to the HIP-event average of the same stage printed by the
+    same (traced) run, and the sha1 of the kernel's sources."""
+    skip, count = int(skip), int(count)
+    rows = [r for r in _rows(trace_csv) if sub in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+    sel = us[skip:skip + count]
+    line = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    rec = {"kernel": sub, "source_key": source_key, "dispatches_in_trace": len(us),
+           "selected": [skip, skip + count], "dispatches": len(sel),
+           "trace_avg_us": statistics.mean(sel), "trace_min_us": min(sel),
+           "trace_max_us": max(sel), "trace_all_dispatches_avg_us": statistics.mean(us),
+           "events_same_run_us": line["kernels"][stage]["ms"] * 1e3,
+           "kernel_sources_sha1": bench.kernel_source_hash(source_key), "command": command}
+    json.dump(rec, open(out_json, "w"), indent=1)
+    print(json.dumps(rec))
 
 
 def _per_kernel(path, counter, sub, grid=None, first=None):
@@ -97,6 +135,8 @@ def counters(fetch_csv, write_csv, sub, source_key, out_json, fetch_cmd, write_c
 
 if __name__ == "__main__":
     if sys.argv[1] == "trace":
-        trace(*sys.argv[2:5])
+        trace(*sys.argv[2:6])
+    elif sys.argv[1] == "dispatches":
+        dispatches(*sys.argv[2:11])
     else:
         counters(*sys.argv[2:9], *sys.argv[9:])
