@@ -11,9 +11,9 @@
 // loads issued before the stores. The per-sequence counts live on the device,
 // so grids are sized from k_max and surplus workgroups exit at once. The
 // gather (hidden rows, 8 KB at the workloads) takes one workgroup per row;
-// the scatter (K/V rows of a few KB) treats a sequence's kept rows as one flat
-// space of count[b] * chunks-per-row chunks split evenly over n_split
-// workgroups. All three keep a sequence's workgroups on one XCD, in order
+// the scatter (K/V rows of a few KB) treats a sequence's kept K and V rows as
+// one flat space of chunks split evenly over n_split workgroups (one per
+// sequence at large batches). All three keep a sequence's workgroups on one XCD, in order
 // (xcd_seq_part): measured 10-45 % faster than sequence-major or slot-major
 // grids, whose real rows pile up on a few XCDs or lose write locality.
 #include "bte_device.h"
@@ -25,6 +25,8 @@ constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
 constexpr int kPass = kThreads * kUnroll;   // chunks one workgroup moves per pass
 constexpr int kMaxTensors = 8;             // tensors of one multi-row gather
+constexpr int kScatterUnroll = 8;          // chunks in flight per thread in the scatter
+constexpr int kScatterTarget = 4096;       // workgroups a scatter launch aims at
 
 // Row and chunk of flat chunk index c, with chunks per row cpr and its float
 // reciprocal (exact after the +-1 correction for c < 2^24).
@@ -35,32 +37,6 @@ __device__ __forceinline__ void split_chunk(uint32_t c, uint32_t cpr, float inv_
   if ((t + 1) * cpr <= c) ++t;
   row = t;
   chunk = c - t * cpr;
-}
-
-// Copies chunks [lo, hi) of the flat space: row t's source is src_row(t) and
-// its destination dst_row(t) (byte pointers).
-template <class SrcRow, class DstRow>
-__device__ __forceinline__ void copy_range(uint32_t lo, uint32_t hi, uint32_t cpr, float inv_cpr,
-                                           SrcRow src_row, DstRow dst_row) {
-  for (uint32_t base = lo; base < hi; base += kPass) {
-    u32x4 v[kUnroll];
-    char* d[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t c = base + u * kThreads + threadIdx.x;
-      d[u] = nullptr;
-      if (c < hi) {
-        uint32_t t, ch;
-        split_chunk(c, cpr, inv_cpr, t, ch);
-        v[u] = ld16_stream(src_row(t) + 16 * (size_t)ch);
-        d[u] = dst_row(t) + 16 * (size_t)ch;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      if (d[u])
-        __builtin_nontemporal_store(v[u], (__attribute__((address_space(1))) u32x4*)d[u]);
-  }
 }
 
 // This workgroup's share [lo, hi) of sequence b's `total` chunks: part s of
@@ -149,6 +125,10 @@ struct ScatterMap {
   int lg_page;
 };
 
+// Scatter: sequence b's kept rows of new_k and then of new_v form one flat
+// space of (1 or 2) * count[b] * chunks-per-row chunks, split evenly over the
+// sequence's n_split workgroups, so one workgroup moves K and V rows alike and
+// each thread keeps kScatterUnroll chunks in flight.
 template <bool kPaged>
 __global__ __launch_bounds__(kThreads) void scatter_rows_kernel(
     const char* __restrict__ new_k, const char* __restrict__ new_v, const int32_t* __restrict__ idx,
@@ -158,47 +138,62 @@ __global__ __launch_bounds__(kThreads) void scatter_rows_kernel(
     float inv_cpr) {
   int b, part;
   if (!xcd_seq_part(batch, n_split, b, part)) return;
-  const uint32_t s = (uint32_t)part;
   const uint32_t cpr = (uint32_t)(row_bytes / 16);
+  const uint32_t rows = (uint32_t)count[b];
+  const uint32_t tensors = new_v ? 2u : 1u;
   uint32_t lo, hi;
-  if (!share((uint32_t)count[b] * cpr, (uint32_t)n_split, s, lo, hi)) return;
+  if (!share(tensors * rows * cpr, (uint32_t)n_split, (uint32_t)part, lo, hi)) return;
   const int32_t* ib = idx + (size_t)b * k_max;
   const int32_t* pm = pos_map ? pos_map + (size_t)b * n : nullptr;
   const int64_t rb = kPaged ? (int64_t)map.pos_base[b] : map.row_base[b];
   const int32_t* bt = kPaged ? map.block_table + (size_t)b * map.max_pages : nullptr;
-  const char* sb = (blockIdx.y == 0 ? new_k : new_v) + (size_t)cu[b] * row_bytes;
-  char* cache = blockIdx.y == 0 ? cache_k : cache_v;
-  copy_range(lo, hi, cpr, inv_cpr, [&](uint32_t t) { return sb + (size_t)t * row_bytes; },
-             [&](uint32_t t) {
-               const int j = ib[t];
-               const int64_t p = rb + (pm ? pm[j] : j);
-               size_t row = (size_t)p;
-               if constexpr (kPaged) {
-                 const int lg = map.lg_page;
-                 row = ((size_t)bt[p >> lg] << lg) + (size_t)(p & ((1 << lg) - 1));
-               }
-               return cache + row * row_bytes;
-             });
+  const size_t first = (size_t)cu[b];
+  for (uint32_t base = lo; base < hi; base += kThreads * kScatterUnroll) {
+    u32x4 v[kScatterUnroll];
+    char* d[kScatterUnroll];
+#pragma unroll
+    for (int u = 0; u < kScatterUnroll; ++u) {
+      const uint32_t c = base + u * kThreads + threadIdx.x;
+      d[u] = nullptr;
+      if (c < hi) {
+        uint32_t q, ch;
+        split_chunk(c, cpr, inv_cpr, q, ch);
+        const bool is_v = q >= rows;
+        const uint32_t t = is_v ? q - rows : q;
+        const int j = ib[t];
+        const int64_t p = rb + (pm ? pm[j] : j);
+        size_t row = (size_t)p;
+        if constexpr (kPaged) {
+          const int lg = map.lg_page;
+          row = ((size_t)bt[p >> lg] << lg) + (size_t)(p & ((1 << lg) - 1));
+        }
+        v[u] = ld16_stream((is_v ? new_v : new_k) + (first + t) * row_bytes + 16 * (size_t)ch);
+        d[u] = (is_v ? cache_v : cache_k) + row * row_bytes + 16 * (size_t)ch;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kScatterUnroll; ++u)
+      if (d[u])
+        __builtin_nontemporal_store(v[u], (__attribute__((address_space(1))) u32x4*)d[u]);
+  }
 }
 
-// Workgroups per sequence: enough that a sequence at k_max rows takes at most
-// 4 passes each, and that a small batch still spreads over the GPU (>= 2048
-// workgroups), but not more than one chunk per thread at k_max. Each
-// sequence's real rows are split evenly over its workgroups on the device.
+// Workgroups per sequence: about kScatterTarget workgroups in all (one per
+// sequence at large batches), but no more than one chunk per thread at k_max
+// rows of every tensor. Each sequence's real rows are split evenly over its
+// workgroups on the device.
 struct Split {
   int n_split;
   bool ok;
 };
 
-Split plan(int batch, int k_max, size_t row_bytes) {
+Split plan(int batch, int k_max, size_t row_bytes, int tensors) {
   const uint64_t cpr = row_bytes / 16;
-  const uint64_t chunks = (uint64_t)k_max * cpr;            // largest flat space of a sequence
+  const uint64_t chunks = (uint64_t)tensors * k_max * cpr;   // largest flat space of a sequence
   if (chunks >= (1u << 24)) return {0, false};
-  uint64_t n_split = (chunks + 4 * kPass - 1) / (4 * kPass);
-  const uint64_t want = (2048 + batch - 1) / batch;
+  const uint64_t want = (kScatterTarget + batch - 1) / batch;
   const uint64_t most = (chunks + kThreads - 1) / kThreads;
-  const uint64_t spread = want < most ? want : most;
-  if (n_split < spread) n_split = spread;
+  uint64_t n_split = want < most ? want : most;
   if (n_split < 1) n_split = 1;
   if ((uint64_t)(batch + kXcds - 1) / kXcds * kXcds * n_split > 0x7fffffffu) return {0, false};
   return {(int)n_split, true};
@@ -241,10 +236,10 @@ static int scatter_launch(const void* new_k, const void* new_v, const int32_t* i
                           bte::ScatterMap map, void* cache_k, void* cache_v, int batch, int k_max,
                           size_t row_bytes, hipStream_t stream) {
   using namespace bte;
-  const Split sp = plan(batch, k_max, row_bytes);
+  const Split sp = plan(batch, k_max, row_bytes, new_v ? 2 : 1);
   if (!sp.ok) return BTE_ERR_DIM;
   const unsigned grid = (unsigned)((batch + kXcds - 1) / kXcds * kXcds * sp.n_split);
-  hipLaunchKernelGGL(scatter_rows_kernel<kPaged>, dim3(grid, new_v ? 2 : 1), dim3(kThreads), 0,
+  hipLaunchKernelGGL(scatter_rows_kernel<kPaged>, dim3(grid), dim3(kThreads), 0,
                      stream, (const char*)new_k, (const char*)new_v, idx, count, cu, pos_map, n,
                      map, (char*)cache_k, (char*)cache_v, batch, k_max, row_bytes, sp.n_split,
                      1.0f / (float)(row_bytes / 16));
