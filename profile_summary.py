@@ -7,6 +7,8 @@ Usage:
   python profile_summary.py trace  <kernel_stats.csv> <out.md> "<command>" [<dispatches.json>]
   python profile_summary.py dispatches <kernel_trace.csv> <kernel-substring> <source-key>
         <skip> <count> <bench_json_line_file> <stage> <out.json> "<command>"
+  python profile_summary.py mfma <mfma_counter_collection.csv> <out.md> "<command>"
+        <kernel-substring>@<grid>@<label>@<algorithmic flops> ...
   python profile_summary.py counters <fetch_counter_collection.csv> <write_counter_collection.csv>
         <kernel-substring> <source-key> <out.json> "<fetch command>" "<write command>"
         [grid=<work-items>] [first=<n>]
@@ -90,6 +92,27 @@ def dispatches(trace_csv, sub, source_key, skip, count, bench_json, stage, out_j
     print(json.dumps(rec))
 
 
+def mfma(csv_path, out_md, command, *kernels):
+    """MfmaUtil and MfmaFlopsBF16 (rocprofv3 derived counters) averaged per launch of each
+    named kernel of the given grid size (work-items), next to its algorithmic flops."""
+    rows = _rows(csv_path)
+    lines = ["# MFMA utilisation (rocprofv3 derived counters)", "", f"Command: `{command}`", "",
+             "`MfmaUtil` = 100 * sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max(GRBM_GUI_ACTIVE) * SIMDs);",
+             "`MfmaFlopsBF16` = SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 (flops the matrix cores executed).",
+             "", "| kernel | workload | launches | MfmaUtil | MFMA flops executed | algorithmic flops |",
+             "|---|---|---|---|---|---|"]
+    for spec in kernels:
+        sub, grid, label, algo = spec.split("@")
+        vals = {"MfmaUtil": [], "MfmaFlopsBF16": []}
+        for r in rows:
+            if sub in r["Kernel_Name"] and r["Grid_Size"] == grid and r["Counter_Name"] in vals:
+                vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
+        n = len(vals["MfmaUtil"])
+        lines.append(f"| `{sub}` | {label} | {n} | {statistics.mean(vals['MfmaUtil']):.1f} % | "
+                     f"{statistics.mean(vals['MfmaFlopsBF16']) / 1e9:.2f} G | {float(algo) / 1e9:.2f} G |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 def _per_kernel(path, counter, sub, grid=None, first=None):
     """Counter values of the named kernel's dispatches (of grid size `grid` and
     the first `first` of them, if given), and of the calibration copy (the last
@@ -121,7 +144,8 @@ def counters(fetch_csv, write_csv, sub, source_key, out_json, fetch_cmd, write_c
     wscale = bench.COPY_CAL_BYTES / (max(wcal) * kib)
     fetch = statistics.mean(f) * kib * fscale
     write = statistics.mean(w) * kib * wscale
-    rec = {"kernel": sub, "grid_size": grid, "first": first, "launches": len(f), "fetch_kib_raw": statistics.mean(f),
+    rec = {"kernel": sub, "source_key": source_key, "grid_size": grid, "first": first,
+           "launches": len(f), "fetch_kib_raw": statistics.mean(f),
            "write_kib_raw": statistics.mean(w), "copy_fetch_kib_raw": max(fcal),
            "copy_write_kib_raw": max(wcal), "copy_bytes": bench.COPY_CAL_BYTES,
            "fetch_scale": fscale, "write_scale": wscale,
@@ -138,5 +162,7 @@ if __name__ == "__main__":
         trace(*sys.argv[2:6])
     elif sys.argv[1] == "dispatches":
         dispatches(*sys.argv[2:11])
+    elif sys.argv[1] == "mfma":
+        mfma(*sys.argv[2:])
     else:
         counters(*sys.argv[2:9], *sys.argv[9:])
