@@ -22,6 +22,8 @@ import numpy as np
 
 def _bytes(a: np.ndarray, rows: int) -> np.ndarray:
     a = np.ascontiguousarray(a)
+    if a.size == 0:                    # no rows to copy (e.g. a sequence with nothing kept)
+        return np.zeros((rows, 0), dtype=np.uint8)
     return a.view(np.uint8).reshape(rows, -1)
 
 

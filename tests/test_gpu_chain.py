@@ -1,6 +1,7 @@
 """GPU parity of the whole FOCUS step at the batch-1024 workload, in the launch
-configuration bench.py times (FocusStep on one stream), checked on a sample of
-sequences against the oracle's own chain. Also a small full-check chain."""
+configuration bench.py times (FocusStep on one stream), checked against the
+oracle on every sequence: the delta, the selection, the gather, the KV cache
+and the attention outputs. Also a small chain.""" 
 import math
 
 import numpy as np
@@ -23,16 +24,21 @@ def _f64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def _check_chain(fc, ac, sample, device="cuda", fused=False):
+def _check_chain(fc, ac, attn_sample, device="cuda", fused=False):
+    """Every sequence: delta to tolerance, a valid selection, and, where the kept set equals
+    the oracle's own, the gathered rows and the scattered block rows bit for bit; the rest
+    of both caches unchanged (compared on the device against a copy taken before the step).
+    attn_sample: the sequences whose attention output is checked against the oracle."""
     from block_token_eviction_amd.chain import FocusStep
-    say(f"chain {fc.name} batch={fc.batch} sample={len(sample)} fused={fused}")
+    say(f"chain {fc.name} batch={fc.batch} attention sample={len(attn_sample)} fused={fused}")
     x = W.chain_inputs(fc, ac, device=device)
-    cache_k0 = {int(b): None for b in sample}
     seq_start = x["seq_start"].cpu().numpy()
     kv_len = x["kv_len"].cpu().numpy()
-    for b in sample:                         # pre-images of the sampled sequences' caches
-        r0, r1 = int(seq_start[b]), int(seq_start[b] + kv_len[b])
-        cache_k0[int(b)] = (_bits(x["cache_k"][r0:r1]), _bits(x["cache_v"][r0:r1]))
+    block_rows = torch.from_numpy((x["row_base"].cpu().numpy()[:, None]
+                                   + np.arange(fc.block)[None, :]).reshape(-1)).to(device)
+    pre_k, pre_v = x["cache_k"].clone(), x["cache_v"].clone()
+    blk_k0 = _bits(x["cache_k"][block_rows]).reshape(fc.batch, fc.block, -1)
+    blk_v0 = _bits(x["cache_v"][block_rows]).reshape(fc.batch, fc.block, -1)
     step = FocusStep(fc.batch, fc.block, fc.hidden, fc.hq, fc.head_dim, fc.k_hi, fc.dtype, device,
                      hkv=fc.hkv)
     step.run(q0=x["q0"], k0=x["k0"], q1=x["q1"], k1=x["k1"], decoded=x["decoded"], k=x["k"],
@@ -41,48 +47,58 @@ def _check_chain(fc, ac, sample, device="cuda", fused=False):
              seq_start=x["seq_start"], kv_len=x["kv_len"], row_base=x["row_base"],
              pos_base=x["prefix"].to(torch.int32), fused=fused)
     torch.cuda.synchronize()
+    # rows outside every block are untouched (on the device: the caches are GBs)
+    outside = torch.ones(x["cache_k"].shape[0], dtype=torch.bool, device=device)
+    outside[block_rows] = False
+    assert torch.equal(x["cache_k"][outside], pre_k[outside])
+    assert torch.equal(x["cache_v"][outside], pre_v[outside])
+    del pre_k, pre_v, outside
     g_delta = step.delta.cpu().numpy()
     g_idx, g_cnt, g_cu = step.idx.cpu().numpy(), step.count.cpu().numpy(), step.cu.cpu().numpy()
     assert g_cu[0] == 0 and np.array_equal(np.diff(g_cu), g_cnt)
-    sample = np.asarray(sample)
-    ref_delta = oracle.focus_importance_delta(_f64(x["q0"][sample]), _f64(x["k0"][sample]),
-                                              _f64(x["q1"][sample]), _f64(x["k1"][sample]),
-                                              x["decoded"][sample].cpu().numpy(), fc.hq, fc.hkv,
-                                              fc.pool_kernel)
-    assert_close(g_delta[sample], ref_delta, "delta")
+    ref_delta = oracle.focus_importance_delta(_f64(x["q0"]), _f64(x["k0"]), _f64(x["q1"]),
+                                              _f64(x["k1"]), x["decoded"].cpu().numpy(), fc.hq,
+                                              fc.hkv, fc.pool_kernel)
+    assert_close(g_delta, ref_delta, "delta")
     k_host = x["k"].cpu().numpy()
-    differ = selection_valid(g_idx[sample], g_cnt[sample], ref_delta, k_host[sample], fc.k_hi)
-    assert len(differ) <= max(2, len(sample) // 50), f"near-tie selections on {len(differ)} rows"
+    differ = selection_valid(g_idx, g_cnt, ref_delta, k_host, fc.k_hi)
+    assert len(differ) <= max(2, fc.batch // 50), f"near-tie selections on {len(differ)} rows"
     # Downstream of the selection: sequences whose kept set equals the oracle's own.
-    r_idx, r_cnt, _ = oracle.topk_select(ref_delta, k_host[sample], fc.k_hi)
-    hid = _bits(x["hidden_rows"][sample])
+    r_idx, r_cnt, _ = oracle.topk_select(ref_delta, k_host, fc.k_hi)
+    hid = _bits(x["hidden_rows"])
+    gathered = _bits(step.gathered)
+    blk_k, blk_v = (_bits(x[c][block_rows]).reshape(fc.batch, fc.block, -1)
+                    for c in ("cache_k", "cache_v"))
+    new_k, new_v = _bits(x["new_k"]), _bits(x["new_v"])
+    zero = np.zeros(1, np.int64)
     checked = 0
-    for si, b in enumerate(sample):
-        if si in differ:
+    for b in range(fc.batch):
+        if b in differ:
             continue
-        n_b, cub = int(r_cnt[si]), int(g_cu[b])
+        n_b, cub = int(r_cnt[b]), int(g_cu[b])
         one = np.array([n_b], np.int32)
         ocu = np.array([0, n_b], np.int32)
-        ridx = r_idx[si:si + 1]
-        # gather
-        ref_rows = oracle.gather_rows(hid[si:si + 1], ridx, one, ocu)
-        np.testing.assert_array_equal(_bits(step.gathered[cub:cub + n_b]), ref_rows)
-        # scatter (this sequence's slice of the cache)
-        ck0, cv0 = cache_k0[int(b)]
-        nk, nv = _bits(x["new_k"][cub:cub + n_b]), _bits(x["new_v"][cub:cub + n_b])
-        pre = int(kv_len[b]) - fc.block
-        rk, rv = oracle.kv_scatter(nk, nv, ridx, one, ocu, np.array([pre]), ck0, cv0)
+        ridx = r_idx[b:b + 1]
+        np.testing.assert_array_equal(gathered[cub:cub + n_b],
+                                      oracle.gather_rows(hid[b:b + 1], ridx, one, ocu))
+        rk, rv = oracle.kv_scatter(new_k[cub:cub + n_b], new_v[cub:cub + n_b], ridx, one, ocu,
+                                   zero, blk_k0[b], blk_v0[b])
+        np.testing.assert_array_equal(blk_k[b], rk)
+        np.testing.assert_array_equal(blk_v[b], rv)
+        checked += 1
+    assert checked == fc.batch - len(differ)
+    for b in attn_sample:
+        if b in differ:
+            continue
+        n_b, cub = int(r_cnt[b]), int(g_cu[b])
         r0, r1 = int(seq_start[b]), int(seq_start[b] + kv_len[b])
-        np.testing.assert_array_equal(_bits(x["cache_k"][r0:r1]), rk)
-        np.testing.assert_array_equal(_bits(x["cache_v"][r0:r1]), rv)
-        # attention of this sequence's kept rows
+        ck, cv = _bits(x["cache_k"][r0:r1]), _bits(x["cache_v"][r0:r1])
         ref_o = oracle.reduced_attention(oc.bf16_bits_to_f64(_bits(x["q_kept"][cub:cub + n_b])),
-                                         one, ocu, oc.bf16_bits_to_f64(rk), oc.bf16_bits_to_f64(rv),
+                                         np.array([n_b]), np.array([0, n_b]),
+                                         oc.bf16_bits_to_f64(ck), oc.bf16_bits_to_f64(cv),
                                          np.array([0]), np.array([kv_len[b]]), fc.hq, fc.hkv,
                                          1.0 / math.sqrt(fc.head_dim))
         assert_close(_f64(step.out[cub:cub + n_b]), ref_o, f"attention seq {b}")
-        checked += 1
-    assert checked >= len(sample) - len(differ)
     return differ
 
 
@@ -98,10 +114,10 @@ def test_chain_small_every_sequence(fused):
 
 
 @FUSED
-def test_chain_b1024_full_size_sampled(fused):
-    """The benchmarked workload itself (batch 1024, prefixes 1024..4096)."""
-    sample = sorted(np.random.default_rng(9).choice(1024, size=48, replace=False).tolist())
-    _check_chain(W.CHAIN_FOCUS_B1024, W.CHAIN_ATTN_B1024, sample, fused=fused)
+def test_chain_b1024_full_size(fused):
+    """The benchmarked workload itself (batch 1024, prefixes 1024..4096): every sequence's
+    delta, selection, gathered rows, cache rows and attention outputs."""
+    _check_chain(W.CHAIN_FOCUS_B1024, W.CHAIN_ATTN_B1024, list(range(1024)), fused=fused)
 
 
 @FUSED

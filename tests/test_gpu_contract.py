@@ -90,3 +90,42 @@ def test_checked_fused_scatter_attention(monkeypatch):
                                      g["seq_start"], g["kv_len"], ai["k_max"])
     torch.cuda.synchronize()
     assert torch.equal(ck3, g["cache_k"]) and torch.equal(cv3, g["cache_v"])
+
+
+def test_binding_rejects_wrong_index_dtypes_and_shapes():
+    """Index tensors must be int32 (an int64 tensor would be read as pairs of int32) and
+    caller-supplied outputs must have the documented shapes: ValueError before any launch."""
+    import block_token_eviction_amd as bte
+    say("binding argument checks")
+    dev = "cuda"
+    scores = torch.randn((4, 32), device=dev)
+    k = torch.full((4,), 3, dtype=torch.int32, device=dev)
+    with pytest.raises(ValueError):
+        bte.topk_select(scores, k.long(), 8)
+    with pytest.raises(ValueError):
+        bte.topk_select(scores, k, 8, idx=torch.empty((4, 4), dtype=torch.int32, device=dev))
+    with pytest.raises(ValueError):
+        bte.topk_select(scores, k, 8, cu=torch.empty((4,), dtype=torch.int32, device=dev))
+    idx, count, cu = bte.topk_select(scores, k, 8)
+    src = torch.randn((4, 32, 64), device=dev)
+    with pytest.raises(ValueError):
+        bte.gather_rows(src, idx.long(), count, cu)
+    with pytest.raises(ValueError):
+        bte.gather_rows(src, idx, count.long(), cu)
+    with pytest.raises(ValueError):
+        bte.gather_rows(src, idx, count, cu, out=torch.empty((32, 32), device=dev))
+    cache = torch.randn((200, 2, 64), device=dev)
+    new = torch.randn((32, 2, 64), device=dev)
+    rb = torch.arange(4, dtype=torch.int64, device=dev) * 40
+    with pytest.raises(ValueError):
+        bte.kv_scatter(new, new, idx, count, cu, rb.int(), cache, cache.clone())
+    with pytest.raises(ValueError):
+        bte.kv_scatter(new, new, idx, count, cu.long(), rb, cache, cache.clone())
+    q = torch.randn((32, 4, 64), device=dev)
+    kv_len = torch.full((4,), 40, dtype=torch.int32, device=dev)
+    with pytest.raises(ValueError):
+        bte.reduced_attention(q, count, cu, cache, cache, rb, kv_len.long(), 8)
+    with pytest.raises(ValueError):
+        bte.reduced_attention(q, count, cu, cache, cache, rb, kv_len, 8,
+                              out=torch.empty((32, 4, 32), device=dev))
+    torch.cuda.synchronize()

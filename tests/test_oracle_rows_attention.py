@@ -216,3 +216,23 @@ def test_paged_scatter_hand_example():
     want = cache.copy()
     want[7], want[1], want[3] = new[0], new[1], new[2]
     np.testing.assert_array_equal(k2, want)
+
+
+def test_zero_kept_rows():
+    """A sequence that keeps nothing (every position decoded): the gather writes no rows
+    and the scatter leaves the cache as it was, also when its new-row slice is empty."""
+    src = np.arange(2 * 4 * 3, dtype=np.float32).reshape(2, 4, 3)
+    idx = np.array([[-1, -1], [1, 3]], np.int32)
+    count = np.array([0, 2], np.int32)
+    cu = np.array([0, 0, 2], np.int32)
+    got = oracle.gather_rows(src, idx, count, cu)
+    np.testing.assert_array_equal(got, src[1, [1, 3]])
+    one0 = np.array([0], np.int32)
+    empty = oracle.gather_rows(src[:1], idx[:1], one0, np.array([0, 0], np.int32))
+    assert empty.shape == (0, 3)
+    cache = np.arange(6 * 3, dtype=np.float32).reshape(6, 3)
+    ck, cv = oracle.kv_scatter(np.zeros((0, 3), np.float32), np.zeros((0, 3), np.float32),
+                               idx[:1], one0, np.array([0, 0], np.int32), np.array([2]), cache,
+                               cache)
+    np.testing.assert_array_equal(ck, cache)
+    np.testing.assert_array_equal(cv, cache)
