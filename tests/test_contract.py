@@ -142,3 +142,34 @@ def test_positions():
     C.check_positions(np.array([[0, 5, 767]]), 768, "surv_pos")
     with pytest.raises(C.ContractError, match="surv_pos"):
         C.check_positions(np.array([[0, 768]]), 768, "surv_pos")
+
+
+def test_survivors():
+    """Skip-layer survivor sets: positions in range and distinct per sequence (each
+    survivor's new state is written to its own cache row); with count/cu the counts
+    within cap, cu their prefix sum and the rows inside the input."""
+    sp = np.array([[5, 6, 7], [0, 1, 9]], np.int32)
+    C.check_survivors(sp, 10)
+    with pytest.raises(C.ContractError, match="leave"):
+        C.check_survivors(np.array([[5, 6, 10]], np.int32), 10)
+    with pytest.raises(C.ContractError, match="repeat"):
+        C.check_survivors(np.array([[5, 6, 5]], np.int32), 10)
+    rows = np.array([3, 4, 8, 1, 2], np.int32)
+    cnt, cu = np.array([3, 0, 2], np.int32), np.array([0, 3, 3, 5], np.int32)
+    C.check_survivors(rows, 10, cnt, cu, cap=3, rows=5)
+    with pytest.raises(C.ContractError, match="prefix"):
+        C.check_survivors(rows, 10, cnt, np.array([0, 3, 4, 5], np.int32), cap=3, rows=5)
+    with pytest.raises(C.ContractError, match="cap"):
+        C.check_survivors(rows, 10, cnt, cu, cap=2, rows=5)
+    with pytest.raises(C.ContractError, match="exceed"):
+        C.check_survivors(rows, 10, cnt, cu, cap=3, rows=4)
+    with pytest.raises(C.ContractError, match="repeat"):
+        C.check_survivors(np.array([3, 4, 3, 1, 2], np.int32), 10, cnt, cu, cap=3, rows=5)
+
+
+def test_ragged_source():
+    idx, cnt, cu = _rows([2, 0, 3], n=4, k_max=4)
+    src_cu = np.array([0, 4, 4], np.int32)
+    C.check_ragged_source(src_cu, idx, cnt, 8)
+    with pytest.raises(C.ContractError, match="source row"):
+        C.check_ragged_source(src_cu, idx, cnt, 6)

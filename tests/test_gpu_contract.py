@@ -129,3 +129,40 @@ def test_binding_rejects_wrong_index_dtypes_and_shapes():
         bte.reduced_attention(q, count, cu, cache, cache, rb, kv_len, 8,
                               out=torch.empty((32, 4, 32), device=dev))
     torch.cuda.synchronize()
+
+
+def test_checked_es_calls_match_and_violations_raise(monkeypatch):
+    """With BTE_CHECK=1 the fused ES score/update and the ragged gather give what the
+    unchecked calls give, and repeated survivor positions or out-of-range source rows
+    raise before launching (the caches stay untouched)."""
+    import block_token_eviction_amd as bte
+    say("checked ES calls")
+    r = np.random.default_rng(71)
+    batch, L, h, cap = 3, 40, 64, 8
+    cache = torch.randn((batch, L, h), device="cuda")
+    counts = np.array([5, 0, 8], np.int32)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
+    surv = torch.from_numpy(np.concatenate([np.sort(r.choice(L, size=c, replace=False))
+                                            for c in counts]).astype(np.int32)).cuda()
+    rows = torch.randn((int(counts.sum()), h), device="cuda")
+    conf = torch.rand((batch, L), device="cuda")
+    cnt = torch.from_numpy(counts).cuda()
+    c1, c2 = cache.clone(), cache.clone()
+    plain = bte.esdllm_score_update(rows, c1, surv, conf, 0.5, count=cnt, cu=cu, cap=cap)
+    monkeypatch.setenv("BTE_CHECK", "1")
+    checked = bte.esdllm_score_update(rows, c2, surv, conf, 0.5, count=cnt, cu=cu, cap=cap)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, checked) and torch.equal(c1, c2)
+    dup = surv.clone()
+    dup[1] = dup[0]
+    c3 = cache.clone()
+    with pytest.raises(bte.contract.ContractError):
+        bte.esdllm_score_update(rows, c3, dup, conf, 0.5, count=cnt, cu=cu, cap=cap)
+    assert torch.equal(c3, cache)
+    k = torch.tensor([2, 0, 3], dtype=torch.int32, device="cuda")
+    idx, kc, kcu = bte.topk_select(plain, k, cap)
+    outs = bte.gather_rows_multi_ragged([rows, surv], cu, idx, kc, kcu)
+    torch.cuda.synchronize()
+    with pytest.raises(bte.contract.ContractError):
+        bte.gather_rows_multi_ragged([rows[:4], surv[:4]], cu, idx, kc, kcu)
+    assert outs[0].shape[0] == batch * cap
