@@ -60,6 +60,9 @@ CASES = [
     W.AttnCfg("rows_beyond_64", seed=37, batch=3, kept=20, hq=16, hkv=4, head_dim=128,
               prefix_lo=40, prefix_hi=130),
     W.AttnCfg("long", seed=38, batch=2, kept=3, hq=8, hkv=2, head_dim=128, prefix_lo=8000, prefix_hi=9000),
+    # sequences of about 131K positions: over 4,000 key tiles per item
+    W.AttnCfg("very_long", seed=39, batch=2, kept=2, hq=8, hkv=2, head_dim=128, prefix_lo=130000,
+              prefix_hi=131040),
 ]
 
 
