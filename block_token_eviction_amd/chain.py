@@ -4,7 +4,8 @@ FOCUS mode (FOCUS paper Section 4.2 and Figure 5's flow: delta from layers 0
 and 1, top-K under the budget, gather of the kept rows; then, for every later
 layer, the KV scatter and the reduced-query attention):
 
-    focus_importance_delta -> topk_select -> gather_rows -> kv_scatter -> reduced_attention
+    focus_importance_delta -> topk_select -> gather_rows -> kv_scatter
+        -> attention_order (longest first) -> reduced_attention
 
 Extended FOCUS step (FOCUS paper Section 4.1 budget, Section 4.2 selection
 with its structural constraints, Section 4.3 delayed commit; App. E.2.2 to

@@ -10,10 +10,12 @@
 // Work item: one workgroup per (sequence b, KV head g, group of 32*T query
 // rows); the group's rows are the kept tokens' G query heads that share KV
 // head g (row = token * G + head-in-group), so every K/V byte of the sequence
-// is read once per KV head. The 4 waves split the key tiles (32 keys each)
-// round-robin, each keeping a private flash-style state (reference max, sum and
-// output) and the 4 states are merged in LDS in a fixed order at the end: no
-// HBM workspace and no second launch.
+// is read once per KV head. The workgroup's waves (two, or four when there are
+// few items: waves_for) split the key tiles (32 keys each) round-robin, each
+// keeping a private flash-style state (reference max, sum and output), and the
+// states are merged in LDS in a fixed order at the end: no HBM workspace and
+// no second launch. A group of more than 64 rows splits its rows over the
+// waves instead (kQSplit).
 //
 // Per key tile: S^T = K . Q^T on the matrix cores (keys as MFMA rows fed in a
 // permuted order so that lane l owns query column l%32 and the 16 contiguous

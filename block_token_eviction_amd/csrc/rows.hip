@@ -12,8 +12,9 @@
 // so grids are sized from k_max and surplus workgroups exit at once. The
 // gather (hidden rows, 8 KB at the workloads) takes one workgroup per row;
 // the scatter (K/V rows of a few KB) treats a sequence's kept K and V rows as
-// one flat space of chunks split evenly over n_split workgroups (one per
-// sequence at large batches). All three keep a sequence's workgroups on one XCD, in order
+// one flat space of chunks split evenly over n_split workgroups (about
+// kScatterTarget in all: four per sequence at a batch of 1,024, one from a
+// batch of 4,096). All three keep a sequence's workgroups on one XCD, in order
 // (xcd_seq_part): measured 10-45 % faster than sequence-major or slot-major
 // grids, whose real rows pile up on a few XCDs or lose write locality.
 #include "bte_device.h"
