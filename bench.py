@@ -644,12 +644,12 @@ def score_resident_leg(dev, batch: int = 256, reps: int = 100):
             "frac_of_bf16_dense_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
 
 
-def graph_step_ms(step_fn, steps: int, warm_s: float = 0.3):
+def graph_step_ms(step_fn, steps: int, warm_s: float = 0.6):
     """ms per step of `steps` calls of step_fn captured as one HIP graph and replayed
     once, or None if capture fails. Before the timed replay the same graph is
     replayed back to back for at least warm_s seconds: the GPU clocks down while the
     host captures and instantiates the graph (or sits idle), and the step then runs
-    about 3 % slower for the next 0.1-0.2 s of load (measured at the batch-1,024
+    about 3 % slower for the next 0.1-0.3 s of load (measured at the batch-1,024
     step: 1,944-1,950 us per step in a replay right after capture, 1,880-1,884 us
     once warm; the attention kernel alone 1,780-1,786 against 1,715-1,725 us)."""
     import torch
