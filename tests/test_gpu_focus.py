@@ -39,6 +39,30 @@ def test_focus_b256_full_size():
     assert_close(got, ref, "focus_b256")
 
 
+# From a batch of 512 (two per workgroup) and 1,024 (four), blocks of 32 with 32 query /
+# 8 KV heads in bf16 and a pooling radius up to 3 take several sequences per workgroup,
+# the last workgroup possibly partial. Every sequence's delta must be bitwise the one a
+# workgroup per sequence gives (the same inputs in slices of 256 sequences, which take
+# that path) and match the oracle.
+@pytest.mark.parametrize("batch,pool", [(513, 7), (1024, 3), (1027, 7), (1025, 1), (1026, 5)])
+def test_focus_sequences_per_workgroup(batch, pool):
+    bte = _bte()
+    cfg = W.FocusCfg("multi", seed=41, batch=batch, block=32, pool_kernel=pool, hidden=64)
+    fi = W.focus_inputs(cfg)
+    g = dev(fi)
+    say(f"focus several sequences per workgroup: batch={batch} pool={pool}")
+    out = bte.focus_importance_delta(g["q0"], g["k0"], g["q1"], g["k1"], g["decoded"], pool)
+    parts = [bte.focus_importance_delta(g["q0"][i:i + 256], g["k0"][i:i + 256], g["q1"][i:i + 256],
+                                        g["k1"][i:i + 256], g["decoded"][i:i + 256], pool)
+             for i in range(0, batch, 256)]
+    torch.cuda.synchronize()
+    assert torch.equal(out, torch.cat(parts))
+    f64 = W.to_f64
+    ref = oracle.focus_importance_delta(f64(fi["q0"]), f64(fi["k0"]), f64(fi["q1"]), f64(fi["k1"]),
+                                        fi["decoded"].numpy(), cfg.hq, cfg.hkv, pool)
+    assert_close(out.cpu().numpy(), ref, f"multi {batch}")
+
+
 CASES = [
     # block, hq, hkv, head_dim, pool, dtype
     (32, 32, 8, 128, 3, W.BF16),
