@@ -53,6 +53,30 @@ constexpr int kStreamPolicy = 2;
 // Compute units of an MI355X (256 over 8 XCDs).
 constexpr int kCUs = 256;
 
+// Sequences per workgroup (1, 2 or 4) for the static-tile kernels below, which
+// run one workgroup per CU: the choice with the least modelled time, i.e.
+// rounds of kCUs workgroups x sequences each workgroup streams x the measured
+// cost per sequence (1, 0.92 and 0.89 for 1, 2 and 4 per workgroup: 118.9,
+// 109.6 and 105.3 us at batch 1,024). A grid just past a multiple of kCUs
+// leaves a last round of few workgroups, each as long as a whole round:
+// batch 1,027 at 4 per workgroup (257 workgroups) measured 340 us against
+// 246 us at one per workgroup, for the 64-key kernel.
+inline int seqs_per_workgroup(int batch) {
+  constexpr int kSeqs[3] = {1, 2, 4};
+  constexpr int kCost[3] = {100, 92, 89};
+  int best = 1;
+  long best_cost = -1;
+  for (int i = 0; i < 3; ++i) {
+    const long wgs = (batch + kSeqs[i] - 1) / kSeqs[i];
+    const long cost = (wgs + kCUs - 1) / kCUs * kSeqs[i] * kCost[i];
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = kSeqs[i];
+    }
+  }
+  return best;
+}
+
 // This lane's MFMA operand: half h of one tile row, as kHalf 16-byte chunks.
 template <int D, bool BF16>
 struct HalfRow {
@@ -230,9 +254,9 @@ __device__ __forceinline__ void issue_tile(const char* __restrict__ q0, const ch
 // workgroup per CU streams without rounds of workgroups starting and ending.
 // Measured at batch 1,024, outputs bitwise equal: 118.9 us with one sequence
 // per workgroup, 109.6 with two, 105.3 with four (256 workgroups), 145.9 with
-// eight (128 workgroups: half the CUs idle). A last workgroup with fewer
-// sequences repeats its last one (reads only, no second write), so the tile
-// sequence stays fixed at compile time.
+// eight (128 workgroups: half the CUs idle); seqs_per_workgroup picks the
+// number. A last workgroup with fewer sequences repeats its last one (reads
+// only, no second write), so the tile sequence stays fixed at compile time.
 template <int D, bool BF16, int R, int kWaves, bool kFull, int kG, int kSeqs = 1>
 __global__ __launch_bounds__(64 * kWaves) void focus_delta_kernel(
     const char* __restrict__ q0, const char* __restrict__ k0, const char* __restrict__ q1,
@@ -496,11 +520,12 @@ __device__ __forceinline__ void issue_tile_wide(const char* __restrict__ q,
 
 // kFull: B = 64 at compile time. kG > 0: kG query heads per KV head and one
 // group per wave (hkv == kWaves), so the tile sequence is static and unrolled.
-template <int D, bool BF16, int R, int kWaves, bool kFull, int kG>
+template <int D, bool BF16, int R, int kWaves, bool kFull, int kG, int kSeqs = 1>
 __global__ __launch_bounds__(64 * kWaves) void focus_delta_wide_kernel(
     const char* __restrict__ q0, const char* __restrict__ k0, const char* __restrict__ q1,
     const char* __restrict__ k1, const uint8_t* __restrict__ decoded, float* __restrict__ out,
-    int B, int hq, int hkv, int rt_r, float c) {
+    int batch, int B, int hq, int hkv, int rt_r, float c) {
+  static_assert(kSeqs == 1 || kG > 0, "several sequences per workgroup need the static tiles");
   if constexpr (kFull) B = 64;
   if constexpr (kG > 0) {
     hkv = kWaves;
@@ -514,9 +539,13 @@ __global__ __launch_bounds__(64 * kWaves) void focus_delta_wide_kernel(
   // The 32-key kernel keeps two (one measured 4-5 % slower at batches 256 and 512).
   constexpr int kStages = 1;
   __shared__ __attribute__((aligned(16))) char ring[kWaves * kStages * Tl::kBytes];
-  __shared__ float red[kWaves][2][64];
+  // per-wave column sums of a sequence; two buffers when sequences follow one another
+  __shared__ float red[kSeqs > 1 ? 2 : 1][kWaves][2][64];
 
-  const int b = blockIdx.x;
+  // As in the 32-key kernel: kSeqs consecutive sequences per workgroup, a last
+  // partial workgroup repeating its last one.
+  const int b0 = blockIdx.x * kSeqs;
+  auto seq = [&](int s) { return b0 + s < batch ? b0 + s : batch - 1; };
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31;
@@ -530,19 +559,23 @@ __global__ __launch_bounds__(64 * kWaves) void focus_delta_wide_kernel(
   const int ngroups = kG > 0 ? 1 : (hkv - w + kWaves - 1) / kWaves;
   const int per_layer = 2 + 2 * G;
   const int per_group = 2 * per_layer;
-  const int ntiles = ngroups * per_group;
+  const int ntiles = kSeqs * ngroups * per_group;
   const int lrow = lane / Tl::kChunks;
   const int lslot = lane % Tl::kChunks;
   float acc[32];
 #pragma unroll
   for (int r = 0; r < 32; ++r) acc[r] = 0.f;
 
+  // Tile `tile` of the stream: group gi of sequence 0 (kSeqs == 1), or the one
+  // group of sequence gi (kSeqs > 1).
   auto issue = [&](int tile, int stage) __attribute__((always_inline)) {
     const int gi = tile / per_group;
     const int t = tile - gi * per_group;
     const int l = t >= per_layer;
-    issue_tile_wide<D, BF16>(l ? q1 : q0, l ? k1 : k0, b, B, hq, hkv, w + gi * kWaves,
-                             t - l * per_layer, wring + stage * Tl::kBytes, lrow, lslot);
+    const int bs = kSeqs > 1 ? seq(gi) : b0;
+    const int g = kSeqs > 1 ? w : w + gi * kWaves;
+    issue_tile_wide<D, BF16>(l ? q1 : q0, l ? k1 : k0, bs, B, hq, hkv, g, t - l * per_layer,
+                             wring + stage * Tl::kBytes, lrow, lslot);
   };
   Row KA, KB;
   if (ntiles > 0) issue(0, 0);
@@ -596,33 +629,45 @@ __global__ __launch_bounds__(64 * kWaves) void focus_delta_wide_kernel(
 #pragma unroll
         for (int x = 1; x < 32; x <<= 1) acc[r] += __shfl_xor(acc[r], x, kWave);
       }
+      // (kSeqs > 1: buffer gi & 1 for sequence gi; it was last read before the
+      // previous sequence's barrier, which every wave has passed)
       if (n == 0) {
+        const bool first = kSeqs > 1 || gi == 0;
 #pragma unroll
         for (int r = 0; r < 32; ++r) {
-          float* slot = &red[w][l][32 * h + r];
-          *slot = gi == 0 ? acc[r] : *slot + acc[r];
+          float* slot = &red[kSeqs > 1 ? (gi & 1) : 0][w][l][32 * h + r];
+          *slot = first ? acc[r] : *slot + acc[r];
         }
       }
 #pragma unroll
       for (int r = 0; r < 32; ++r) acc[r] = 0.f;
     }
   };
+  // Sequence s's delta from the waves' column sums in LDS (fixed order).
+  auto finish = [&](int s) __attribute__((always_inline)) {
+    __syncthreads();
+    if (threadIdx.x < B && b0 + s < batch) {
+      const int j = threadIdx.x;
+      const int b = b0 + s;
+      float(&rb)[kWaves][2][64] = red[kSeqs > 1 ? (s & 1) : 0];
+      float i0 = 0.f, i1 = 0.f;
+      for (int v = 0; v < kWaves; ++v) {
+        i0 += rb[v][0][j];
+        i1 += rb[v][1][j];
+      }
+      out[(size_t)b * B + j] = decoded[(size_t)b * B + j] ? -INFINITY : i1 - i0;
+    }
+  };
   if constexpr (kG > 0) {
 #pragma unroll
-    for (int tile = 0; tile < 2 * (2 + 2 * kG); ++tile) step(tile);
+    for (int sq = 0; sq < kSeqs; ++sq) {
+#pragma unroll
+      for (int t = 0; t < 2 * (2 + 2 * kG); ++t) step(sq * 2 * (2 + 2 * kG) + t);
+      finish(sq);
+    }
   } else {
     for (int tile = 0; tile < ntiles; ++tile) step(tile);
-  }
-
-  __syncthreads();
-  if (threadIdx.x < B) {
-    const int j = threadIdx.x;
-    float i0 = 0.f, i1 = 0.f;
-    for (int v = 0; v < kWaves; ++v) {
-      i0 += red[v][0][j];
-      i1 += red[v][1][j];
-    }
-    out[(size_t)b * B + j] = decoded[(size_t)b * B + j] ? -INFINITY : i1 - i0;
+    finish(0);
   }
 }
 
@@ -630,22 +675,40 @@ template <int D, bool BF16, int R, int kWaves>
 hipError_t launch_wide_w(const void* q0, const void* k0, const void* q1, const void* k1,
                          const uint8_t* decoded, float* out, int batch, int B, int hq, int hkv,
                          int rt_r, float c, hipStream_t stream) {
+  const char *a0 = (const char*)q0, *a1 = (const char*)k0, *a2 = (const char*)q1,
+             *a3 = (const char*)k1;
   if constexpr (kWaves == 8 && R >= 0) {
     if (B == 64 && hkv == 8 && hq == 32) {
+      // Sequences per workgroup as in the 32-key kernel (bf16 only).
+      if constexpr (BF16) {
+        const int per_wg = seqs_per_workgroup(batch);
+        if (per_wg == 4) {
+          hipLaunchKernelGGL((focus_delta_wide_kernel<D, BF16, R, kWaves, true, 4, 4>),
+                             dim3((batch + 3) / 4), dim3(64 * kWaves), 0, stream, a0, a1, a2, a3,
+                             decoded, out, batch, B, hq, hkv, rt_r, c);
+          return hipGetLastError();
+        }
+        if (per_wg == 2) {
+          hipLaunchKernelGGL((focus_delta_wide_kernel<D, BF16, R, kWaves, true, 4, 2>),
+                             dim3((batch + 1) / 2), dim3(64 * kWaves), 0, stream, a0, a1, a2, a3,
+                             decoded, out, batch, B, hq, hkv, rt_r, c);
+          return hipGetLastError();
+        }
+      }
       hipLaunchKernelGGL((focus_delta_wide_kernel<D, BF16, R, kWaves, true, 4>), dim3(batch),
-                         dim3(64 * kWaves), 0, stream, (const char*)q0, (const char*)k0,
-                         (const char*)q1, (const char*)k1, decoded, out, B, hq, hkv, rt_r, c);
+                         dim3(64 * kWaves), 0, stream, a0, a1, a2, a3, decoded, out, batch, B, hq,
+                         hkv, rt_r, c);
       return hipGetLastError();
     }
   }
   if (B == 64)
     hipLaunchKernelGGL((focus_delta_wide_kernel<D, BF16, R, kWaves, true, 0>), dim3(batch),
-                       dim3(64 * kWaves), 0, stream, (const char*)q0, (const char*)k0,
-                       (const char*)q1, (const char*)k1, decoded, out, B, hq, hkv, rt_r, c);
+                       dim3(64 * kWaves), 0, stream, a0, a1, a2, a3, decoded, out, batch, B, hq,
+                       hkv, rt_r, c);
   else
     hipLaunchKernelGGL((focus_delta_wide_kernel<D, BF16, R, kWaves, false, 0>), dim3(batch),
-                       dim3(64 * kWaves), 0, stream, (const char*)q0, (const char*)k0,
-                       (const char*)q1, (const char*)k1, decoded, out, B, hq, hkv, rt_r, c);
+                       dim3(64 * kWaves), 0, stream, a0, a1, a2, a3, decoded, out, batch, B, hq,
+                       hkv, rt_r, c);
   return hipGetLastError();
 }
 
@@ -657,17 +720,17 @@ hipError_t launch_w(const void* q0, const void* k0, const void* q1, const void* 
              *a3 = (const char*)k1;
   if constexpr (kWaves == 8) {
     if (B == 32 && hkv == 8 && hq == 32) {
-      // Sequences per workgroup: the most (up to 4) that still leave a
-      // workgroup for every CU. bf16 with a compile-time radius only: the
-      // runtime-radius and fp32 variants would spill registers.
+      // Several sequences per workgroup in bf16 with a compile-time radius
+      // only: the runtime-radius and fp32 variants would spill registers.
       if constexpr (BF16 && R >= 0) {
-        if (batch >= 4 * kCUs) {
+        const int per_wg = seqs_per_workgroup(batch);
+        if (per_wg == 4) {
           hipLaunchKernelGGL((focus_delta_kernel<D, BF16, R, kWaves, true, 4, 4>),
                              dim3((batch + 3) / 4), dim3(64 * kWaves), 0, stream, a0, a1, a2, a3,
                              decoded, out, batch, B, hq, hkv, rt_r, c);
           return hipGetLastError();
         }
-        if (batch >= 2 * kCUs) {
+        if (per_wg == 2) {
           hipLaunchKernelGGL((focus_delta_kernel<D, BF16, R, kWaves, true, 4, 2>),
                              dim3((batch + 1) / 2), dim3(64 * kWaves), 0, stream, a0, a1, a2, a3,
                              decoded, out, batch, B, hq, hkv, rt_r, c);

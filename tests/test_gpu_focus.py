@@ -39,18 +39,21 @@ def test_focus_b256_full_size():
     assert_close(got, ref, "focus_b256")
 
 
-# From a batch of 512 (two per workgroup) and 1,024 (four), blocks of 32 with 32 query /
-# 8 KV heads in bf16 and a pooling radius up to 3 take several sequences per workgroup,
-# the last workgroup possibly partial. Every sequence's delta must be bitwise the one a
-# workgroup per sequence gives (the same inputs in slices of 256 sequences, which take
-# that path) and match the oracle.
-@pytest.mark.parametrize("batch,pool", [(513, 7), (1024, 3), (1027, 7), (1025, 1), (1026, 5)])
-def test_focus_sequences_per_workgroup(batch, pool):
+# Blocks of 32 or 64 with 32 query / 8 KV heads in bf16 and a pooling radius up to 3 take
+# several sequences per workgroup at large batches: 2 per workgroup at batches 257-512,
+# 4 at 1,000-1,024 (the launch's cost model), the last workgroup possibly partial (511:
+# one sequence in it; 1,021-1,023: one to three); 1,027 takes one per workgroup. Every
+# sequence's delta must be bitwise the one a workgroup per sequence gives (the same
+# inputs in slices of 256 sequences, which take that path) and match the oracle.
+@pytest.mark.parametrize("batch,pool,block", [(511, 7, 32), (1024, 3, 32), (1021, 7, 32),
+                                              (1022, 1, 32), (1023, 5, 32), (1027, 7, 32),
+                                              (511, 3, 64), (1021, 7, 64)])
+def test_focus_sequences_per_workgroup(batch, pool, block):
     bte = _bte()
-    cfg = W.FocusCfg("multi", seed=41, batch=batch, block=32, pool_kernel=pool, hidden=64)
+    cfg = W.FocusCfg("multi", seed=41, batch=batch, block=block, pool_kernel=pool, hidden=64)
     fi = W.focus_inputs(cfg)
     g = dev(fi)
-    say(f"focus several sequences per workgroup: batch={batch} pool={pool}")
+    say(f"focus several sequences per workgroup: batch={batch} pool={pool} block={block}")
     out = bte.focus_importance_delta(g["q0"], g["k0"], g["q1"], g["k1"], g["decoded"], pool)
     parts = [bte.focus_importance_delta(g["q0"][i:i + 256], g["k0"][i:i + 256], g["q1"][i:i + 256],
                                         g["k1"][i:i + 256], g["decoded"][i:i + 256], pool)
