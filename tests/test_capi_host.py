@@ -275,3 +275,38 @@ def test_gather_rows_multi_ragged_errors():
     assert f(arr, 1, None, FAKE, FAKE, FAKE, 4, 8, None) == NULL
     assert f(arr, 0, FAKE, FAKE, FAKE, FAKE, 4, 8, None) == DIM
     assert f(arr, 1, FAKE, FAKE, FAKE, FAKE, 0, 8, None) == DIM
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/bte.h compiles as C99 on its own (gcc, no C++ and no torch), every declared
+    entry point links against libbte.so, and a C caller gets the documented host-side
+    status codes without a GPU."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not installed")
+    names = declared()
+    src = tmp_path / "caller.c"
+    src.write_text(
+        "#include <stdio.h>\n#include \"bte.h\"\n"
+        "int main(void) {\n"
+        "  void* const entry[] = {\n" + "".join(f"    (void*){n},\n" for n in names) + "  };\n"
+        "  size_t i;\n"
+        "  for (i = 0; i < sizeof(entry) / sizeof(entry[0]); ++i) if (!entry[i]) return 10;\n"
+        "  if (bte_version() < 100) return 11;\n"
+        "  if (bte_topk_select(NULL, NULL, NULL, NULL, NULL, 1, 1, 1, NULL) != BTE_ERR_NULL) return 12;\n"
+        "  if (bte_esdllm_score((void*)16, (void*)16, (int32_t*)16, (float*)16, 0.5f, (float*)16,\n"
+        "                       0, 1, 1, 8, BTE_BF16, NULL) != BTE_ERR_DIM) return 13;\n"
+        "  printf(\"%s\\n\", bte_status_string(BTE_ERR_DIM));\n"
+        "  return 0;\n}\n")
+    libdir = os.path.join(ROOT, "block_token_eviction_amd")
+    exe = tmp_path / "caller"
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror=implicit-function-declaration",
+           "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+           str(src), "-L", libdir, "-lbte", f"-Wl,-rpath,{libdir}", "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, (r.returncode, r.stderr[-2000:])
+    assert r.stdout.strip() == bte.status_string(DIM)
