@@ -533,10 +533,11 @@ __global__ __launch_bounds__(64 * kWaves) void focus_delta_wide_kernel(
   }
   using Tl = Tile<D, BF16>;
   using Row = HalfRow<D, BF16>;
-  // One LDS stage per wave (a 68 KB ring at eight waves, so two workgroups fit a CU).
-  // Measured at batch 1,024, block 64, in one process on three boxes: 214.8 / 219.1 /
+  // One LDS stage per wave (a 64 KB ring at eight waves). Measured at batch 1,024,
+  // block 64, one sequence per workgroup, in one process on three boxes: 214.8 / 219.1 /
   // 223.3 us against 220.0 / 224.4 / 224.4 us with two stages (outputs bitwise equal).
-  // The 32-key kernel keeps two (one measured 4-5 % slower at batches 256 and 512).
+  // With several sequences per workgroup two stages would spill registers. The 32-key
+  // kernel keeps two (one measured 4-5 % slower at batches 256 and 512).
   constexpr int kStages = 1;
   __shared__ __attribute__((aligned(16))) char ring[kWaves * kStages * Tl::kBytes];
   // per-wave column sums of a sequence; two buffers when sequences follow one another
