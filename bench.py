@@ -19,6 +19,7 @@ Other legs, each reported under its own key:
   focus_b256           FOCUS scoring at batch 256 (delta -> top-K -> gather),
   attn_b256            KV scatter -> order -> attention at batch 256,
   focus_b1024_block64  the scoring path with blocks of 64 positions,
+  focus_b2048_block16  the scoring path with blocks of 16 positions,
   es_mode              ES-dLLM score -> top-K -> gather -> KV scatter, batch 8,
   es_pipeline          two ES-dLLM skip layers (256 -> 128 -> 64 survivors),
   es_iteration         ES-dLLM iterations with the device bookkeeping and a
@@ -51,7 +52,8 @@ PAGE = 64                      # KV pool page size (rows) of the extended step
 FLUSH_BYTES = 1 << 30          # read before each timed iteration of the flushed legs
 LEG_ITERS = 30                 # timed iterations of each flushed leg
 METRIC = "block tokens/s through score→top-K→gather→reduced attn; % of HBM/MFMA roofline"
-LEGS = ["focus_b256", "attn_b256", "focus_b1024_block64", "es_mode", "es_pipeline",
+LEGS = ["focus_b256", "attn_b256", "focus_b1024_block64", "focus_b2048_block16", "es_mode",
+        "es_pipeline",
         "es_iteration", "fused_scatter_attention", "full_step", "score_resident"]
 
 
@@ -183,6 +185,7 @@ def main():
         "focus_b256": lambda: focus_b256_leg(dev, flush),
         "attn_b256": lambda: attn_b256_leg(dev, flush),
         "focus_b1024_block64": lambda: focus_block64_leg(dev, flush),
+        "focus_b2048_block16": lambda: focus_block16_leg(dev, flush),
         "es_mode": lambda: es_mode_leg(dev, flush, args.steps),
         "es_pipeline": lambda: es_pipeline_leg(dev, flush, args.steps),
         "es_iteration": lambda: es_iteration_leg(dev, flush),
@@ -378,15 +381,14 @@ def attn_b256_leg(dev, flush):
             "kernels": leg_kernels(per, bytes_, flops)}
 
 
-def focus_block64_leg(dev, flush):
-    """The scoring path with blocks of 64 positions (the FOCUS paper's largest block):
-    batch 1024, 32q/8kv heads, head dim 128, bf16, MaxPool 7, K ~ U{8..24} (the batch-256
-    budget range scaled with the block), hidden 4096: delta -> top-K -> gather."""
-    import torch
+def focus_block_leg(dev, flush, batch: int, block: int, k_lo: int, k_hi: int, seed: int):
+    """The scoring path at another block size: delta -> top-K -> gather, 32q/8kv heads,
+    head dim 128, bf16, MaxPool 7, hidden 4096, K ~ U{k_lo..k_hi}."""
     from block_token_eviction_amd.chain import FocusStep
     import workloads as W
 
-    cfg = W.FocusCfg("focus_b1024_block64", seed=6, batch=1024, block=64, k_lo=8, k_hi=24)
+    name = f"focus_b{batch}_block{block}"
+    cfg = W.FocusCfg(name, seed=seed, batch=batch, block=block, k_lo=k_lo, k_hi=k_hi)
     fi = W.focus_inputs(cfg, device=dev)
     st = FocusStep(cfg.batch, cfg.block, cfg.hidden, cfg.hq, cfg.head_dim, cfg.k_hi, cfg.dtype, dev)
     stages = [
@@ -402,14 +404,27 @@ def focus_block64_leg(dev, flush):
               "gather_rows": 2 * sum_k * cfg.hidden * 2}
     flops = {"focus_importance_delta": score_flops(n, B, cfg.hq, cfg.head_dim)}
     med = percentile(step, 50)
-    res = {"workload": "focus_b1024_block64 (batch 1024, block 64, 32q/8kv heads, head dim 128, "
-                       "bf16, MaxPool 7, K ~ U{8..24}, hidden 4096)", "timing": FLUSHED,
+    res = {"workload": f"{name} (batch {batch}, block {block}, 32q/8kv heads, head dim 128, "
+                       f"bf16, MaxPool 7, K ~ U{{{k_lo}..{k_hi}}}, hidden 4096)", "timing": FLUSHED,
            "kept_rows": sum_k,
            "ms_per_step_p10_p50_p90": [round(percentile(step, q), 4) for q in (10, 50, 90)],
            "block tokens/s": round(n * B / (med * 1e-3), 1),
            "kernels": leg_kernels(per, bytes_, flops)}
     del fi
     return res
+
+
+def focus_block64_leg(dev, flush):
+    """Blocks of 64 positions (the FOCUS paper's largest block) at batch 1024; K ~ U{8..24},
+    the batch-256 budget range scaled with the block."""
+    return focus_block_leg(dev, flush, 1024, 64, 8, 24, seed=6)
+
+
+def focus_block16_leg(dev, flush):
+    """Blocks of 16 positions (the FOCUS paper's smallest block) at batch 2048, the same
+    bytes as the main step's delta; K ~ U{2..6}, the budget range scaled with the block.
+    The delta runs the blocks in pairs as blocks of 32."""
+    return focus_block_leg(dev, flush, 2048, 16, 2, 6, seed=7)
 
 
 def es_mode_leg(dev, flush, steps: int):

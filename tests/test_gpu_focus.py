@@ -66,6 +66,60 @@ def test_focus_sequences_per_workgroup(batch, pool, block):
     assert_close(out.cpu().numpy(), ref, f"multi {batch}")
 
 
+# Blocks of 16 run in pairs as blocks of 32 (the same memory), the two kept apart by a mask;
+# an odd last block runs on its own. Batches 2-7 (one to three pairs, odd and even), 512 and
+# 1,024 (two and four pairs per workgroup at the 32/8-head shape), pools up to the whole row
+# and a runtime radius wider than the block, other head shapes, fp32.
+PAIR_CASES = [
+    # batch, hq, hkv, head_dim, pool, dtype
+    (2, 32, 8, 128, 7, W.BF16),
+    (7, 32, 8, 128, 7, W.BF16),
+    (5, 32, 8, 128, 1, W.BF16),
+    (6, 32, 8, 128, 31, W.BF16),      # window covers the whole block
+    (3, 32, 8, 128, 41, W.BF16),      # runtime radius 20, wider than the block
+    (4, 8, 2, 64, 5, W.BF16),         # waves loop over nothing: runtime group count
+    (5, 16, 16, 128, 3, W.BF16),      # more KV heads than waves
+    (3, 8, 8, 128, 7, W.F32),
+    (512, 32, 8, 128, 7, W.BF16),
+    (1024, 32, 8, 128, 7, W.BF16),
+    (1025, 32, 8, 128, 3, W.BF16),
+]
+
+
+@pytest.mark.parametrize("case", PAIR_CASES, ids=[str(c[:5]) for c in PAIR_CASES])
+def test_blocks_of_16_in_pairs(case):
+    batch, hq, hkv, D, pool, dt = case
+    cfg = W.FocusCfg("pairs", seed=17, batch=batch, block=16, hq=hq, hkv=hkv, head_dim=D,
+                     dtype=dt, pool_kernel=pool, hidden=64)
+    got, ref, _ = _run(cfg)
+    assert_close(got, ref, str(case))
+
+
+def test_blocks_of_16_spike_at_the_pair_edge():
+    """The spike closed form of a block of 16 with the spike at its last position, whose
+    pooling window would reach into the paired block: the neighbour block (spike-free,
+    uniform) must stay exactly uniform, and the spiked block must follow the closed form
+    with the window cut at the block's edge."""
+    bte = _bte()
+    B, hq, D = 16, 4, 64
+    q0 = torch.zeros((4, B, hq, D))
+    k0 = torch.randn((4, B, hq, D), generator=torch.Generator().manual_seed(3))
+    q1 = torch.zeros((4, B, hq, D)); q1[..., 0] = 1.0
+    k1 = torch.zeros((4, B, hq, D)); k1[0, 15, :, 0] = 5.5; k1[3, 0, :, 0] = 5.5
+    dec = torch.zeros((4, B), dtype=torch.uint8)
+    say("focus spike, blocks of 16 in pairs")
+    got = bte.focus_importance_delta(q0.cuda(), k0.cuda(), q1.cuda(), k1.cuda(), dec.cuda(), 7).cpu().numpy()
+    es = np.exp(5.5 / 8.0)
+    for b, p in ((0, 15), (3, 0)):
+        nw = min(B - 1, p + 3) - max(0, p - 3) + 1
+        den = nw * es + (B - nw)
+        win = np.zeros(B, bool); win[max(0, p - 3):min(B - 1, p + 3) + 1] = True
+        want = np.where(win, hq * (B * es / den - 1.0), hq * (B / den - 1.0))
+        np.testing.assert_allclose(got[b], want, rtol=2e-2, atol=1e-3)
+    # blocks 1 and 2 (each paired with a spiked block) have identical layers: exactly +0.0
+    assert np.all(got[1] == 0.0) and np.all(got[2] == 0.0)
+
+
 CASES = [
     # block, hq, hkv, head_dim, pool, dtype
     (32, 32, 8, 128, 3, W.BF16),
