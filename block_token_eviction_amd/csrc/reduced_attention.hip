@@ -14,8 +14,10 @@
 // few items: waves_for) split the key tiles (32 keys each) round-robin, each
 // keeping a private flash-style state (reference max, sum and output), and the
 // states are merged in LDS in a fixed order at the end: no HBM workspace and
-// no second launch. A group of more than 64 rows splits its rows over the
-// waves instead (kQSplit).
+// no second launch. When a sequence may have more than 64 rows per KV head,
+// four-wave workgroups over 128-row groups split the rows instead (kQSplit):
+// each wave holds 32 of them and sees every key tile, which the waves copy
+// into one shared LDS ring.
 //
 // Per key tile: S^T = K . Q^T on the matrix cores (keys as MFMA rows fed in a
 // permuted order so that lane l owns query column l%32 and the 16 contiguous
@@ -58,6 +60,9 @@ struct Cfg {
   static constexpr int kStageBytes = 2 * kTile;
   static constexpr int kStage = kWaves * kStages * kStageBytes;
   static constexpr int kLds = kStage > kMerge ? kStage : kMerge;
+  // Query split: the workgroup's waves share one ring of kRing stages.
+  static constexpr int kRing = 4;
+  static constexpr int kRingLds = kRing * kStageBytes > kMerge ? kRing * kStageBytes : kMerge;
 };
 
 // LDS placement of 16-byte chunk `c` of tile row `row`. K tiles: rows that the
@@ -208,10 +213,10 @@ constexpr int kPageCache = 2048;
 // One workgroup's work: sequence b, KV head g, the T 32-row query tiles from
 // row0 on (each holding at least one real row).
 // kQSplit = false: the waves share the query rows and take every kWaves-th key
-// tile, their states merged at the end. kQSplit = true: wave w takes the 32*T
-// query rows from row0 + 32*T*w and every key tile (each wave streams the same
-// K/V through its own LDS stages, side by side on one CU, so the second read of
-// a tile is mostly an L2 hit instead of a second pass over HBM).
+// tile, their states merged at the end. kQSplit = true (four waves): wave w
+// takes the 32*T query rows from row0 + 32*T*w and every key tile; the tiles
+// go through one LDS ring shared by the waves, so each K/V byte is copied from
+// HBM once per workgroup.
 // kScatter: the KV positions [pb, pb + sc.n) may hold kept rows; bit j of
 // `kept` marks block index j (position pb + j) as kept.
 template <int D, bool BF16, int T, int kWaves, int kPaged, bool kQSplit, bool kScatter>
@@ -281,7 +286,21 @@ __device__ __forceinline__ void attn_body(
 
   const int ntiles = (L + 31) / 32;
   const int kj = 16 * ((n >> 2) & 1) + (n & 3) + 4 * (n >> 3);   // key fed as MFMA row n
-  char* wave_lds = smem + w * C::kStages * C::kStageBytes;         // this wave's stages
+  // Query split: the waves use the same key tiles, so they share one ring of
+  // C::kRing stages; of every tile, wave w copies half w % 2 of the copies of
+  // the K (w < 2) or V (w >= 2) tile. Key split: each wave has its own kStages
+  // stages.
+  constexpr bool kShared = kQSplit;
+  static_assert(!kShared || (kWaves == 4 && BF16), "the shared ring takes four bf16 waves");
+  constexpr int kParts = kShared ? 2 : 1;               // waves per tile half
+  constexpr int kRing = kShared ? C::kRing : C::kStages;
+  constexpr int kPer = C::kHalf / kParts;               // copies per wave and tile (shared ring)
+  const int my_half = kShared ? w / kParts : 0;
+  const int my_part = kShared ? w % kParts : 0;
+  // A query-split wave whose rows all lie past the end copies and waits with
+  // the others but computes nothing.
+  const bool active = !kQSplit || qrow0 < rows;
+  char* wave_lds = kShared ? smem : smem + w * C::kStages * C::kStageBytes;
 
   // Tile loads go straight from HBM into LDS (16 bytes per lane, no registers):
   // load i of a tile fills the 1 KB at i*1024, lane l writing byte 16*l of it, i.e.
@@ -343,7 +362,7 @@ __device__ __forceinline__ void attn_body(
   // trow = tile_row(kt) when tile_in_page. A full tile's copies each cover kRpi
   // consecutive rows that share one page (pages hold a multiple of kRpi rows),
   // so each copy has a wave-uniform base.
-  auto issue_half = [&](int kt, int stage, int which, size_t trow) {
+  auto issue_half = [&](int kt, int stage, int which, size_t trow, int part) {
     char* dst = wave_lds + stage * C::kStageBytes + which * C::kTile;
     const char* base = which ? vbase : kbase;
     if (kScatter && in_block(kt)) {
@@ -353,7 +372,8 @@ __device__ __forceinline__ void attn_body(
       const char* nbase = (which ? sc.new_v : sc.new_k) + (size_t)g * C::kRowBytes;
       const int last = L - 1 - kt * 32;
 #pragma unroll
-      for (int i = 0; i < C::kHalf; ++i) {
+      for (int u = 0; u < C::kHalf / kParts; ++u) {
+        const int i = part * (C::kHalf / kParts) + u;
         const int row = C::kRpi * i + lrow;
         const int p = kt * 32 + (row < last ? row : last);
         const int j = p - pb;
@@ -365,7 +385,8 @@ __device__ __forceinline__ void attn_body(
       }
     } else if (kt * 32 + 32 <= L) {
 #pragma unroll
-      for (int i = 0; i < C::kHalf; ++i) {
+      for (int u = 0; u < C::kHalf / kParts; ++u) {
+        const int i = part * (C::kHalf / kParts) + u;
         const int row = C::kRpi * i + lrow;
         const size_t first = tile_in_page ? trow + C::kRpi * i : kv_pos_row(kt * 32 + C::kRpi * i);
         const size_t row_base = first * kv_row;                            // wave-uniform
@@ -377,7 +398,8 @@ __device__ __forceinline__ void attn_body(
       // They get probability 0 below and a finite V row.
       const int last = L - 1 - kt * 32;
 #pragma unroll
-      for (int i = 0; i < C::kHalf; ++i) {
+      for (int u = 0; u < C::kHalf / kParts; ++u) {
+        const int i = part * (C::kHalf / kParts) + u;
         const int row = C::kRpi * i + lrow;
         const size_t prow = kv_pos_row(kt * 32 + (row < last ? row : last));
         const int chunk = which ? vpos(row, lslot) : kpos(row, lslot);
@@ -387,8 +409,8 @@ __device__ __forceinline__ void attn_body(
   };
   auto issue_tile = [&](int kt, int stage) {
     const size_t trow = tile_in_page ? tile_row(kt) : 0;
-    issue_half(kt, stage, 0, trow);
-    issue_half(kt, stage, 1, trow);
+    issue_half(kt, stage, 0, trow, 0);
+    issue_half(kt, stage, 1, trow, 0);
   };
 
   // Lane part of the V^T transposing reads: k-slot (h, t) of P.V MFMA cc is
@@ -409,7 +431,17 @@ __device__ __forceinline__ void attn_body(
   // them complete and puts no wait for them into the tile loop, where it would
   // have to wait for every copy in flight.
   static_assert(C::kStages * 2 * C::kHalf <= 63, "vmcnt holds at most 63");
-  if (kt0 < ntiles) {
+  static_assert((kRing - 1) * kPer <= 63, "vmcnt holds at most 63");
+  if (kShared && ntiles > 0) {
+    // Shared ring: this wave's part of tiles 0 .. kRing - 2 (repeating the last
+    // tile past the end, into stages the loop does not read).
+#pragma unroll
+    for (int st = 0; st + 1 < kRing; ++st) {
+      const int kt = min(st, ntiles - 1);
+      issue_half(kt, st, my_half, tile_in_page ? tile_row(kt) : 0, my_part);
+    }
+    __builtin_amdgcn_s_waitcnt(kVmcntNoLgkm | vmcnt_bits((kRing - 1) * kPer));
+  } else if (kt0 < ntiles) {
     const int last = kt0 + (ntiles - 1 - kt0) / kStep * kStep;    // this wave's last tile
 #pragma unroll
     for (int st = 0; st < C::kStages; ++st) issue_tile(min(kt0 + st * kStep, last), st);
@@ -421,9 +453,28 @@ __device__ __forceinline__ void attn_body(
   for (int kt = kt0; kt < ntiles; kt += kStep) {
     // Wait for this tile's copies; those of the wave's later tiles already
     // issued (up to kStages - 1 tiles of 2 * kHalf copies) may stay in flight.
-    const int later = min(C::kStages - 1, (ntiles - 1 - kt) / kStep);
-    wait_copies_behind<C::kStages - 1, 2 * C::kHalf>(later);
-    __builtin_amdgcn_wave_barrier();
+    if constexpr (kShared) {
+      // This wave's part of tile kt has landed once only those of its later
+      // tiles (up to kRing - 2) are in flight; the barrier then waits for the
+      // other waves' parts, and every wave is past tile kt - 1, whose stage now
+      // takes tile kt + kRing - 1.
+      wait_copies_behind<kRing - 2, kPer>(min(kRing - 2, ntiles - 1 - kt));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const int ahead = kt + kRing - 1;
+      if (ahead < ntiles)
+        issue_half(ahead, stage == 0 ? kRing - 1 : stage - 1, my_half,
+                   tile_in_page ? tile_row(ahead) : 0, my_part);
+      if (!active) {
+        stage = stage + 1 == kRing ? 0 : stage + 1;
+        continue;
+      }
+    } else {
+      const int later = min(C::kStages - 1, (ntiles - 1 - kt) / kStep);
+      wait_copies_behind<C::kStages - 1, 2 * C::kHalf>(later);
+      __builtin_amdgcn_wave_barrier();
+    }
     const char* kt_lds = wave_lds + stage * C::kStageBytes;
     const char* vt_lds = kt_lds + C::kTile;
 
@@ -462,10 +513,10 @@ __device__ __forceinline__ void attn_body(
     // now (the V half follows after P.V), once the operand reads have landed.
     const int refill = kt + C::kStages * kStep;
     size_t refill_row = 0;
-    if (refill < ntiles) {
+    if (!kShared && refill < ntiles) {
       __builtin_amdgcn_s_waitcnt(kLgkm0);
       refill_row = tile_in_page ? tile_row(refill) : 0;
-      issue_half(refill, stage, 0, refill_row);
+      issue_half(refill, stage, 0, refill_row, 0);
     }
 
     // V^T operands, shared by the query tiles: k-slot (h, t) of MFMA cc is key
@@ -557,8 +608,8 @@ __device__ __forceinline__ void attn_body(
     __builtin_amdgcn_wave_barrier();
     if (writer && in_block(kt)) write_kept(kt, vt_lds, 1);
     // The V half is consumed too: refill it.
-    if (refill < ntiles) issue_half(refill, stage, 1, refill_row);
-    stage = stage + 1 == C::kStages ? 0 : stage + 1;
+    if (!kShared && refill < ntiles) issue_half(refill, stage, 1, refill_row, 0);
+    stage = stage + 1 == kRing ? 0 : stage + 1;
   }
   // Every copy has landed (the last tile's wait took all of them); the merge
   // below reuses the stage memory.
@@ -666,9 +717,9 @@ __device__ __forceinline__ void attn_body(
 // heads the row group is the slowest grid dimension instead: every
 // sequence's first row group, then the second ones, and so on.
 
-// kQSplitOk: a row group spans 32*T*kWaves query rows; a workgroup with more
-// than 32*T real rows in it splits them over its waves (attn_body kQSplit),
-// one with fewer splits the keys as usual.
+// kQSplitOk (four waves): a row group spans 32*T*4 query rows, which the waves
+// split (attn_body kQSplit); waves past the group's last real row only copy.
+// The kernel's LDS is the shared ring (the key-split body is not built in).
 // kFixed: 32 query heads over 8 KV heads, known at compile time (constant row
 // strides and head mapping in the tile loop's address arithmetic).
 template <int D, bool BF16, int T, int kWaves, int kPaged, bool kQSplitOk, bool kScatter,
@@ -683,7 +734,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T =
     hkv = 8;
     rg_inner = 1;
   }
-  __shared__ __attribute__((aligned(16))) char smem[Cfg<D, BF16, kWaves>::kLds];
+  static_assert(!kQSplitOk || kWaves == 4, "the query split takes four waves");
+  __shared__ __attribute__((aligned(16))) char
+      smem[kQSplitOk ? Cfg<D, BF16, kWaves>::kRingLds : Cfg<D, BF16, kWaves>::kLds];
   __shared__ int32_t pages[kLdsTable<kPaged> ? kPageCache : 1];
   int r, g, rg;                                        // r: position in the processing order
   if (rg_inner) {
@@ -736,26 +789,20 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(T =
     pb = __builtin_amdgcn_readfirstlane(sc.pos_base[b]);
   }
   // Workgroup-uniform choices (every wave of the workgroup takes the same body,
-  // so their barriers match): split the query rows when one wave's tiles do not
-  // hold them all; otherwise skip query tiles that hold no real row.
-  bool done = false;
+  // so their barriers match): the query split in its own kernels; otherwise
+  // skip query tiles that hold no real row.
   if constexpr (kQSplitOk) {
-    if (rows - row0 > 32 * T) {
-      attn_body<D, BF16, T, kWaves, kPaged, true, kScatter>(smem, pages, q, cu, cache_k, cache_v,
-                                                            map, kv_len, out, hq, hkv, c, b, g,
-                                                            rows, row0, sc, kept, pb);
-      done = true;
-    }
-  }
-  if (!done) {
-    if (T == 2 && rows - row0 > 32)
-      attn_body<D, BF16, T, kWaves, kPaged, false, kScatter>(smem, pages, q, cu, cache_k, cache_v,
-                                                             map, kv_len, out, hq, hkv, c, b, g,
-                                                             rows, row0, sc, kept, pb);
-    else
-      attn_body<D, BF16, 1, kWaves, kPaged, false, kScatter>(smem, pages, q, cu, cache_k, cache_v,
-                                                             map, kv_len, out, hq, hkv, c, b, g,
-                                                             rows, row0, sc, kept, pb);
+    attn_body<D, BF16, T, kWaves, kPaged, true, kScatter>(smem, pages, q, cu, cache_k, cache_v, map,
+                                                          kv_len, out, hq, hkv, c, b, g, rows, row0,
+                                                          sc, kept, pb);
+  } else if (T == 2 && rows - row0 > 32) {
+    attn_body<D, BF16, T, kWaves, kPaged, false, kScatter>(smem, pages, q, cu, cache_k, cache_v,
+                                                           map, kv_len, out, hq, hkv, c, b, g,
+                                                           rows, row0, sc, kept, pb);
+  } else {
+    attn_body<D, BF16, 1, kWaves, kPaged, false, kScatter>(smem, pages, q, cu, cache_k, cache_v,
+                                                           map, kv_len, out, hq, hkv, c, b, g,
+                                                           rows, row0, sc, kept, pb);
   }
 }
 
@@ -811,11 +858,13 @@ template <int D, int kPaged, bool kScatter>
 hipError_t launch_bf16(const AttnArgs& a, hipStream_t stream) {
   const long rows = (long)a.k_max * (a.hq / a.hkv);
   const int T = rows > 32 ? 2 : 1;
-  // More than 64 query rows per KV head possible: two-wave workgroups over
-  // 128-row groups, whose waves split the rows when there are more than 64
-  // (each streams the K/V once; the second stream is served mostly by L2) and
-  // the keys otherwise.
-  if (rows > 64) return launch<D, true, 2, 2, kPaged, kScatter, true>(a, stream);
+  // More than 64 query rows per KV head possible: four-wave workgroups over
+  // 128-row groups, whose waves split the rows (32 each) and share one LDS
+  // ring. Past 64 rows the matrix-core work per K/V byte doubles; waves of 32
+  // rows fit two per SIMD (LDS and registers), so one wave's softmax overlaps
+  // another's products. At batch 1,024 with 80-128 rows per KV head: 2,061 us,
+  // against 2,316 us for two waves of 64 rows that each copied every tile.
+  if (rows > 64) return launch<D, true, 1, 4, kPaged, kScatter, true>(a, stream);
   const long items = (long)a.batch * a.hkv * ((rows + 32 * T - 1) / (32 * T));
   const int nw = waves_for(items, a.order != nullptr);
   if (T == 2)
@@ -840,9 +889,9 @@ int attention(const AttnArgs& a, int head_dim, bte_dtype dtype, hipStream_t stre
 }
 
 // Descending-work processing order. Work is the KV length, or with the kept
-// counts the length times the 64-row query passes over the keys (a wave holds
-// 64 query rows; a sequence with more rows per KV head takes the query split,
-// whose waves each stream every key tile). Sequence i's key is (work
+// counts the length times the 64-row query passes over the keys (a key-split
+// wave holds 64 query rows; past 64 rows per KV head the query split's
+// matrix-core work per key tile doubles). Sequence i's key is (work
 // descending, index ascending) packed in 64 bits, so keys are distinct and the
 // position of sequence i in the order is the number of keys below its own. A wave ranks
 // kOrderPerWave sequences: its lanes take every 64th key (read straight from

@@ -492,9 +492,9 @@ int bte_kv_scatter_attention_paged(const void* q, const int32_t* count, const in
  * same attention results.
  *   work[b] = max(kv_len[b], 0)                         (count == NULL)
  *   work[b] = max(kv_len[b], 0) * ceil(max(count[b], 0) * group / 64)
- * capped at 2^32 - 1: an attention wave holds 64 query rows, and a sequence
- * with more kept query rows per KV head than that streams its keys once per
- * 64-row pass (sequences with nothing kept go last).
+ * capped at 2^32 - 1: the attention's key-split waves hold 64 query rows, and
+ * past 64 kept query rows per KV head the matrix-core work per key tile
+ * doubles, so work counts 64-row passes (sequences with nothing kept go last).
  *
  *   kv_len [batch] int32; count [batch] int32 or NULL (the kept counts of the
  *   attention call); group = hq / hkv; order_out [batch] int32 (4 byte

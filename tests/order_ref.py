@@ -10,8 +10,9 @@ work by index ascending. Any order gives the same attention outputs.
 Work of sequence i: its KV length (negative counts as 0); with the kept-row
 counts given, the length times the number of 64-row query passes over its
 keys, ceil(count_i * group / 64) (group = query heads per KV head; a negative
-count counts as 0), capped at 2^32 - 1. One attention wave holds 64 query rows,
-so a sequence with more rows per KV head streams its keys once per pass.
+count counts as 0), capped at 2^32 - 1. A key-split attention wave holds 64
+query rows, and past 64 rows per KV head the matrix-core work per key tile
+doubles.
 """
 from __future__ import annotations
 

@@ -90,11 +90,12 @@ def test_attention_many_items(cfg, ordered):
     _attn(cfg, ordered=ordered)
 
 
-# More than 64 query rows per KV head (k_max * G > 64): two-wave workgroups over
-# 128-row groups; those with more than 64 real rows split them over the waves
-# (each wave streams all keys), the others split the keys. Budgets 0..32 mix
-# both kinds in one launch; with G = 8 a sequence has up to 256 rows, so its
-# second 128-row group is split or not as well.
+# More than 64 query rows per KV head (k_max * G > 64): four-wave workgroups over
+# 128-row groups, whose waves take 32 rows each and share one LDS ring of key
+# tiles; waves past a group's last row only copy. Budgets 0..32 give groups with
+# one to four busy waves in one launch; with G = 8 a sequence has up to 256
+# rows (a second row group). Sequences of one to three key tiles are shorter
+# than the ring's lead (the prologue repeats the last tile).
 QSPLIT = [
     W.AttnCfg("qsplit_mixed", seed=64, batch=300, kept=None, k_lo=0, k_hi=32, hq=32, hkv=8,
               head_dim=128, prefix_lo=1, prefix_hi=300),
@@ -102,6 +103,8 @@ QSPLIT = [
               head_dim=128, prefix_lo=20, prefix_hi=260),
     W.AttnCfg("qsplit_d64", seed=66, batch=200, kept=None, k_lo=10, k_hi=32, hq=32, hkv=8,
               head_dim=64, prefix_lo=1, prefix_hi=150),
+    W.AttnCfg("qsplit_short", seed=67, batch=60, kept=None, k_lo=17, k_hi=32, hq=32, hkv=8,
+              head_dim=128, prefix_lo=0, prefix_hi=64),
 ]
 
 
