@@ -210,11 +210,15 @@ template <int kPaged>
 constexpr bool kLdsTable = kPaged == kPagedLds || kPaged == kPagedBig;
 constexpr int kPageCache = 2048;
 
+// Row block of query-split wave w (four waves): 0, 2, 1, 3. The map swaps the two
+// bits of w, so it is its own inverse: block j belongs to wave qblock(j).
+__device__ __forceinline__ int qblock(int w) { return (w >> 1) | ((w & 1) << 1); }
+
 // One workgroup's work: sequence b, KV head g, the T 32-row query tiles from
 // row0 on (each holding at least one real row).
 // kQSplit = false: the waves share the query rows and take every kWaves-th key
 // tile, their states merged at the end. kQSplit = true (four waves): wave w
-// takes the 32*T query rows from row0 + 32*T*w and every key tile; the tiles
+// takes the 32*T query rows of row block qblock(w) and every key tile; the tiles
 // go through one LDS ring shared by the waves, so each K/V byte is copied from
 // HBM once per workgroup.
 // kScatter: the KV positions [pb, pb + sc.n) may hold kept rows; bit j of
@@ -233,7 +237,12 @@ __device__ __forceinline__ void attn_body(
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31;
   const int h = lane >> 5;
-  const int qrow0 = kQSplit ? row0 + 32 * T * w : row0;   // this wave's first query row
+  // Query split: wave w holds the 32*T rows of row block qblock(w) of the group.
+  // Waves 0 and 2 take the first two blocks: in a group of at most 64 rows the
+  // busy waves are then 0 and 2, which measured faster than 0 and 1 (on the
+  // extended step's selection: 1,889 against 1,966 us), presumably because the
+  // busy waves of a CU's two workgroups then spread over more SIMDs.
+  const int qrow0 = kQSplit ? row0 + 32 * T * qblock(w) : row0;   // this wave's first query row
   const int kt0 = kQSplit ? 0 : w;                       // this wave's first key tile
   constexpr int kStep = kQSplit ? 1 : kWaves;            // and its key-tile stride
   const int L = kv_len[b];
@@ -657,9 +666,9 @@ __device__ __forceinline__ void attn_body(
 #pragma unroll
     for (int r0 = 0; r0 < kOutRows; r0 += kRowsPerPass) {
       const int ro = r0 + threadIdx.x / kChunks;         // output row of this tq
-      const int vq = kQSplit ? ro / 32 : 0;              // query split: the wave that owns it
+      const int vq = kQSplit ? qblock(ro / 32) : 0;      // query split: the wave that owns it
       const int rr = ro % 32;                            // its row within the 32-row tile
-      const int rho = row0 + (kQSplit ? 32 * T * vq : 0) + 32 * tq + rr;
+      const int rho = row0 + (kQSplit ? 32 * T * (ro / 32) : 0) + 32 * tq + rr;
       if (rho < rows) {
         // Merge weights: one state per wave (key split), or the owner's own state.
         constexpr int kStates = kQSplit ? 1 : kWaves;
