@@ -59,6 +59,9 @@ CASES = [
               prefix_lo=60, prefix_hi=200),
     W.AttnCfg("rows_beyond_64", seed=37, batch=3, kept=20, hq=16, hkv=4, head_dim=128,
               prefix_lo=40, prefix_hi=130),
+    # fp32 takes 32-row groups: 80 rows per KV head are three of them
+    W.AttnCfg("f32_rows_beyond_64", seed=40, batch=3, kept=20, hq=16, hkv=4, head_dim=128,
+              dtype=W.F32, prefix_lo=40, prefix_hi=130),
     W.AttnCfg("long", seed=38, batch=2, kept=3, hq=8, hkv=2, head_dim=128, prefix_lo=8000, prefix_hi=9000),
     # sequences of about 131K positions: over 4,000 key tiles per item
     W.AttnCfg("very_long", seed=39, batch=2, kept=2, hq=8, hkv=2, head_dim=128, prefix_lo=130000,
@@ -105,6 +108,11 @@ QSPLIT = [
               head_dim=64, prefix_lo=1, prefix_hi=150),
     W.AttnCfg("qsplit_short", seed=67, batch=60, kept=None, k_lo=17, k_hi=32, hq=32, hkv=8,
               head_dim=128, prefix_lo=0, prefix_hi=64),
+    # fewer than four KV heads: the row group is the slowest grid dimension
+    W.AttnCfg("qsplit_hkv2", seed=68, batch=50, kept=None, k_lo=9, k_hi=32, hq=16, hkv=2,
+              head_dim=128, prefix_lo=10, prefix_hi=200),
+    W.AttnCfg("qsplit_hkv1", seed=69, batch=40, kept=None, k_lo=0, k_hi=32, hq=8, hkv=1,
+              head_dim=64, prefix_lo=10, prefix_hi=200),
 ]
 
 
