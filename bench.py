@@ -52,7 +52,8 @@ PAGE = 64                      # KV pool page size (rows) of the extended step
 FLUSH_BYTES = 1 << 30          # read before each timed iteration of the flushed legs
 LEG_ITERS = 30                 # timed iterations of each flushed leg
 METRIC = "block tokens/s through score→top-K→gather→reduced attn; % of HBM/MFMA roofline"
-LEGS = ["focus_b256", "attn_b256", "focus_b1024_block64", "focus_b2048_block16", "es_mode",
+LEGS = ["focus_b256", "attn_b256", "focus_b1024_block64", "chain_b1024_block64",
+        "focus_b2048_block16", "es_mode",
         "es_pipeline",
         "es_iteration", "fused_scatter_attention", "full_step", "score_resident"]
 
@@ -185,6 +186,7 @@ def main():
         "focus_b256": lambda: focus_b256_leg(dev, flush),
         "attn_b256": lambda: attn_b256_leg(dev, flush),
         "focus_b1024_block64": lambda: focus_block64_leg(dev, flush),
+        "chain_b1024_block64": lambda: chain_block64_leg(dev, args.steps, args.warmup),
         "focus_b2048_block16": lambda: focus_block16_leg(dev, flush),
         "es_mode": lambda: es_mode_leg(dev, flush, args.steps),
         "es_pipeline": lambda: es_pipeline_leg(dev, flush, args.steps),
@@ -418,6 +420,77 @@ def focus_block64_leg(dev, flush):
     """Blocks of 64 positions (the FOCUS paper's largest block) at batch 1024; K ~ U{8..24},
     the batch-256 budget range scaled with the block."""
     return focus_block_leg(dev, flush, 1024, 64, 8, 24, seed=6)
+
+
+def chain_block64_leg(dev, steps: int, warmup: int):
+    """The whole step at blocks of 64 (batch 1024, K ~ U{8..24}, prefixes 1024..4096 + 64):
+    delta -> top-K -> gather -> scatter -> order -> attention, timed like the main step
+    (per-stage events over `steps` eager steps after `warmup`, and the warm HIP-graph
+    replay). Up to 96 query rows per KV head: the attention takes the query split."""
+    import numpy as np
+    import torch
+
+    from block_token_eviction_amd.chain import FocusStep
+    import workloads as W
+
+    name = "chain_b1024_block64"
+    fc = W.FocusCfg(name, seed=8, batch=1024, block=64, k_lo=8, k_hi=24)
+    ac = W.AttnCfg(name, seed=8, batch=1024, kept=None, k_lo=8, k_hi=24, block=64,
+                   prefix_lo=1024, prefix_hi=4096)
+    x = W.chain_inputs(fc, ac, device=dev)
+    st = FocusStep(fc.batch, fc.block, fc.hidden, fc.hq, fc.head_dim, fc.k_hi, fc.dtype, dev)
+    run_args = {k: x[k] for k in ("q0", "k0", "q1", "k1", "decoded", "k", "hidden_rows",
+                                  "pool_kernel", "new_k", "new_v", "q_kept", "cache_k", "cache_v",
+                                  "seq_start", "kv_len", "row_base")}
+    stages = [
+        ("focus_importance_delta", lambda: st.score(x["q0"], x["k0"], x["q1"], x["k1"], x["decoded"], fc.pool_kernel)),
+        ("topk_select", lambda: st.select(x["k"])),
+        ("gather_rows", lambda: st.gather(x["hidden_rows"])),
+        ("kv_scatter", lambda: st.scatter(x["new_k"], x["new_v"], x["row_base"], x["cache_k"], x["cache_v"])),
+        ("attention_order", lambda: st.schedule(x["kv_len"])),
+        ("reduced_attention", lambda: st.attend(x["q_kept"], x["cache_k"], x["cache_v"], x["seq_start"], x["kv_len"])),
+    ]
+    for _ in range(warmup):
+        st.run(**run_args)
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [[(E(), E()) for _ in stages] for _ in range(steps)]
+    for it in range(steps):
+        for i, (_, fn) in enumerate(stages):
+            ev[it][i][0].record()
+            fn()
+            ev[it][i][1].record()
+    torch.cuda.synchronize()
+    stage_ms = {n_: float(np.mean([ev[it][i][0].elapsed_time(ev[it][i][1]) for it in range(steps)]))
+                for i, (n_, _) in enumerate(stages)}
+    graph_ms = graph_step_ms(lambda: st.run(**run_args), steps)
+    count = st.count.cpu().numpy().astype(np.int64)
+    sum_k = int(count.sum())
+    kv_len = x["kv_len"].cpu().numpy().astype(np.int64)
+    n, B, hq, hkv, D, H = fc.batch, fc.block, fc.hq, fc.hkv, fc.head_dim, fc.hidden
+    bytes_ = {"focus_importance_delta": delta_bytes(n, B, hq, hkv, D, 2),
+              "topk_select": n * B * 4 + n * 4 + n * (fc.k_hi + 2) * 4,
+              "gather_rows": 2 * sum_k * H * 2,
+              "kv_scatter": 2 * 2 * sum_k * hkv * D * 2,
+              "attention_order": 2 * n * 4,
+              "reduced_attention": attention_bytes(kv_len, sum_k, hq, hkv, D, 2)}
+    kernels = {k: {"ms": round(v, 4), "algo_bytes": int(bytes_[k]),
+                   "GB/s": round(bytes_[k] / (v * 1e-3) / 1e9, 1),
+                   "hbm_frac": round(bytes_[k] / (v * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+               for k, v in stage_ms.items()}
+    kernels["reduced_attention"]["tflops"] = round(
+        attention_flops(count, kv_len, hq, D) / (stage_ms["reduced_attention"] * 1e-3) / 1e12, 2)
+    ms = graph_ms if graph_ms is not None else float(np.mean(
+        [ev[it][0][0].elapsed_time(ev[it][-1][1]) for it in range(steps)]))
+    res = {"workload": f"{name} (batch 1024, block 64, 32q/8kv heads, head dim 128, bf16, "
+                       "MaxPool 7, K ~ U{8..24}, hidden 4096, prefixes U{1024..4096} + 64)",
+           "timing": "warm HIP-graph replay for the step; eager per-kernel HIP events",
+           "kept_rows": sum_k, "sequences_above_64_rows": int((count * (hq // hkv) > 64).sum()),
+           "ms_per_step": round(ms, 4), "block tokens/s": round(n * B / (ms * 1e-3), 1),
+           "kernels": kernels}
+    del x, st
+    torch.cuda.empty_cache()
+    return res
 
 
 def focus_block16_leg(dev, flush):
