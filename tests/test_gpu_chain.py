@@ -121,6 +121,18 @@ def test_chain_b1024_full_size(fused):
 
 
 @FUSED
+def test_chain_b1024_block64_full_size(fused):
+    """The whole step at blocks of 64 as bench.py's chain_b1024_block64 leg runs it (batch
+    1024, K ~ U{8..24}, prefixes 1024..4096 + 64): every sequence's delta, selection,
+    gathered rows and cache rows; the attention of every 8th sequence, about 40 % of which
+    have more than 64 query rows per KV head (query-split workgroups)."""
+    fc = W.FocusCfg("chain_b1024_block64", seed=8, batch=1024, block=64, k_lo=8, k_hi=24)
+    ac = W.AttnCfg("chain_b1024_block64", seed=8, batch=1024, kept=None, k_lo=8, k_hi=24,
+                   block=64, prefix_lo=1024, prefix_hi=4096)
+    _check_chain(fc, ac, list(range(0, 1024, 8)), fused=fused)
+
+
+@FUSED
 def test_focus_step_graph_replays_match_eager(fused):
     """A FOCUS step captured in a HIP graph and replayed three times, with eager
     work and synchronisations in between: every replay equals the eager step
