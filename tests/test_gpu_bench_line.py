@@ -45,3 +45,23 @@ def test_bench_line_contract():
               "attention_order", "reduced_attention")
     assert set(stages) <= set(d["kernels"])
     assert sum(d["kernels"][s]["ms"] for s in stages) == pytest.approx(d["eager_ms_per_step"], rel=0.25)
+
+
+def test_bench_block64_chain_leg():
+    """The whole-step leg at blocks of 64: its throughput is the batch's block positions over
+    its step time, and its attention runs the query split (sequences above 64 rows)."""
+    say("bench.py --steps 3 --warmup 2 --no-cpu-baseline --legs chain_b1024_block64")
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "3",
+                        "--warmup", "2", "--no-cpu-baseline", "--legs", "chain_b1024_block64"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-3000:]
+    d = json.loads([l for l in r.stdout.splitlines() if l.strip()][-1])
+    leg = d["chain_b1024_block64"]
+    assert leg["block tokens/s"] == pytest.approx(1024 * 64 / (leg["ms_per_step"] * 1e-3), rel=1e-3)
+    assert 0 < leg["sequences_above_64_rows"] < 1024
+    ks = leg["kernels"]
+    assert set(ks) == {"focus_importance_delta", "topk_select", "gather_rows", "kv_scatter",
+                       "attention_order", "reduced_attention"}
+    att = ks["reduced_attention"]
+    assert att["hbm_frac"] == pytest.approx(att["algo_bytes"] / (att["ms"] * 1e-3) / 8e12, abs=1e-3)
+    assert 0.3 < att["hbm_frac"] < 1.0
