@@ -113,6 +113,9 @@ QSPLIT = [
               head_dim=128, prefix_lo=10, prefix_hi=200),
     W.AttnCfg("qsplit_hkv1", seed=69, batch=40, kept=None, k_lo=0, k_hi=32, hq=8, hkv=1,
               head_dim=64, prefix_lo=10, prefix_hi=200),
+    # more than eight KV heads (a sequence's workgroups span two rounds of the XCDs)
+    W.AttnCfg("qsplit_hkv16", seed=70, batch=30, kept=None, k_lo=12, k_hi=32, hq=64, hkv=16,
+              head_dim=128, prefix_lo=10, prefix_hi=300),
 ]
 
 
