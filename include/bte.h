@@ -36,7 +36,7 @@ typedef enum {
   BTE_OK = 0,
   BTE_ERR_NULL = -1,         /* a required pointer is NULL                        */
   BTE_ERR_DIM = -2,          /* a size is out of range or inconsistent            */
-  BTE_ERR_UNSUPPORTED = -3,  /* valid request this build does not implement       */
+  BTE_ERR_UNSUPPORTED = -3,  /* valid request the library does not implement      */
   BTE_ERR_ALIGN = -4,        /* a pointer or row size breaks the alignment rule   */
   BTE_ERR_LAUNCH = -5        /* the HIP runtime rejected a kernel launch          */
 } bte_status;
