@@ -133,14 +133,19 @@ def test_chain_b1024_block64_full_size(fused):
 
 
 @FUSED
-def test_focus_step_graph_replays_match_eager(fused):
+@pytest.mark.parametrize("block", [32, 64], ids=["block32", "block64_query_split"])
+def test_focus_step_graph_replays_match_eager(fused, block):
     """A FOCUS step captured in a HIP graph and replayed three times, with eager
     work and synchronisations in between: every replay equals the eager step
-    bit for bit (the kernels allocate nothing and record no memset nodes)."""
+    bit for bit (the kernels allocate nothing and record no memset nodes). At
+    blocks of 64 (budgets 8..24) the delta takes its 64-key kernel and the
+    attention its query-split workgroups."""
     from block_token_eviction_amd.chain import FocusStep
-    fc = W.FocusCfg("graph", seed=81, batch=64)
-    ac = W.AttnCfg("graph", seed=81, batch=64, kept=None, prefix_lo=100, prefix_hi=600)
-    say(f"focus step under graph capture fused={fused}")
+    k_lo, k_hi = (4, 12) if block == 32 else (8, 24)
+    fc = W.FocusCfg("graph", seed=81, batch=64, block=block, k_lo=k_lo, k_hi=k_hi)
+    ac = W.AttnCfg("graph", seed=81, batch=64, kept=None, k_lo=k_lo, k_hi=k_hi, block=block,
+                   prefix_lo=100, prefix_hi=600)
+    say(f"focus step under graph capture fused={fused} block={block}")
     x = W.chain_inputs(fc, ac, device="cuda")
     step = FocusStep(fc.batch, fc.block, fc.hidden, fc.hq, fc.head_dim, fc.k_hi, fc.dtype, "cuda",
                      hkv=fc.hkv)
