@@ -116,6 +116,9 @@ QSPLIT = [
     # more than eight KV heads (a sequence's workgroups span two rounds of the XCDs)
     W.AttnCfg("qsplit_hkv16", seed=70, batch=30, kept=None, k_lo=12, k_hi=32, hq=64, hkv=16,
               head_dim=128, prefix_lo=10, prefix_hi=300),
+    # many short items: 3,000 sequences over 24,000 query-split workgroups
+    W.AttnCfg("qsplit_many", seed=71, batch=3000, kept=None, k_lo=10, k_hi=24, hq=32, hkv=8,
+              head_dim=128, prefix_lo=1, prefix_hi=40),
 ]
 
 
